@@ -1,0 +1,294 @@
+"""Plain CPU oracle for FP8 (OCP E4M3FN) W8A8 quantization and scaled GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``fp8_w8a8_quantized_amd``) never imports it, and nothing here imports the
+product path: the two share no code, headers, tables or helpers.
+
+Layout:
+  * ``fp8_oracle.c`` -- the codec, scales, quantizers and RMSNorm as plain C
+    (built with gcc, no FMA contraction, no fast-math).
+  * this module -- ctypes marshalling for the C part, and the GEMM oracle:
+    dequantize each operand to fp64 (code value times its scale, exact in fp64)
+    and multiply with an fp64 matrix product, left unrounded.
+
+Pages cited (short tag -> page title, section):
+  [FP8-RL]       "FP8-RL: A Practical and Stable Low-Precision Stack for LLM RL",
+                 abstract (i): FP8 W8A8 linear layers with blockwise scales, for
+                 dense and MoE models.
+  [vllm-54894]   "[vllm] [ROCm] DeepSeek V4 ... FP8 WO_A 출력 프로젝션 최적화 분석",
+                 §2 (weights viewed as (groups, out, in), scales as
+                 (groups, out/128, in/128)), §3 (group-128 activation quant feeding
+                 the a8w8 GEMM).
+  [sglang-21403] "[sglang] SGLang의 AMD GPU 최적화: RMSNorm과 FP8 Per-token
+                 Quantization 커널 융합", §3 (per-token x per-channel a8w8 GEMM
+                 with bf16 output, bias None).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfp8_oracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+GRAN_BLOCK = 0
+GRAN_ROW = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/libfp8_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        i64 = ctypes.c_int64
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode_bits.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode_bits.restype = ctypes.c_uint8
+        L.orc_e4m3_encoders_disagree.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.orc_e4m3_encoders_disagree.restype = ctypes.c_uint64
+        L.orc_e4m3_encode_array.argtypes = [f32p, i64, u8p]
+        L.orc_e4m3_encode_array.restype = None
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.orc_scale_f32.argtypes = [ctypes.c_float]
+        L.orc_scale_f32.restype = ctypes.c_float
+        L.orc_e8m0_exponent.argtypes = [ctypes.c_float]
+        L.orc_e8m0_exponent.restype = ctypes.c_int
+        L.orc_e8m0_lossless.argtypes = [f32p, i64, u8p]
+        L.orc_e8m0_lossless.restype = ctypes.c_int
+        L.orc_quantize_block.argtypes = [u16p, i64, i64, u8p, f32p]
+        L.orc_quantize_block.restype = None
+        L.orc_quantize_token.argtypes = [u16p, i64, i64, u8p, f32p]
+        L.orc_quantize_token.restype = None
+        L.orc_quantize_weight_block.argtypes = [u16p, i64, i64, ctypes.c_int, u8p,
+                                                ctypes.c_void_p]
+        L.orc_quantize_weight_block.restype = None
+        L.orc_rmsnorm_bf16.argtypes = [u16p, u16p, ctypes.c_float, i64, i64, u16p]
+        L.orc_rmsnorm_bf16.restype = None
+        L.orc_rms_sumsq.argtypes = [u16p, i64]
+        L.orc_rms_sumsq.restype = ctypes.c_float
+        L.orc_rmsnorm_quant.argtypes = [u16p, u16p, ctypes.c_float, i64, i64, u8p, f32p]
+        L.orc_rmsnorm_quant.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _bits16(x) -> np.ndarray:
+    """bf16 input as a contiguous uint16 bit-pattern array (numpy or torch CPU)."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch  # bf16 tensors arrive from the shared input generators
+
+    assert x.dtype == torch.bfloat16 and x.device.type == "cpu"
+    return np.ascontiguousarray(x.contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+# ---------------------------------------------------------------- codec --
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def e4m3_encode_bits(v: float) -> int:
+    return lib().orc_e4m3_encode_bits(v)
+
+
+def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_encode_array(_p(v, ctypes.c_float), v.size, _p(out, ctypes.c_uint8))
+    return out
+
+
+def encoders_disagree(lo: int, hi: int) -> int:
+    return lib().orc_e4m3_encoders_disagree(lo, hi)
+
+
+def decode_table() -> np.ndarray:
+    """fp64 values of all 256 codes (NaN at 0x7F and 0xFF)."""
+    return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def bf16_to_f32(b: int) -> float:
+    return lib().orc_bf16_to_f32(b)
+
+
+def f32_to_bf16_rne(f: float) -> int:
+    return lib().orc_f32_to_bf16_rne(f)
+
+
+def scale_f32(amax: float) -> float:
+    return lib().orc_scale_f32(amax)
+
+
+def e8m0_exponent(s: float) -> int:
+    return lib().orc_e8m0_exponent(s)
+
+
+def e8m0_lossless(s: np.ndarray):
+    """[vllm-54894] §1 lossless conversion; returns codes or None."""
+    s = np.ascontiguousarray(s, dtype=np.float32).reshape(-1)
+    codes = np.empty(s.shape, np.uint8)
+    ok = lib().orc_e8m0_lossless(_p(s, ctypes.c_float), s.size, _p(codes, ctypes.c_uint8))
+    return codes if ok else None
+
+
+# ----------------------------------------------------------- quantizers --
+def quantize_block(x):
+    """1x128 groups ([FP8-RL] blockwise; [vllm-54894] §3 group size 128)."""
+    xb = _bits16(x)
+    M, K = xb.shape
+    assert K % 128 == 0
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // 128), np.float32)
+    lib().orc_quantize_block(_p(xb, ctypes.c_uint16), M, K, _p(q, ctypes.c_uint8),
+                             _p(s, ctypes.c_float))
+    return q, s
+
+
+def quantize_token(x):
+    """One scale per row (per-token activations, per-row weights)."""
+    xb = _bits16(x)
+    M, K = xb.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M,), np.float32)
+    lib().orc_quantize_token(_p(xb, ctypes.c_uint16), M, K, _p(q, ctypes.c_uint8),
+                             _p(s, ctypes.c_float))
+    return q, s
+
+
+def quantize_weight_block(w, fmt: int = 0):
+    """128x128 blocks; fmt 0 -> fp32 scales, fmt 1 -> E8M0 bytes."""
+    wb = _bits16(w)
+    N, K = wb.shape
+    assert N % 128 == 0 and K % 128 == 0
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N // 128, K // 128), np.float32 if fmt == 0 else np.uint8)
+    lib().orc_quantize_weight_block(_p(wb, ctypes.c_uint16), N, K, fmt,
+                                    _p(q, ctypes.c_uint8), s.ctypes.data)
+    return q, s
+
+
+def rmsnorm_bf16(x, gamma, eps: float) -> np.ndarray:
+    xb, gb = _bits16(x), _bits16(gamma)
+    M, K = xb.shape
+    y = np.empty((M, K), np.uint16)
+    lib().orc_rmsnorm_bf16(_p(xb, ctypes.c_uint16), _p(gb, ctypes.c_uint16), eps, M, K,
+                           _p(y, ctypes.c_uint16))
+    return y
+
+
+def rms_sumsq(xrow) -> float:
+    xb = _bits16(xrow).reshape(-1)
+    return lib().orc_rms_sumsq(_p(xb, ctypes.c_uint16), xb.size)
+
+
+def rmsnorm_quant(x, gamma, eps: float):
+    xb, gb = _bits16(x), _bits16(gamma)
+    M, K = xb.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M,), np.float32)
+    lib().orc_rmsnorm_quant(_p(xb, ctypes.c_uint16), _p(gb, ctypes.c_uint16), eps, M, K,
+                            _p(q, ctypes.c_uint8), _p(s, ctypes.c_float))
+    return q, s
+
+
+# ----------------------------------------------------------------- GEMM --
+_DEC = None
+
+
+def _dec() -> np.ndarray:
+    global _DEC
+    if _DEC is None:
+        _DEC = decode_table()
+    return _DEC
+
+
+def dequant_act(q: np.ndarray, s: np.ndarray, gran: int) -> np.ndarray:
+    """fp64 value of each activation element: code value x its scale.
+    BLOCK: s[m, k // 128]; ROW: s[m]."""
+    d = _dec()[q]
+    if gran == GRAN_BLOCK:
+        return d * np.repeat(s.astype(np.float64), 128, axis=1)
+    return d * s.astype(np.float64)[:, None]
+
+
+def dequant_weight(q: np.ndarray, s: np.ndarray, gran: int) -> np.ndarray:
+    """fp64 value of each weight element.  BLOCK: s[n // 128, k // 128]
+    ([vllm-54894] §2 block view); ROW: s[n] (per output channel)."""
+    d = _dec()[q]
+    if gran == GRAN_BLOCK:
+        full = np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)
+        return d * full
+    return d * s.astype(np.float64)[:, None]
+
+
+def gemm(qa, qw, sa, sw, gran: int, rows=None) -> np.ndarray:
+    """Y[m, n] = sum_k deq(A)[m, k] * deq(W)[n, k] in fp64 (Y = X W^T).
+
+    ``rows`` optionally restricts the output to those rows of A (a sample)."""
+    if rows is not None:
+        rows = np.asarray(rows)
+        qa = qa[rows]
+        sa = sa[rows]
+    A = dequant_act(qa, sa, gran)
+    W = dequant_weight(qw, sw, gran)
+    return A @ W.T
+
+
+def grouped_gemm(qa, qw, sa, sw, offsets, rows=None) -> np.ndarray:
+    """[FP8-RL] MoE coverage: for expert e, rows offsets[e]:offsets[e+1] of A
+    use weight qw[e] with block scales sw[e] (BLOCK granularity).  Returns the
+    rows listed in ``rows`` (all rows when None), fp64."""
+    T = qa.shape[0]
+    E = qw.shape[0]
+    offsets = np.asarray(offsets, dtype=np.int64)
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows)
+    out = np.zeros((rows.size, qw.shape[1]), np.float64)
+    expert_of = np.searchsorted(offsets, rows, side="right") - 1
+    for e in range(E):
+        sel = np.nonzero(expert_of == e)[0]
+        if sel.size == 0:
+            continue
+        out[sel] = gemm(qa[rows[sel]], qw[e], sa[rows[sel]], sw[e], GRAN_BLOCK)
+    return out

@@ -1,0 +1,88 @@
+"""Pins for the oracle's RMSNorm and fused RMSNorm + per-token quantization.
+
+The fixed fp32 summation order is a definition (the pages fix none), so the
+order itself is pinned only by self-consistency; everything around it is
+pinned by: closed forms (x == 1, equal magnitudes), the exact sum of squares
+within the fp32 error bound of the fixed order, agreement with
+torch.nn.functional.rms_norm in fp64 (the definition the page cites) to one
+bf16 ulp, the bf16 rounding against torch's dtype conversion, and the fused ==
+composed identity.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def _f32(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_bf16_rounding_matches_torch_conversion():
+    rng = np.random.default_rng(0)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    # exact ties: bf16 value + half an ulp
+    base = (rng.integers(0x3000, 0x4F00, 2000).astype(np.uint32) << 16)
+    ties = (base | 0x8000).view(np.float32)
+    allv = np.concatenate([v, ties, -ties])
+    ref = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16_rne(float(x)) for x in allv], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_ones_closed_form():
+    K = 5120
+    x = np.full((3, K), 0x3F80, np.uint16)  # 1.0
+    g = np.full(K, 0x3F80, np.uint16)
+    assert oracle.rms_sumsq(x[0]) == float(K)
+    y = oracle.rmsnorm_bf16(x, g, 1e-6)
+    assert np.all(y == 0x3F80)  # 1/sqrt(1 + 1e-6) rounds to 1.0 in bf16
+    q, s = oracle.rmsnorm_quant(x, g, 1e-6)
+    assert np.all(q == 0x7E)
+    assert np.all(s == np.float32(1.0) / np.float32(448.0))
+
+
+def test_equal_magnitudes_quantize_to_max():
+    K = 1024
+    rng = np.random.default_rng(3)
+    sign = np.where(rng.random((4, K)) < 0.5, 0x8000, 0).astype(np.uint16)
+    x = (sign | np.uint16(0x4040)).astype(np.uint16)  # +-3.0
+    g = np.full(K, 0x3F80, np.uint16)
+    q, s = oracle.rmsnorm_quant(x, g, 1e-6)
+    assert np.array_equal(q, np.where(sign != 0, 0xFE, 0x7E).astype(np.uint8))
+
+
+@pytest.mark.parametrize("K", [8, 64, 520, 5120])
+def test_fixed_order_sum_within_fp32_bound_of_exact(K):
+    rng = np.random.default_rng(K)
+    for trial in range(5):
+        x = synth.bf16_bits(synth.to_bf16(rng.standard_normal(K).astype(np.float32) *
+                                          np.exp2(rng.integers(-8, 8, K)).astype(np.float32)))
+        xf = _f32(x)
+        exact = sum(Fraction(float(v)) ** 2 for v in xf)
+        got = Fraction(oracle.rms_sumsq(x))
+        # each fp32 addition adds at most one rounding of relative 2^-24
+        assert abs(got - exact) <= (K - 1) * Fraction(1, 2 ** 24) * exact * Fraction(11, 10)
+
+
+def test_matches_torch_rms_norm_in_fp64_within_one_bf16_ulp():
+    h, gamma = synth.rms_inputs(M=64, K=5120, seed=2)
+    y = oracle.rmsnorm_bf16(h, gamma, 1e-6)
+    ref = torch.nn.functional.rms_norm(h.double(), (5120,), weight=gamma.double(), eps=1e-6)
+    ref_b = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).astype(np.int32)
+    yi = y.astype(np.int32)
+    # same sign, bf16 patterns differ by at most one step
+    assert np.all(np.abs(yi - ref_b) <= 1)
+    assert np.mean(yi == ref_b) > 0.99
+
+
+def test_fused_equals_composed():
+    h, gamma = synth.rms_inputs(M=32, K=5120, seed=4)
+    qf, sf = oracle.rmsnorm_quant(h, gamma, 1e-6)
+    y = oracle.rmsnorm_bf16(h, gamma, 1e-6)
+    qc, sc = oracle.quantize_token(y)
+    assert np.array_equal(qf, qc) and np.array_equal(sf, sc)
