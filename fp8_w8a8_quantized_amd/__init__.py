@@ -1,0 +1,245 @@
+"""MI355X (gfx950) FP8 W8A8 quantization and scaled GEMM.
+
+Thin Python binding over the C ABI of ``libfp8w8a8.so`` (include/fp8w8a8.h).
+Every function here only checks tensor properties, allocates outputs with
+torch on the input's device and passes raw pointers plus torch's current HIP
+stream to the library; all computation runs in the library's HIP kernels.
+If the library has not been built, every call raises ``Fp8LibraryMissing``.
+
+The pairs returned by the quantizers are the (fp8 tensor, scale) tuples that
+the page "[sglang] SGLang의 AMD GPU 최적화: RMSNorm과 FP8 Per-token Quantization
+커널 융합" (§3) passes straight into the GEMM without re-quantizing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
+    "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
+    "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
+    "status_string", "abi_version",
+]
+
+GRAN_BLOCK, GRAN_ROW = 0, 1
+SCALE_F32, SCALE_E8M0 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8w8a8.so")
+
+
+class Fp8Error(RuntimeError):
+    """A library call returned a non-OK status."""
+
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func}: status {status} ({message})")
+        self.status = status
+
+
+class Fp8LibraryMissing(RuntimeError):
+    """libfp8w8a8.so has not been built."""
+
+
+class _WeightDesc(ctypes.Structure):
+    _fields_ = [("w_bf16", ctypes.c_void_p), ("q_e4m3", ctypes.c_void_p),
+                ("s", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp8w8a8.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise Fp8LibraryMissing(
+            f"{_LIB_PATH} is not built; run fp8_w8a8_quantized_amd/build.py "
+            "(or __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sig = {
+        "fp8_abi_version": ([], i32),
+        "fp8_status_string": ([i32], ctypes.c_char_p),
+        "fp8_quantize_block": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_quantize_token": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_rmsnorm_quant": ([vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
+        "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
+        "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
+        "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
+        "fp8_encode_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().fp8_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return load_library().fp8_abi_version()
+
+
+def _check(func: str, rc: int) -> None:
+    if rc != 0:
+        raise Fp8Error(func, rc, status_string(rc))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _as_u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+# ------------------------------------------------------------ quantizers --
+def quantize_block(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M, K/128])."""
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 128 if K % 128 == 0 else 0), dtype=torch.float32, device=x.device)
+    L = load_library()
+    _check("fp8_quantize_block", L.fp8_quantize_block(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def quantize_token(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M])."""
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    L = load_library()
+    _check("fp8_quantize_token", L.fp8_quantize_token(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                  group_size: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused RMSNorm + FP8 quantization.  group_size 0: scales [M];
+    group_size 128: scales [M, K/128]."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(gamma, torch.bfloat16, 1, "gamma")
+    M, K = x.shape
+    if gamma.shape[0] != K:
+        raise ValueError("gamma must have K elements")
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sshape = (M,) if group_size == 0 else (M, K // 128 if K % 128 == 0 else 0)
+    s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    L = load_library()
+    _check("fp8_rmsnorm_quant", L.fp8_rmsnorm_quant(_ptr(q), _ptr(x), _ptr(s), _ptr(gamma),
+                                                   float(eps), M, K, group_size, _stream(x)))
+    return q, s
+
+
+def requantize_weights(weights: Sequence[torch.Tensor], scale_fmt: int = SCALE_F32,
+                       out: Sequence[Tuple[torch.Tensor, torch.Tensor]] = None
+                       ) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+    """128x128-block quantization of every bf16 [N, K] weight in one batched
+    call.  Returns [(E4M3 bytes [N, K], scales [N/128, K/128])] with fp32
+    scales or uint8 E8M0 bytes.  ``out`` may supply preallocated outputs."""
+    if len(weights) == 0:
+        return []
+    dev = weights[0].device
+    sdt = torch.float32 if scale_fmt == SCALE_F32 else torch.uint8
+    descs = (_WeightDesc * len(weights))()
+    results = []
+    for i, w in enumerate(weights):
+        _need(w, torch.bfloat16, 2, f"weights[{i}]")
+        N, K = w.shape
+        if out is not None:
+            q, s = out[i]
+        else:
+            q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            s = torch.empty((N // 128, K // 128), dtype=sdt, device=dev)
+        descs[i] = _WeightDesc(w.data_ptr(), _as_u8(q).data_ptr(), s.data_ptr(), N, K)
+        results.append((q, s))
+    L = load_library()
+    _check("fp8_requantize_weights",
+           L.fp8_requantize_weights(descs, len(weights), scale_fmt, _stream(weights[0])))
+    return results
+
+
+# ----------------------------------------------------------------- GEMMs --
+def gemm_a8w8_scaled(a: Tuple[torch.Tensor, torch.Tensor], w: Tuple[torch.Tensor, torch.Tensor],
+                     gran: int = GRAN_BLOCK, out: torch.Tensor = None) -> torch.Tensor:
+    """Y = X W^T in bf16 from (q, s) pairs: a = (E4M3 [M, K], scales),
+    w = (E4M3 [N, K], scales)."""
+    qa, sa = _as_u8(a[0]), a[1]
+    qw, sw = _as_u8(w[0]), w[1]
+    _need(qa, torch.uint8, 2, "a")
+    _need(qw, torch.uint8, 2, "w")
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("a and w disagree on K")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    L = load_library()
+    _check("fp8_gemm_a8w8_scaled",
+           L.fp8_gemm_a8w8_scaled(_ptr(qa), _ptr(qw), _ptr(sa), _ptr(sw), None, _ptr(y), M, N, K,
+                                  gran, _stream(qa)))
+    return y
+
+
+def grouped_gemm_a8w8_scaled(a: Tuple[torch.Tensor, torch.Tensor],
+                             w: Tuple[torch.Tensor, torch.Tensor], offsets: torch.Tensor,
+                             out: torch.Tensor = None) -> torch.Tensor:
+    """MoE grouped block-scaled GEMM: a = (E4M3 [T, K], [T, K/128]),
+    w = (E4M3 [E, N, K], [E, N/128, K/128]), offsets int32 [E+1] on the device."""
+    qa, sa = _as_u8(a[0]), a[1]
+    qw, sw = _as_u8(w[0]), w[1]
+    _need(qa, torch.uint8, 2, "a")
+    _need(qw, torch.uint8, 3, "w")
+    _need(offsets, torch.int32, 1, "offsets")
+    T, K = qa.shape
+    E, N, _ = qw.shape
+    if offsets.shape[0] != E + 1:
+        raise ValueError("offsets must have E + 1 entries")
+    y = out if out is not None else torch.empty((T, N), dtype=torch.bfloat16, device=qa.device)
+    L = load_library()
+    _check("fp8_grouped_gemm_a8w8_scaled",
+           L.fp8_grouped_gemm_a8w8_scaled(_ptr(qa), _ptr(qw), _ptr(sa), _ptr(sw), _ptr(offsets),
+                                          _ptr(y), T, E, N, K, _stream(qa)))
+    return y
+
+
+def encode_f32_bits(first_bits: int, n: int, device="cuda") -> torch.Tensor:
+    """Diagnostic: E4M3 codes of the fp32 bit patterns first_bits .. +n-1."""
+    q = torch.empty((n,), dtype=torch.uint8, device=device)
+    L = load_library()
+    _check("fp8_encode_f32_bits",
+           L.fp8_encode_f32_bits(first_bits, n, _ptr(q), _stream(q)))
+    return q

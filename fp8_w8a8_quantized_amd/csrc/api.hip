@@ -1,0 +1,185 @@
+// api.hip -- the C ABI of libfp8w8a8.so (declared in include/fp8w8a8.h).
+//
+// Each entry point validates its arguments on the host (null pointers,
+// alignment, the divisibility rules), then checks that the current device is
+// gfx950, then enqueues its kernels.  On any error nothing is launched and
+// nothing is written.  The refusal of shapes that are not multiples of 128 and
+// the device capability check mirror the FP8 path preparation of the page
+// "[vllm] [ROCm] DeepSeek V4 ... FP8 WO_A ...", §2, where the caller keeps its
+// bf16 path when either fails.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fp8w8a8.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_arch_once[kMaxDevices];
+bool g_arch_ok[kMaxDevices];
+
+// gfx950 check of the current device, cached per device.  The environment
+// variable FP8W8A8_FORCE_ARCH replaces the reported architecture name (used
+// to exercise the refusal path on a gfx950 machine).
+int device_check() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return FP8_ERR_DEVICE;
+    }
+    const char* forced = std::getenv("FP8W8A8_FORCE_ARCH");
+    if (forced) return std::strncmp(forced, "gfx950", 6) == 0 ? FP8_OK : FP8_ERR_DEVICE;
+    std::call_once(g_arch_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        g_arch_ok[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                         std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        (void)hipGetLastError();
+    });
+    return g_arch_ok[dev] ? FP8_OK : FP8_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8W8A8_ABI_VERSION; }
+
+const char* fp8_status_string(int status) {
+    switch (status) {
+        case FP8_OK: return "ok";
+        case FP8_ERR_ARG: return "invalid argument";
+        case FP8_ERR_SHAPE: return "unsupported shape (a dimension is not a required multiple)";
+        case FP8_ERR_ALIGN: return "misaligned pointer";
+        case FP8_ERR_DEVICE: return "no gfx950 (MI355X) HIP device";
+        case FP8_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fp8_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s, void* stream) {
+    if (M < 0 || K <= 0) return K <= 0 ? FP8_ERR_SHAPE : FP8_ERR_ARG;
+    if (K % 128 != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!x || !q || !s) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_quantize_block(x, M, K, q, s, as_stream(stream)));
+}
+
+int fp8_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s, void* stream) {
+    if (M < 0) return FP8_ERR_ARG;
+    if (K <= 0 || K % 8 != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!x || !q || !s) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_quantize_token(x, M, K, q, s, as_stream(stream)));
+}
+
+int fp8_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps, int64_t M,
+                      int64_t K, int group_size, void* stream) {
+    if (M < 0 || (group_size != 0 && group_size != 128)) return FP8_ERR_ARG;
+    if (K <= 0 || K % (group_size == 0 ? 8 : 128) != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!x || !q || !s || !gamma) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(gamma, 16) || !aligned(s, 4))
+        return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(
+        fp8k::launch_rmsnorm_quant(q, x, s, gamma, eps, M, K, group_size, as_stream(stream)));
+}
+
+int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream) {
+    if (n < 0 || (scale_fmt != FP8_SCALE_F32 && scale_fmt != FP8_SCALE_E8M0)) return FP8_ERR_ARG;
+    if (n == 0) return FP8_OK;
+    if (!descs) return FP8_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        const fp8_weight_desc& d = descs[i];
+        if (d.N < 0 || d.K < 0) return FP8_ERR_ARG;
+        if (d.N % 128 != 0 || d.K % 128 != 0) return FP8_ERR_SHAPE;
+        if (d.N == 0 || d.K == 0) continue;
+        if (!d.w_bf16 || !d.q_e4m3 || !d.s) return FP8_ERR_ARG;
+        if (!aligned(d.w_bf16, 16) || !aligned(d.q_e4m3, 16) ||
+            !aligned(d.s, scale_fmt == FP8_SCALE_F32 ? 4 : 1))
+            return FP8_ERR_ALIGN;
+    }
+    if (int st = device_check()) return st;
+    fp8k::ReqBatch batch;
+    std::memset(&batch, 0, sizeof(batch));
+    int64_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (batch.n == 0) return FP8_OK;
+        const int r = launched(fp8k::launch_requant(batch, blocks, scale_fmt, as_stream(stream)));
+        std::memset(&batch, 0, sizeof(batch));
+        blocks = 0;
+        return r;
+    };
+    for (int i = 0; i < n; ++i) {
+        const fp8_weight_desc& d = descs[i];
+        if (d.N == 0 || d.K == 0) continue;
+        fp8k::ReqDesc& r = batch.d[batch.n++];
+        r.w = static_cast<const uint16_t*>(d.w_bf16);
+        r.q = static_cast<uint8_t*>(d.q_e4m3);
+        r.s = d.s;
+        r.K = d.K;
+        r.kblocks = (int32_t)(d.K / 128);
+        r.block_begin = blocks;
+        blocks += (d.N / 128) * (d.K / 128);
+        if (batch.n == fp8k::kReqMaxDescs)
+            if (int st = flush()) return st;
+    }
+    return flush();
+}
+
+int fp8_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s, const float* w_s,
+                         const void* bias, void* y, int64_t M, int64_t N, int64_t K, int gran,
+                         void* stream) {
+    if (bias != nullptr) return FP8_ERR_ARG;
+    if (gran != FP8_GRAN_BLOCK && gran != FP8_GRAN_ROW) return FP8_ERR_ARG;
+    if (M < 0) return FP8_ERR_ARG;
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(a_s, 4) ||
+        !aligned(w_s, 4))
+        return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, as_stream(stream)));
+}
+
+int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
+                                 const float* w_s, const int32_t* offsets, void* y, int64_t T,
+                                 int64_t E, int64_t N, int64_t K, void* stream) {
+    if (T < 0 || E < 1) return FP8_ERR_ARG;
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (T == 0) return FP8_OK;
+    if (!a || !w || !a_s || !w_s || !offsets || !y) return FP8_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(a_s, 4) ||
+        !aligned(w_s, 4) || !aligned(offsets, 4))
+        return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_grouped_gemm(a, w, a_s, w_s, offsets, y, T, E, N, K,
+                                              as_stream(stream)));
+}
+
+int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream) {
+    if (n < 0 || first_bits > 0xFFFFFFFFull || (uint64_t)n > 0x100000000ull - first_bits)
+        return FP8_ERR_ARG;
+    if (n == 0) return FP8_OK;
+    if (!q) return FP8_ERR_ARG;
+    if (!aligned(q, 16)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_encode_bits(first_bits, n, q, as_stream(stream)));
+}
+
+}  // extern "C"

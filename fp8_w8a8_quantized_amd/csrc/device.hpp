@@ -1,0 +1,92 @@
+// device.hpp -- gfx950 device helpers shared by the quantizer and GEMM kernels:
+// bf16 unpacking and rounding, the E4M3FN encoder, wave reductions.
+//
+// E4M3FN (OCP 8-bit FP, E4M3 without infinities, max 448; the float8_e4m3fn
+// dtype of the verl "Test" section) is produced by the gfx950 conversion
+// instruction v_cvt_pk_fp8_f32, which rounds to nearest even into the OCP
+// format.  The input is first clamped to [-448, 448] with v_med3_f32, which
+// makes the conversion saturating: it never produces the NaN pattern.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// 8 bf16 values packed in 16 bytes -> 8 floats (element i = i-th bf16 in memory)
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// fp32 -> the fp32 value of its bf16 rounding (round to nearest even).
+__device__ __forceinline__ float bf16_round(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// Four floats -> four E4M3FN bytes (byte i encodes element i).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+}
+
+__device__ __forceinline__ uint2 e4m3x8(const float (&t)[8]) {
+    return make_uint2(e4m3x4(t[0], t[1], t[2], t[3]), e4m3x4(t[4], t[5], t[6], t[7]));
+}
+
+__device__ __forceinline__ float amax8(const float (&f)[8]) {
+    float m = fabsf(f[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    return m;
+}
+
+// Max over aligned groups of 16 lanes (order-free, so exact).
+__device__ __forceinline__ float max_16lanes(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+__device__ __forceinline__ float max_wave(float v) {
+    v = max_16lanes(v);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Sum over the 64 lanes as the halving tree T(0..63) = T(0..31) + T(32..63),
+// recursively: the xor partner at distance 1, 2, 4, ... 32 holds the sibling
+// subtree, and IEEE addition is commutative, so every lane ends with the same
+// tree sum.
+__device__ __forceinline__ float tree_sum_wave(float v) {
+    v = v + __shfl_xor(v, 1);
+    v = v + __shfl_xor(v, 2);
+    v = v + __shfl_xor(v, 4);
+    v = v + __shfl_xor(v, 8);
+    v = v + __shfl_xor(v, 16);
+    v = v + __shfl_xor(v, 32);
+    return v;
+}
+
+}  // namespace fp8k

@@ -1,0 +1,43 @@
+// launch.hpp -- internal launchers behind the C ABI (shapes already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+// Descriptor of one weight inside a re-quantization launch.
+struct ReqDesc {
+    const uint16_t* w;
+    uint8_t* q;
+    void* s;
+    int64_t K;
+    int64_t block_begin;  // first block index of this weight within the launch
+    int32_t kblocks;      // K / 128
+    int32_t pad;
+};
+
+constexpr int kReqMaxDescs = 64;
+
+struct ReqBatch {
+    ReqDesc d[kReqMaxDescs];
+    int32_t n;
+    int32_t pad;
+};
+
+hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s,
+                                 hipStream_t st);
+hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s,
+                                 hipStream_t st);
+hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps,
+                                int64_t M, int64_t K, int group_size, hipStream_t st);
+hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, hipStream_t st);
+hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st);
+
+hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
+                       void* y, int64_t M, int64_t N, int64_t K, int gran, hipStream_t st);
+hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
+                               const int32_t* offsets, void* y, int64_t T, int64_t E,
+                               int64_t N, int64_t K, hipStream_t st);
+
+}  // namespace fp8k

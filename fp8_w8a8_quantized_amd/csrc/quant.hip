@@ -1,0 +1,440 @@
+// quant.hip -- memory-bound FP8 quantizers for gfx950.
+//
+// Pages (title, section):
+//   "FP8-RL: A Practical and Stable Low-Precision Stack for LLM RL", abstract
+//     (i): blockwise FP8 quantization of linear-layer inputs and weights, and
+//     per-RL-step re-quantization of the policy weights.
+//   "[vllm] feat: Support online quant for rollout with torchao", "Test":
+//     per-row dynamic scales, e4m3fn operands, no activation value bounds.
+//   "[vllm] [ROCm] DeepSeek V4 ... FP8 WO_A ...", §1 E8M0 scales, §2 the
+//     (groups, out/128, in/128) block-scale view, §3 group-128 quantization.
+//   "[sglang] SGLang의 AMD GPU 최적화: RMSNorm과 FP8 Per-token Quantization 커널
+//     융합", §1 RMSNorm fused with per-token quantization in registers, so the
+//     normalized tensor never makes an HBM round trip.
+//
+// Every kernel streams bf16 through 16-byte loads (8 elements per lane), keeps
+// a group in registers, reduces |x| with cross-lane max, computes the group
+// scale s = amax / 448 with one IEEE division, and encodes each element from
+// the correctly rounded quotient x / s (quotient.hpp) with the hardware E4M3
+// conversion (device.hpp).
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+#include "quotient.hpp"
+
+namespace fp8k {
+namespace {
+
+// Encoder state of one group: its scale and how to divide by it.
+struct GroupDiv {
+    float s;     // stored scale amax / 448 (0 for an all-zero group)
+    float r;     // RN(1 / s) when the reciprocal path applies
+    float d;     // IEEE divisor otherwise (1 for an all-zero group: codes are +-0)
+    bool fast;
+};
+
+__device__ __forceinline__ GroupDiv group_div(float amax) {
+    GroupDiv g;
+    g.s = amax / 448.0f;
+    g.fast = fp8q::scale_has_fast_path(g.s);
+    g.r = g.fast ? 1.0f / g.s : 0.0f;
+    g.d = (g.s == 0.0f) ? 1.0f : g.s;
+    return g;
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&f)[8], const GroupDiv& g) {
+    float t[8];
+    if (g.fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = fp8q::quotient(f[i], g.s, g.r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = f[i] / g.d;
+    }
+    return e4m3x8(t);
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 groups.  The M x K/128 groups are contiguous 256-byte runs in memory,
+// so the kernel treats x as a flat array of groups: a wave covers 4 groups
+// (16 lanes x 16 bytes each) per step and takes U steps, all loads issued
+// before any compute.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void k_quant_block(const uint4* __restrict__ x,
+                                                     uint2* __restrict__ q,
+                                                     float* __restrict__ s, int64_t G) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t chunk0 = wave * U;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+        v[u] = gid < G ? x[(chunk0 + u) * 64 + lane] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+        float f[8];
+        unpack8(v[u], f);
+        const GroupDiv g = group_div(max_16lanes(amax8(f)));
+        if (gid < G) {
+            q[(chunk0 + u) * 64 + lane] = encode8(f, g);
+            if ((lane & 15) == 0) s[gid] = g.s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One scale per row.  One wave per row; lane l holds the row's 8-element
+// vectors l, l+64, l+128, ... in registers (VPL of them), so the row is read
+// from HBM once.  VPL == 0 streams the row twice (rows longer than 32 * 512).
+// ---------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(256) void k_quant_token(const uint4* __restrict__ x,
+                                                     uint2* __restrict__ q,
+                                                     float* __restrict__ s, int64_t M,
+                                                     int64_t V) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // whole wave leaves together
+    const uint4* xr = x + row * V;
+    uint2* qr = q + row * V;
+    if constexpr (VPL > 0) {
+        uint4 v[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int64_t idx = lane + 64 * i;
+            v[i] = idx < V ? xr[idx] : make_uint4(0, 0, 0, 0);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float f[8];
+            unpack8(v[i], f);
+            m = fmaxf(m, amax8(f));
+        }
+        const GroupDiv g = group_div(max_wave(m));
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int64_t idx = lane + 64 * i;
+            if (idx < V) {
+                float f[8];
+                unpack8(v[i], f);
+                qr[idx] = encode8(f, g);
+            }
+        }
+        if (lane == 0) s[row] = g.s;
+    } else {
+        float m = 0.0f;
+        for (int64_t idx = lane; idx < V; idx += 64) {
+            float f[8];
+            unpack8(xr[idx], f);
+            m = fmaxf(m, amax8(f));
+        }
+        const GroupDiv g = group_div(max_wave(m));
+        for (int64_t idx = lane; idx < V; idx += 64) {
+            float f[8];
+            unpack8(xr[idx], f);
+            qr[idx] = encode8(f, g);
+        }
+        if (lane == 0) s[row] = g.s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + quantization, one wave per row.
+//   sum of squares: lane l adds, in order, the squares of its vectors
+//   l, l+64, ... (elements 8v .. 8v+7 in order), then the 64 lane partials are
+//   combined by the halving tree; mean = S / K; inv = 1 / sqrt(mean + eps);
+//   y = bf16_rne((x * inv) * gamma), all single fp32 operations (the library is
+//   built without FMA contraction).  y stays in registers and is quantized per
+//   row (GROUP == 0) or per 1x128 group (GROUP == 128): with vector v held by
+//   lane v % 64, a 128-element group is 16 adjacent lanes of one step.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rms_y8(const uint4& xv, const uint4& gv, float inv,
+                                       float (&y)[8]) {
+    float f[8], g[8];
+    unpack8(xv, f);
+    unpack8(gv, g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = bf16_round((f[j] * inv) * g[j]);
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&y)[8]) {
+    // y already holds bf16 values; keep their upper halves
+    uint4 o;
+    o.x = (__float_as_uint(y[0]) >> 16) | (__float_as_uint(y[1]) & 0xFFFF0000u);
+    o.y = (__float_as_uint(y[2]) >> 16) | (__float_as_uint(y[3]) & 0xFFFF0000u);
+    o.z = (__float_as_uint(y[4]) >> 16) | (__float_as_uint(y[5]) & 0xFFFF0000u);
+    o.w = (__float_as_uint(y[6]) >> 16) | (__float_as_uint(y[7]) & 0xFFFF0000u);
+    return o;
+}
+
+__device__ __forceinline__ float sumsq8(float p, const uint4& xv) {
+    float f[8];
+    unpack8(xv, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p = p + f[j] * f[j];
+    return p;
+}
+
+template <int VPL, int GROUP>
+__global__ __launch_bounds__(256) void k_rmsnorm_quant(uint2* __restrict__ q,
+                                                       const uint4* __restrict__ x,
+                                                       float* __restrict__ s,
+                                                       const uint4* __restrict__ gamma,
+                                                       float eps, int64_t M, int64_t V) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const uint4* xr = x + row * V;
+    uint2* qr = q + row * V;
+    const float kf = (float)(V * 8);
+    if constexpr (VPL > 0) {
+        uint4 v[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int64_t idx = lane + 64 * i;
+            v[i] = idx < V ? xr[idx] : make_uint4(0, 0, 0, 0);
+        }
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (lane + 64 * i < V) p = sumsq8(p, v[i]);
+        const float S = tree_sum_wave(p);
+        const float inv = 1.0f / sqrtf(S / kf + eps);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int64_t idx = lane + 64 * i;
+            float y[8];
+            rms_y8(v[i], idx < V ? gamma[idx] : make_uint4(0, 0, 0, 0), inv, y);
+            v[i] = pack_bf16x8(y);  // keep y (bf16) in place of x
+            if constexpr (GROUP == 0) m = fmaxf(m, amax8(y));
+        }
+        if constexpr (GROUP == 0) {
+            const GroupDiv g = group_div(max_wave(m));
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int64_t idx = lane + 64 * i;
+                if (idx < V) {
+                    float y[8];
+                    unpack8(v[i], y);
+                    qr[idx] = encode8(y, g);
+                }
+            }
+            if (lane == 0) s[row] = g.s;
+        } else {
+            const int64_t groups = V / 16;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int64_t idx = lane + 64 * i;
+                float y[8];
+                unpack8(v[i], y);
+                const GroupDiv g = group_div(max_16lanes(amax8(y)));
+                if (idx < V) {
+                    qr[idx] = encode8(y, g);
+                    if ((lane & 15) == 0) s[row * groups + (idx >> 4)] = g.s;
+                }
+            }
+        }
+    } else {
+        // long rows: sum pass, then y recomputed (bit-identically) per pass
+        float p = 0.0f;
+        for (int64_t idx = lane; idx < V; idx += 64) p = sumsq8(p, xr[idx]);
+        const float S = tree_sum_wave(p);
+        const float inv = 1.0f / sqrtf(S / kf + eps);
+        if constexpr (GROUP == 0) {
+            float m = 0.0f;
+            for (int64_t idx = lane; idx < V; idx += 64) {
+                float y[8];
+                rms_y8(xr[idx], gamma[idx], inv, y);
+                m = fmaxf(m, amax8(y));
+            }
+            const GroupDiv g = group_div(max_wave(m));
+            for (int64_t idx = lane; idx < V; idx += 64) {
+                float y[8];
+                rms_y8(xr[idx], gamma[idx], inv, y);
+                qr[idx] = encode8(y, g);
+            }
+            if (lane == 0) s[row] = g.s;
+        } else {
+            const int64_t groups = V / 16;
+            // V % 16 == 0 here, so every step covers whole groups
+            for (int64_t base = 0; base < V; base += 64) {
+                const int64_t idx = base + lane;
+                float y[8];
+                rms_y8(idx < V ? xr[idx] : make_uint4(0, 0, 0, 0),
+                       idx < V ? gamma[idx] : make_uint4(0, 0, 0, 0), inv, y);
+                const GroupDiv g = group_div(max_16lanes(amax8(y)));
+                if (idx < V) {
+                    qr[idx] = encode8(y, g);
+                    if ((lane & 15) == 0) s[row * groups + (idx >> 4)] = g.s;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks, many weights per launch.  One 256-thread workgroup
+// per block: thread t reads 16 bytes of rows t/16 + 16 i (i = 0..7) at column
+// chunk t % 16, so each wave reads four whole 256-byte row segments per step.
+// FMT 0: fp32 scale; FMT 1: E8M0 byte e + 127 with e = ceil(log2(amax / 448)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int e8m0_exponent(float s) {
+    const uint32_t u = __float_as_uint(s) & 0x7FFFFFFFu;
+    int e;
+    if (u == 0) return -127;
+    const int eb = (int)(u >> 23);
+    const uint32_t m = u & 0x7FFFFFu;
+    if (eb == 0)  // subnormal: s = m * 2^-149; ceil(log2 m) - 149
+        e = (m == 1u ? 0 : 32 - __clz((int)(m - 1u))) - 149;
+    else
+        e = eb - 127 + (m != 0u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_requant(ReqBatch batch) {
+    __shared__ float red[4];
+    const int64_t b = blockIdx.x;
+    // which weight: last descriptor whose first block is <= b (uniform search)
+    int lo = 0, hi = batch.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (batch.d[mid].block_begin <= b) lo = mid; else hi = mid - 1;
+    }
+    const ReqDesc& d = batch.d[lo];
+    const int64_t local = b - d.block_begin;
+    const int64_t bi = local / d.kblocks, bj = local % d.kblocks;
+    const int64_t K = d.K;
+    const int t = threadIdx.x;
+    const int c = t & 15, r0 = t >> 4;
+    const uint16_t* wb = d.w + (bi * 128) * K + bj * 128 + c * 8;
+    uint8_t* qb = d.q + (bi * 128) * K + bj * 128 + c * 8;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const uint4*>(wb + (int64_t)(r0 + 16 * i) * K);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+        m = fmaxf(m, amax8(f));
+    }
+    m = max_wave(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if constexpr (FMT == 0) {
+        const GroupDiv g = group_div(amax);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float f[8];
+            unpack8(v[i], f);
+            *reinterpret_cast<uint2*>(qb + (int64_t)(r0 + 16 * i) * K) = encode8(f, g);
+        }
+        if (t == 0) static_cast<float*>(d.s)[local] = g.s;
+    } else {
+        const int e = e8m0_exponent(amax / 448.0f);
+        // x / 2^e == x * 2^-e exactly (both are the rounding of the same real)
+        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 127]
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float f[8], tq[8];
+            unpack8(v[i], f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) tq[j] = f[j] * inv;
+            *reinterpret_cast<uint2*>(qb + (int64_t)(r0 + 16 * i) * K) = e4m3x8(tq);
+        }
+        if (t == 0) static_cast<uint8_t*>(d.s)[local] = (uint8_t)(e + 127);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostic: encode the fp32 bit patterns first .. first + n - 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_encode_bits(uint64_t first, int64_t n,
+                                                     uint32_t* __restrict__ q) {
+    const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i4 >= n) return;
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __uint_as_float((uint32_t)(first + i4 + j));
+    const uint32_t packed = e4m3x4(f[0], f[1], f[2], f[3]);
+    if (i4 + 4 <= n) {
+        q[i4 >> 2] = packed;
+    } else {
+        uint8_t* qb = reinterpret_cast<uint8_t*>(q);
+        for (int j = 0; i4 + j < n; ++j) qb[i4 + j] = (uint8_t)(packed >> (8 * j));
+    }
+}
+
+template <typename Kern, typename... Args>
+hipError_t launch(Kern k, int64_t blocks, hipStream_t st, Args... args) {
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, st, args...);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s,
+                                 hipStream_t st) {
+    constexpr int U = 4;
+    const int64_t G = M * (K / 128);
+    const int64_t waves = (G + 4 * U - 1) / (4 * U);
+    return launch(k_quant_block<U>, (waves + 3) / 4, st, static_cast<const uint4*>(x),
+                  static_cast<uint2*>(q), s, G);
+}
+
+hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s,
+                                 hipStream_t st) {
+    const int64_t V = K / 8, blocks = (M + 3) / 4;
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint2* qv = static_cast<uint2*>(q);
+    if (V <= 64 * 4) return launch(k_quant_token<4>, blocks, st, xv, qv, s, M, V);
+    if (V <= 64 * 8) return launch(k_quant_token<8>, blocks, st, xv, qv, s, M, V);
+    if (V <= 64 * 16) return launch(k_quant_token<16>, blocks, st, xv, qv, s, M, V);
+    if (V <= 64 * 32) return launch(k_quant_token<32>, blocks, st, xv, qv, s, M, V);
+    return launch(k_quant_token<0>, blocks, st, xv, qv, s, M, V);
+}
+
+hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps,
+                                int64_t M, int64_t K, int group_size, hipStream_t st) {
+    const int64_t V = K / 8, blocks = (M + 3) / 4;
+    uint2* qv = static_cast<uint2*>(q);
+    const uint4* xv = static_cast<const uint4*>(x);
+    const uint4* gv = static_cast<const uint4*>(gamma);
+#define FP8_RMS_CASE(VPL)                                                                   \
+    if (VPL == 0 || V <= 64 * VPL) {                                                        \
+        if (group_size == 0)                                                                \
+            return launch(k_rmsnorm_quant<VPL, 0>, blocks, st, qv, xv, s, gv, eps, M, V);   \
+        return launch(k_rmsnorm_quant<VPL, 128>, blocks, st, qv, xv, s, gv, eps, M, V);     \
+    }
+    FP8_RMS_CASE(4)
+    FP8_RMS_CASE(8)
+    FP8_RMS_CASE(16)
+    FP8_RMS_CASE(32)
+    FP8_RMS_CASE(0)
+#undef FP8_RMS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt,
+                          hipStream_t st) {
+    if (fmt == 0) return launch(k_requant<0>, total_blocks, st, batch);
+    return launch(k_requant<1>, total_blocks, st, batch);
+}
+
+hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st) {
+    const int64_t blocks = (n + 1023) / 1024;
+    return launch(k_encode_bits, blocks, st, first, n, static_cast<uint32_t*>(q));
+}
+
+}  // namespace fp8k

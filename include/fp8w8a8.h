@@ -1,0 +1,192 @@
+/*
+ * fp8w8a8.h -- C ABI of the MI355X (gfx950) FP8 W8A8 quantization and scaled
+ * GEMM library (libfp8w8a8.so).
+ *
+ * What it computes (pages cited by title and section):
+ *   "FP8-RL: A Practical and Stable Low-Precision Stack for LLM RL", abstract,
+ *     contribution (i): rollout with FP8 W8A8 linear layers using blockwise FP8
+ *     quantization, for dense and MoE models; policy weights change every RL
+ *     step, so they are re-quantized before each sync into the engine.
+ *   "[vllm] feat: Support online quant for rollout with torchao", section
+ *     "Test": dynamic FP8 with per-row granularity, float8_e4m3fn for both
+ *     activations and weights, no activation value bounds.
+ *   "[vllm] [ROCm] DeepSeek V4 ... FP8 WO_A 출력 프로젝션 최적화 분석":
+ *     §1 E8M0 power-of-two scales (exponent byte, bias 127, accepted only when
+ *     lossless); §2 weights viewed (groups, out, in) with block scales
+ *     (groups, out/128, in/128), and refusal of shapes not divisible by 128;
+ *     §3 group-128 activation quantization feeding an a8w8 GEMM.
+ *   "[sglang] SGLang의 AMD GPU 최적화: RMSNorm과 FP8 Per-token Quantization 커널
+ *     융합": §1 fused RMSNorm + per-token FP8 quantization called output-first
+ *     (out_fp8, hidden_states, scale, weight, epsilon, group_size = 0);
+ *     §3 the (q, scale) pair passed to a per-token x per-channel a8w8 GEMM
+ *     whose arguments are (A, B, A-scale, B-scale, bias = None, bf16 out).
+ *
+ * Number formats:
+ *   E4M3FN (OCP 8-bit FP): 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
+ *   infinities, max finite 448.  Encoding is round-to-nearest-even and
+ *   saturating (|v| >= 448 -> +-448, never NaN); the sign of zero is kept.
+ *   Scale of a group = amax / 448, one IEEE fp32 division (no clamp); each
+ *   element is the E4M3 encoding of the correctly rounded fp32 quotient x / s.
+ *   An all-zero group has scale 0 and signed-zero codes.
+ *   E8M0: one byte e + 127 meaning 2^e, e = ceil(log2(amax / 448)) clamped to
+ *   [-127, 127]; elements are encoded from x / 2^e (exact).
+ *
+ * Conventions for every call:
+ *   * Tensors are row-major and contiguous, innermost dimension last.  bf16
+ *     and E4M3 data pointers must be 16-byte aligned; fp32 scale pointers
+ *     4-byte aligned; everything except host descriptor tables is device
+ *     memory on the current HIP device.
+ *   * `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it; the call returns before the kernels finish.
+ *   * The caller owns and allocates every buffer; the library allocates no
+ *     device memory and keeps no pointer after the call returns (the kernels
+ *     use the buffers until the stream reaches them).
+ *   * Errors: argument, shape and device checks run on the host before any
+ *     launch; on error nothing is written and a negative fp8_status returns.
+ *     Launch failures return FP8_ERR_LAUNCH.  Faults inside kernels surface
+ *     at the caller's next synchronization of the stream.
+ *   * Empty inputs (M == 0, n == 0, T == 0) are valid and launch nothing.
+ *   * The device must be gfx950 (MI355X); other devices get FP8_ERR_DEVICE so
+ *     the caller can keep its bf16 path (the capability check + fallback of
+ *     the DeepSeek V4 page, §2).
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8W8A8_ABI_VERSION 1
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_ARG = -1,    /* null/invalid pointer or argument, non-NULL bias   */
+    FP8_ERR_SHAPE = -2,  /* a dimension breaks the divisibility rules below   */
+    FP8_ERR_ALIGN = -3,  /* a pointer breaks the alignment rules above        */
+    FP8_ERR_DEVICE = -4, /* no HIP device, or the device is not gfx950        */
+    FP8_ERR_LAUNCH = -5  /* the kernel launch itself failed                   */
+} fp8_status;
+
+typedef enum {
+    FP8_GRAN_BLOCK = 0, /* activations 1x128 groups, weights 128x128 blocks */
+    FP8_GRAN_ROW = 1    /* activations one scale per row (token), weights one
+                           scale per output row (channel)                    */
+} fp8_gran;
+
+typedef enum {
+    FP8_SCALE_F32 = 0, /* fp32 scale amax / 448                           */
+    FP8_SCALE_E8M0 = 1 /* one byte: power-of-two scale 2^(byte - 127)      */
+} fp8_scale_fmt;
+
+/* Version of this header's ABI (FP8W8A8_ABI_VERSION). */
+int fp8_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* fp8_status_string(int status);
+
+/*
+ * 1x128 group quantization of activations ("FP8-RL" abstract (i) blockwise;
+ * DeepSeek V4 page §3 quant_group_size = 128).
+ *   x  : bf16 [M, K]            q : E4M3 [M, K]            s : fp32 [M, K/128]
+ *   s[m][g] = amax(x[m][128g : 128g+128]) / 448.
+ *   K % 128 != 0 -> FP8_ERR_SHAPE.  M may be any value >= 0.
+ */
+int fp8_quantize_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* s,
+                       void* stream);
+
+/*
+ * Per-row quantization: per-token activations, or per-output-channel weights
+ * (torchao PerRow of the verl "Test" section; CHANNEL strategy of the SGLang
+ * page §2).
+ *   x  : bf16 [M, K]            q : E4M3 [M, K]            s : fp32 [M]
+ *   K % 8 != 0 or K == 0 -> FP8_ERR_SHAPE.
+ */
+int fp8_quantize_token(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* s,
+                       void* stream);
+
+/*
+ * Fused RMSNorm + FP8 quantization, output-first as in the SGLang page §1.
+ *   q     : E4M3 [M, K] (out)     x : bf16 [M, K]
+ *   s     : fp32 [M] (group_size 0, per token) or [M, K/128] (group_size 128)
+ *   gamma : bf16 [K]              eps : added to mean(x^2) in fp32
+ *   y = bf16_rne((x * inv) * gamma), inv = 1 / sqrt(S / K + eps), S the fp32
+ *   sum of x^2 in a fixed order: 64 partial sums, partial l adding the squares
+ *   of 8-element vectors l, l+64, l+128, ... in order, combined by a halving
+ *   tree; then y is quantized per token (or per 1x128 group).  Equal to
+ *   RMSNorm -> bf16 -> fp8_quantize_token (or fp8_quantize_block).
+ *   K % 8 != 0 (group_size 0) or K % 128 != 0 (group_size 128) ->
+ *   FP8_ERR_SHAPE; another group_size -> FP8_ERR_ARG.
+ */
+int fp8_rmsnorm_quant(void* q_e4m3, const void* x_bf16, float* s, const void* gamma_bf16,
+                      float eps, int64_t M, int64_t K, int group_size, void* stream);
+
+/* One weight of a re-quantization batch (all pointers device memory). */
+typedef struct {
+    const void* w_bf16; /* [N, K] bf16                                          */
+    void* q_e4m3;       /* [N, K] E4M3 (out)                                    */
+    void* s;            /* [N/128, K/128] fp32, or uint8 E8M0 bytes (out)      */
+    int64_t N;          /* multiple of 128 (a stacked expert tensor [E, N', K]  */
+    int64_t K;          /* with N' % 128 == 0 is passed as N = E * N')          */
+} fp8_weight_desc;
+
+/*
+ * Per-RL-step policy weight re-quantization ("FP8-RL" abstract: weights change
+ * every step and are re-quantized before each sync into the engine): every
+ * descriptor's weight is quantized in 128x128 blocks, with fp32 scales or E8M0
+ * bytes (DeepSeek V4 page §1/§2).  `descs` is a host array of n entries, read
+ * during the call only.  The library enqueues one kernel per 64 descriptors.
+ *   N % 128 or K % 128 != 0 -> FP8_ERR_SHAPE; n < 0 -> FP8_ERR_ARG.
+ */
+int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream);
+
+/*
+ * Scaled W8A8 GEMM, Y = X W^T with bf16 output (SGLang page §3 argument order:
+ * A, B, A-scale, B-scale, bias, out; DeepSeek V4 page §3 for block scales).
+ *   a : E4M3 [M, K]    w : E4M3 [N, K]    y : bf16 [M, N] (out)
+ *   FP8_GRAN_BLOCK: a_s fp32 [M, K/128], w_s fp32 [N/128, K/128],
+ *     Y[m,n] = sum_kb a_s[m,kb] * w_s[n/128,kb] * sum_{k in kb} a[m,k] w[n,k]
+ *   FP8_GRAN_ROW: a_s fp32 [M], w_s fp32 [N],
+ *     Y[m,n] = a_s[m] * w_s[n] * sum_k a[m,k] w[n,k]
+ *   Products are exact, sums fp32 (matrix-core accumulate, block results
+ *   scaled and added in fp32), output rounded to bf16 (nearest even).
+ *   bias must be NULL (FP8_ERR_ARG otherwise).  K % 128 != 0 or
+ *   N % 128 != 0 -> FP8_ERR_SHAPE.  M is any value >= 0.
+ */
+int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
+                         const float* w_s, const void* bias, void* y_bf16, int64_t M,
+                         int64_t N, int64_t K, int gran, void* stream);
+
+/*
+ * Grouped (MoE) block-scaled W8A8 GEMM ("FP8-RL" abstract: MoE models; DeepSeek
+ * V4 page §2 weight view (groups, out, in) and scale view (groups, out/128,
+ * in/128)).  Rows of A are grouped by expert: rows offsets[e] .. offsets[e+1]-1
+ * use expert e's weight.
+ *   a   : E4M3 [T, K]          a_s : fp32 [T, K/128]
+ *   w   : E4M3 [E, N, K]       w_s : fp32 [E, N/128, K/128]
+ *   offsets : int32 [E+1], DEVICE memory, non-decreasing, offsets[0] = 0,
+ *             offsets[E] = T (empty experts allowed).  The kernel reads and
+ *             writes only rows in [0, T) whatever the offsets hold.
+ *   y   : bf16 [T, N] (out); rows covered by no expert are left untouched.
+ *   K % 128 != 0 or N % 128 != 0 -> FP8_ERR_SHAPE; E < 1 -> FP8_ERR_ARG.
+ */
+int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
+                                 const float* w_s, const int32_t* offsets, void* y_bf16,
+                                 int64_t T, int64_t E, int64_t N, int64_t K, void* stream);
+
+/*
+ * Diagnostic: the device E4M3 encoder alone.  q[i] = E4M3(float with bit
+ * pattern first_bits + i) for 0 <= i < n (n <= 2^32 - first_bits), so that a
+ * test can compare the encoder used by every quantizer above on all 2^32 fp32
+ * patterns.
+ *   q : uint8 [n] device memory, 16-byte aligned.
+ */
+int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8W8A8_H */

@@ -1,0 +1,54 @@
+"""Helpers for the GPU parity tests (GPU side via the C ABI, oracle on the CPU)."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import fp8_w8a8_quantized_amd as fp8
+
+# GEMM pass criterion: per output row, max |gpu - oracle| <= 1e-2 * max |oracle row|
+GEMM_ROW_TOL = 1e-2
+
+
+def ensure_library():
+    if not os.path.exists(fp8.library_path()):
+        from fp8_w8a8_quantized_amd import build
+
+        build.build()
+    fp8.load_library()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def say(msg: str) -> None:
+    """Name the case on stdout before a GPU step (flushed)."""
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def assert_rows_close(y_gpu: torch.Tensor, ref: np.ndarray, rows=None, what=""):
+    """y_gpu bf16 [R, N] (or the listed rows of it) vs fp64 oracle [R', N]."""
+    y = y_gpu if rows is None else y_gpu[torch.as_tensor(rows, device=y_gpu.device)]
+    got = host(y.float()).astype(np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = np.abs(got - ref).max(axis=1)
+    rowmax = np.abs(ref).max(axis=1)
+    bad = np.nonzero(err > GEMM_ROW_TOL * rowmax)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} rows out of tolerance, first {bad[:8]}, "
+                           f"worst ratio {float((err / np.maximum(rowmax, 1e-300)).max()):.3e}")
+    return float((err / np.maximum(rowmax, 1e-300)).max())
+
+
+def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
+    """First, last and n random distinct rows of [0, M), sorted."""
+    rng = np.random.default_rng(seed)
+    pick = set([0, M - 1]) | set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)

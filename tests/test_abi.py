@@ -1,0 +1,144 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/fp8w8a8.h declares, and its host-side validation returns the
+documented status codes before touching the device (on a machine without a
+GPU, valid arguments reach the device check and get FP8_ERR_DEVICE).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_w8a8_quantized_amd as fp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w8a8.h")
+
+OK, ARG, SHAPE, ALIGN, DEVICE, LAUNCH = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fp8.library_path()):
+        from fp8_w8a8_quantized_amd import build
+
+        build.build()
+    return fp8.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fp8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = _declared_functions()
+    for required in ("fp8_quantize_block", "fp8_quantize_token", "fp8_rmsnorm_quant",
+                     "fp8_requantize_weights", "fp8_gemm_a8w8_scaled",
+                     "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
+                     "fp8_encode_f32_bits"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", fp8.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8_abi_version() == 1
+    for st in (OK, ARG, SHAPE, ALIGN, DEVICE, LAUNCH):
+        assert fp8.status_string(st) and fp8.status_string(st) != "unknown status"
+    assert fp8.status_string(123) == "unknown status"
+
+
+def _gpu():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-null address, never dereferenced on error paths
+
+
+def test_quantize_validation(L):
+    vp = ctypes.c_void_p
+    assert L.fp8_quantize_block(vp(FAKE), 4, 200, vp(FAKE), vp(FAKE), None) == SHAPE
+    assert L.fp8_quantize_block(vp(FAKE), 4, 0, vp(FAKE), vp(FAKE), None) == SHAPE
+    assert L.fp8_quantize_block(vp(FAKE), -1, 128, vp(FAKE), vp(FAKE), None) == ARG
+    assert L.fp8_quantize_block(None, 4, 128, vp(FAKE), vp(FAKE), None) == ARG
+    assert L.fp8_quantize_block(vp(FAKE + 2), 4, 128, vp(FAKE), vp(FAKE), None) == ALIGN
+    assert L.fp8_quantize_block(vp(FAKE), 0, 128, None, None, None) == OK  # empty
+    assert L.fp8_quantize_token(vp(FAKE), 4, 12, vp(FAKE), vp(FAKE), None) == SHAPE
+    assert L.fp8_quantize_token(vp(FAKE), 4, 16, vp(FAKE), vp(FAKE + 1), None) == ALIGN
+    assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 16, 64,
+                               None) == ARG
+    assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 136, 128,
+                               None) == SHAPE
+    assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), None, 1e-6, 4, 16, 0, None) == ARG
+    if not _gpu():
+        assert L.fp8_quantize_block(vp(FAKE), 4, 128, vp(FAKE), vp(FAKE), None) == DEVICE
+        assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 16, 0,
+                                   None) == DEVICE
+
+
+def test_gemm_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, f, f, 16, 256, 256, 0, None) == ARG  # bias
+    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 200, 256, 0, None) == SHAPE
+    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 200, 1, None) == SHAPE
+    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 256, 7, None) == ARG
+    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, vp(FAKE + 8), 16, 256, 256, 0, None) == ALIGN
+    assert L.fp8_gemm_a8w8_scaled(None, None, None, None, None, None, 0, 256, 256, 0, None) == OK
+    assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 0, 256, 256, None) == ARG
+    assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 4, 256, 100, None) == SHAPE
+    assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, vp(FAKE + 2), f, 64, 4, 256, 256,
+                                          None) == ALIGN
+    if not _gpu():
+        assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 256, 0, None) == DEVICE
+
+
+def test_requant_validation(L):
+    D = fp8._WeightDesc
+    good = D(FAKE, FAKE, FAKE, 256, 256)
+    bad_shape = D(FAKE, FAKE, FAKE, 200, 256)
+    bad_align = D(FAKE + 4, FAKE, FAKE, 256, 256)
+    arr = (D * 2)(good, bad_shape)
+    assert L.fp8_requantize_weights(arr, 2, 0, None) == SHAPE
+    arr = (D * 2)(good, bad_align)
+    assert L.fp8_requantize_weights(arr, 2, 1, None) == ALIGN
+    assert L.fp8_requantize_weights(arr, 2, 5, None) == ARG
+    assert L.fp8_requantize_weights(None, 0, 0, None) == OK
+    assert L.fp8_requantize_weights(None, -1, 0, None) == ARG
+    if not _gpu():
+        arr = (D * 1)(good)
+        assert L.fp8_requantize_weights(arr, 1, 0, None) == DEVICE
+
+
+def test_encode_validation(L):
+    vp = ctypes.c_void_p
+    assert L.fp8_encode_f32_bits(1 << 32, 1, vp(FAKE), None) == ARG
+    assert L.fp8_encode_f32_bits(0xFFFFFFFF, 2, vp(FAKE), None) == ARG
+    assert L.fp8_encode_f32_bits(0, 16, vp(FAKE + 3), None) == ALIGN
+
+
+def test_quotient_path_equals_ieee_division_exhaustively(tmp_path):
+    """The quantizers' reciprocal-corrected quotient equals IEEE x / s on every
+    (bf16 x, bf16 amax) pair with |x| <= amax (host build of the same code)."""
+    src = os.path.join(ROOT, "tests", "native", "quotient_check.cpp")
+    exe = str(tmp_path / "quotient_check")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-mfma", src,
+                    "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches 0" in r.stdout

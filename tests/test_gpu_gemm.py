@@ -1,0 +1,168 @@
+"""GPU parity of the scaled GEMMs against the oracle's fp64 dequantize-then-
+multiply: per output row, max |gpu - oracle| <= 1e-2 * max |oracle row|.
+
+The GPU side quantizes and multiplies with the library; the oracle quantizes
+the same bf16 inputs itself and multiplies in fp64.  Shapes: small ones that
+span several 128 x 128 tiles with ragged M, the tiny linear, every dense
+linear at M = 256 and M = 8192 (sampled rows), the per-row workload
+(RMSNorm + per-token activations x per-row weights), and the MoE grouped GEMM
+at full size (sampled rows, at least one per expert) plus small ragged cases
+with empty experts.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_quantized_amd as fp8
+import oracle
+import synth
+from tests.gpu_util import assert_rows_close, dev, ensure_library, host, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+def _block_pipeline(X, W, rows=None):
+    """GPU: quantize X (1x128) and W (128x128), GEMM.  Oracle: same from bf16."""
+    qa, sa = fp8.quantize_block(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev()) if not W.is_cuda else W], fp8.SCALE_F32)
+    y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)
+    Xh = X if rows is None else X[torch.as_tensor(rows)]
+    oqa, osa = oracle.quantize_block(Xh)
+    oqw, osw = oracle.quantize_weight_block(W.cpu(), 0)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_BLOCK)
+    return y, ref
+
+
+def test_tiny_linear():
+    say("block GEMM tiny 16x256x256")
+    X, W = synth.tiny_linear(seed=0)
+    y, ref = _block_pipeline(X, W)
+    assert_rows_close(y, ref, what="tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (16, 256, 256), (130, 384, 512),
+                                   (300, 256, 1024), (257, 128, 4096), (64, 640, 384)])
+def test_block_small_shapes(M, N, K):
+    say(f"block GEMM {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + N + K)
+    W = synth.weight(N, K, seed=N + K)
+    y, ref = _block_pipeline(X, W)
+    assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (130, 384, 512), (77, 256, 5120)])
+def test_row_small_shapes(M, N, K):
+    say(f"row GEMM {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + 3)
+    W = synth.weight(N, K, seed=K + 5)
+    qa, sa = fp8.quantize_token(X.to(dev()))
+    qw, sw = fp8.quantize_token(W.to(dev()))
+    y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_ROW)
+    oqa, osa = oracle.quantize_token(X)
+    oqw, osw = oracle.quantize_token(W)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_ROW)
+    assert_rows_close(y, ref, what=f"row {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name", list(synth.DENSE_SHAPES))
+@pytest.mark.parametrize("M", synth.DENSE_M)
+def test_dense_linears_full_size_sampled(name, M):
+    N, K = synth.DENSE_SHAPES[name]
+    say(f"block GEMM {name} M={M} ({M}x{N}x{K}), sampled rows")
+    X, W = synth.dense_linear(name, M, seed=11)
+    rows = sample_rows(M, 24, seed=M + N)
+    y, ref = _block_pipeline(X, W, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what=f"{name} M={M}")
+
+
+def test_ragged_m_full_k():
+    M, N, K = 8192 + 37, 512, 12288
+    say(f"block GEMM ragged {M}x{N}x{K}, sampled rows incl. the last tile")
+    X = synth.act_col_outliers(M, K, seed=5)
+    W = synth.weight(N, K, seed=6)
+    rows = np.unique(np.concatenate([sample_rows(M, 16, seed=1), np.arange(M - 40, M)]))
+    y, ref = _block_pipeline(X, W, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what="ragged")
+
+
+def test_rms_row_workload_full_size_sampled():
+    say("rmsnorm_quant -> row GEMM 4096x12288x5120, sampled rows")
+    h, gamma = synth.rms_inputs(seed=0)
+    W = synth.weight(synth.RMS_N, synth.RMS_K, seed=21)
+    qa, sa = fp8.rmsnorm_quant(h.to(dev()), gamma.to(dev()), synth.RMS_EPS, 0)
+    qw, sw = fp8.quantize_token(W.to(dev()))
+    y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_ROW)
+    rows = sample_rows(4096, 24, seed=3)
+    oqa, osa = oracle.rmsnorm_quant(h[torch.as_tensor(rows)], gamma, synth.RMS_EPS)
+    oqw, osw = oracle.quantize_token(W)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_ROW)
+    assert_rows_close(y, ref, rows=rows, what="rms row")
+
+
+def _grouped_pipeline(A, W, offsets, rows=None):
+    E, N, K = W.shape
+    qa, sa = fp8.quantize_block(A.to(dev()))
+    Wd = W.to(dev()) if not W.is_cuda else W
+    (qw, sw), = fp8.requantize_weights([Wd.reshape(E * N, K)], fp8.SCALE_F32)
+    qw = qw.view(E, N, K)
+    sw = sw.view(E, N // 128, K // 128)
+    off = torch.as_tensor(offsets, dtype=torch.int32, device=dev())
+    y = fp8.grouped_gemm_a8w8_scaled((qa, sa), (qw, sw), off)
+    T = A.shape[0]
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows)
+    oqa, osa = oracle.quantize_block(A[torch.as_tensor(rows)])
+    expert_of = np.searchsorted(np.asarray(offsets), rows, side="right") - 1
+    ref = np.zeros((rows.size, N))
+    for e in np.unique(expert_of):
+        sel = np.nonzero(expert_of == e)[0]
+        oqw, osw = oracle.quantize_weight_block(W[int(e)].cpu(), 0)
+        ref[sel] = oracle.gemm(oqa[sel], oqw, osa[sel], osw, oracle.GRAN_BLOCK)
+    return y, ref, rows
+
+
+def test_grouped_small_with_empty_experts():
+    say("grouped GEMM small, empty experts")
+    counts = [130, 0, 7, 0, 256, 1]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T, N, K = int(offsets[-1]), 256, 384
+    A = synth.act_col_outliers(T, K, seed=8)
+    W = synth.normal_bf16((len(counts), N, K), seed=9, std=0.02)
+    y, ref, rows = _grouped_pipeline(A, W, offsets)
+    assert_rows_close(y, ref, what="grouped small")
+
+
+def test_grouped_rows_outside_offsets_untouched():
+    say("grouped GEMM rows past offsets[E] untouched")
+    offsets = np.array([0, 5, 5, 40], np.int32)
+    T, N, K = 64, 128, 256
+    A = synth.act_col_outliers(T, K, seed=1)
+    W = synth.normal_bf16((3, N, K), seed=2, std=0.02)
+    qa, sa = fp8.quantize_block(A.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.reshape(3 * N, K).to(dev())], fp8.SCALE_F32)
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device=dev())
+    off = torch.as_tensor(offsets, device=dev())
+    fp8.grouped_gemm_a8w8_scaled((qa, sa), (qw.view(3, N, K), sw.view(3, 1, 2)), off, out=y)
+    assert torch.all(y[40:] == 7.0)
+    assert not torch.all(y[:40] == 7.0)
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_grouped_moe_full_size_sampled(which):
+    say(f"grouped GEMM MoE {which} full size, sampled rows (>= 1 per expert)")
+    A, W, offsets = synth.moe_inputs(which, seed=0)
+    rng = np.random.default_rng(4)
+    rows = []
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            rows += [a, b - 1, int(rng.integers(a, b))]
+    rows = np.unique(np.array(rows))
+    y, ref, rows = _grouped_pipeline(A, W, offsets, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what=f"moe {which}")

@@ -1,0 +1,230 @@
+"""GPU parity of the quantizers against the CPU oracle: bit-exact E4M3 bytes
+and scales (fp32 bits or E8M0 bytes), through the C ABI.
+
+Sizes: small shapes that span several groups/rows with ragged edges, the
+special groups (all zero, signed zero, subnormal amax, constant magnitude),
+and the full workload sizes (dense linears at M = 8192, the MoE activations,
+the rmsnorm workload [4096, 5120], the per-row weight [12288, 5120], the
+36-layer policy) with the oracle run on sampled rows or block rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_w8a8_quantized_amd as fp8
+import oracle
+import synth
+from tests.gpu_util import dev, ensure_library, host, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+def _eq_block(xb: torch.Tensor, rows=None):
+    q, s = fp8.quantize_block(xb.to(dev()))
+    xh = xb if rows is None else xb[torch.as_tensor(rows)]
+    oq, os_ = oracle.quantize_block(xh)
+    gq, gs = host(q), host(s)
+    if rows is not None:
+        gq, gs = gq[rows], gs[rows]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+def test_block_tiny_linear_input():
+    say("quantize_block tiny X [16, 256]")
+    X, _ = synth.tiny_linear(seed=0)
+    _eq_block(X)
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (37, 384), (64, 4096), (130, 12288),
+                                 (5, 640)])
+def test_block_shapes(M, K):
+    say(f"quantize_block [{M}, {K}]")
+    _eq_block(synth.act_col_outliers(M, K, seed=M + K))
+
+
+def test_block_special_groups():
+    say("quantize_block special groups")
+    x = np.zeros((6, 512), np.float32)
+    x[0, 128:256] = -0.0
+    x[1, :128] = 3.0
+    x[1, 1:128:2] = -3.0
+    x[2, 5] = -(2.0 ** -66)
+    x[3, :] = np.float32(2.0 ** -133)           # bf16 subnormal: subnormal fp32 scale
+    x[4, :] = np.float32(2.0 ** -70)             # scale below the reciprocal path's bound
+    x[4, 7] = np.float32(-(2.0 ** -69))
+    x[5, :] = np.float32(3.3895313892515355e38)  # largest bf16
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    _eq_block(xt)
+
+
+@pytest.mark.parametrize("M,K", [(8192, 4096), (8192, 12288), (32768, 2048), (32768, 768)])
+def test_block_full_size_sampled(M, K):
+    say(f"quantize_block full [{M}, {K}] sampled rows")
+    X = synth.act_col_outliers(M, K, seed=1)
+    _eq_block(X, rows=sample_rows(M, 96, seed=M + K))
+
+
+def test_block_deterministic():
+    say("quantize_block determinism")
+    X = synth.act_col_outliers(512, 4096, seed=3).to(dev())
+    q1, s1 = fp8.quantize_block(X)
+    q2, s2 = fp8.quantize_block(X)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+def _eq_token(x: torch.Tensor, rows=None):
+    q, s = fp8.quantize_token(x.to(dev()))
+    xh = x if rows is None else x[torch.as_tensor(rows)]
+    oq, os_ = oracle.quantize_token(xh)
+    gq, gs = host(q), host(s)
+    if rows is not None:
+        gq, gs = gq[rows], gs[rows]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (5, 200), (33, 4096), (64, 5120), (3, 12288),
+                                 (17, 20000), (2, 16384)])
+def test_token_shapes(M, K):
+    say(f"quantize_token [{M}, {K}]")
+    _eq_token(synth.act_col_outliers(M, K, seed=M * 7 + K))
+
+
+def test_token_full_size_weight_sampled():
+    say("quantize_token full W [12288, 5120] sampled rows")
+    W = synth.weight(12288, 5120, seed=5)
+    _eq_token(W, rows=sample_rows(12288, 128, seed=9))
+
+
+def _eq_rms(h, gamma, group_size, eps=1e-6, rows=None):
+    q, s = fp8.rmsnorm_quant(h.to(dev()), gamma.to(dev()), eps, group_size)
+    hh = h if rows is None else h[torch.as_tensor(rows)]
+    if group_size == 0:
+        oq, os_ = oracle.rmsnorm_quant(hh, gamma, eps)
+    else:  # fused group variant == RMSNorm -> bf16 -> 1x128 quantization
+        y = oracle.rmsnorm_bf16(hh, gamma, eps)
+        oq, os_ = oracle.quantize_block(y)
+    gq, gs = host(q), host(s)
+    if rows is not None:
+        gq, gs = gq[rows], gs[rows]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+def test_rmsnorm_quant_full_workload():
+    say("rmsnorm_quant full [4096, 5120], per token")
+    h, gamma = synth.rms_inputs(seed=0)
+    _eq_rms(h, gamma, 0)
+
+
+@pytest.mark.parametrize("M,K,gs", [(3, 8, 0), (7, 200, 0), (5, 4096, 0), (9, 12288, 0),
+                                    (4, 40000, 0), (6, 256, 128), (33, 5120, 128),
+                                    (3, 40064, 128)])
+def test_rmsnorm_quant_shapes(M, K, gs):
+    say(f"rmsnorm_quant [{M}, {K}] group_size {gs}")
+    h, gamma = synth.rms_inputs(M=M, K=K, seed=M + K)
+    _eq_rms(h, gamma, gs)
+
+
+def test_rmsnorm_quant_group128_full_workload_sampled():
+    say("rmsnorm_quant full [4096, 5120], group_size 128, sampled rows")
+    h, gamma = synth.rms_inputs(seed=1)
+    _eq_rms(h, gamma, 128, rows=sample_rows(4096, 128, seed=2))
+
+
+def _eq_req(ws, fmt, out=None, block_rows=None):
+    res = fp8.requantize_weights([w.to(dev()) if not w.is_cuda else w for w in ws], fmt)
+    for i, (w, (q, s)) in enumerate(zip(ws, res)):
+        if block_rows is None:
+            wh = w.cpu()
+            gq, gs = host(q), host(s)
+        else:
+            br = block_rows[i]
+            wh = w[br * 128:(br + 1) * 128].cpu()
+            gq = host(q[br * 128:(br + 1) * 128])
+            gs = host(s[br:br + 1])
+        oq, os_ = oracle.quantize_weight_block(wh, fmt)
+        assert np.array_equal(gq, oq), f"weight {i}: codes differ at {np.argwhere(gq != oq)[:5]}"
+        if fmt == 0:
+            assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), f"weight {i} scales"
+        else:
+            assert np.array_equal(gs, os_), f"weight {i} E8M0 bytes"
+            p2 = np.ldexp(np.float32(1.0), gs.astype(np.int32) - 127).astype(np.float32)
+            codes = oracle.e8m0_lossless(p2)
+            assert codes is not None and np.array_equal(codes.reshape(gs.shape), gs)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_requant_small_batch(fmt):
+    say(f"requantize_weights small batch fmt {fmt}")
+    _, W0 = synth.tiny_linear(seed=0)
+    ws = [W0, synth.weight(384, 640, seed=2), synth.weight(128, 128, seed=3),
+          synth.weight(1536 * 3, 2048, seed=4)]  # last: three stacked experts
+    z = torch.zeros((256, 256), dtype=torch.bfloat16)
+    z[128:, :128] = 1e-30
+    ws.append(z)
+    _eq_req(ws, fmt)
+
+
+def test_requant_more_descriptors_than_one_launch():
+    say("requantize_weights 70 descriptors")
+    ws = [synth.weight(128, 128 * (1 + i % 3), seed=100 + i) for i in range(70)]
+    _eq_req(ws, 0)
+    _eq_req(ws, 1)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_requant_full_policy_sampled(fmt):
+    say(f"requantize_weights full 36-layer policy fmt {fmt}, sampled block rows")
+    ws, rows = [], []
+    rng = np.random.default_rng(fmt)
+    for layer in range(synth.POLICY_LAYERS):
+        for j, (name, (N, K)) in enumerate(synth.DENSE_SHAPES.items()):
+            ws.append(synth.weight(N, K, seed=1000 + 4 * layer + j, device=dev()))
+            rows.append(int(rng.integers(0, N // 128)))
+    res = fp8.requantize_weights(ws, fmt)
+    torch.cuda.synchronize()
+    pick = [0, 1, 2, 3, 70, 141, 142, 143]
+    for i in pick:
+        br = rows[i]
+        wh = ws[i][br * 128:(br + 1) * 128].cpu()
+        oq, os_ = oracle.quantize_weight_block(wh, fmt)
+        q, s = res[i]
+        assert np.array_equal(host(q[br * 128:(br + 1) * 128]), oq), f"tensor {i}"
+        gs = host(s[br:br + 1])
+        if fmt == 0:
+            assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+        else:
+            assert np.array_equal(gs, os_)
+    del ws, res
+    torch.cuda.empty_cache()
+
+
+def test_error_leaves_outputs_untouched():
+    say("error paths leave outputs untouched")
+    L = fp8.load_library()
+    x = torch.ones((4, 200), dtype=torch.bfloat16, device=dev())
+    q = torch.full((4, 200), 0xAB, dtype=torch.uint8, device=dev())
+    s = torch.full((4, 2), 7.0, dtype=torch.float32, device=dev())
+    import ctypes
+
+    rc = L.fp8_quantize_block(ctypes.c_void_p(x.data_ptr()), 4, 200, ctypes.c_void_p(q.data_ptr()),
+                              ctypes.c_void_p(s.data_ptr()), None)
+    assert rc == -2
+    assert torch.all(q == 0xAB) and torch.all(s == 7.0)
+
+
+def test_forced_foreign_arch_is_refused(monkeypatch):
+    say("FP8W8A8_FORCE_ARCH refusal")
+    monkeypatch.setenv("FP8W8A8_FORCE_ARCH", "gfx942")
+    x = torch.ones((4, 128), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(fp8.Fp8Error) as ei:
+        fp8.quantize_block(x)
+    assert ei.value.status == -4
