@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 W8A8 hot path on one MI355X.
+
+One step = one RL step's worth of the hot path over a 36-layer Qwen3-8B-shaped
+policy (qkv 4096->6144, o 4096->4096, gate_up 4096->24576, down 12288->4096):
+  1. re-quantize all 144 bf16 policy weights into E4M3 128x128 blocks with fp32
+     scales (one batched library call);
+  2. for every layer and linear, quantize that layer's bf16 activations in 1x128
+     groups and run the block-scaled W8A8 GEMM, bf16 out -- at M = 8192 (prefill)
+     and at M = 256 (decode).
+Every (layer, linear) has its own weight and activation tensors, so weights
+and activations stream from HBM as they would in a real forward pass.  Inputs
+are seeded synthetic tensors generated on the device before timing.
+
+Prints one JSON line.  ``value`` = all GEMM flops of a step / wall time of a
+step (the quantization work in the step is not counted as flops but its time
+is).  ``roofline`` is for the dominant kernel, the block-scaled GEMM at
+M = 8192, timed with HIP events on the launch stream inside the timed steps.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+METRIC = "block-scaled FP8 GEMM TFLOPS (% FP8 MFMA peak); quantize/requant GB/s (% HBM)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(rows: int):
+    """The oracle (as it stands) on a bounded sample of one step: re-quantize
+    one layer's four bf16 weights, quantize `rows` rows of each M = 8192
+    activation, fp64 GEMM of those rows.  Reported in GEMM TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    inputs = []
+    for j, name in enumerate(synth.DENSE_SHAPES):
+        N, K = synth.DENSE_SHAPES[name]
+        X = synth.act_col_outliers(rows, K, seed=500 + j)
+        W = synth.weight(N, K, seed=600 + j)
+        inputs.append((X, W))
+    flops = 0.0
+    t0 = time.perf_counter()
+    for X, W in inputs:
+        qw, sw = oracle.quantize_weight_block(W, 0)
+        qa, sa = oracle.quantize_block(X)
+        y = oracle.gemm(qa, qw, sa, sw, oracle.GRAN_BLOCK)
+        flops += 2.0 * y.shape[0] * y.shape[1] * qa.shape[1]
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": max(omp, blas),
+        "kind": "oracle",
+        "sample": (f"one layer of the step: requantize the 4 bf16 weights (128x128, fp32 "
+                   f"scales), 1x128-quantize {rows} rows of each M=8192 activation, fp64 "
+                   f"dequantize-then-matmul of those rows; {flops / 1e9:.1f} GFLOP in "
+                   f"{dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(the sharded path is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+
+    import torch
+
+    import fp8_w8a8_quantized_amd as fp8
+    import synth
+
+    L = fp8.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    vp = ctypes.c_void_p
+
+    shapes = list(synth.DENSE_SHAPES.items())
+    Ms = synth.DENSE_M
+    layers = args.layers
+
+    # ---- inputs (device-generated, seeded) and preallocated outputs ----
+    W, Wq, Ws = [], [], []
+    X, Xq, Xs = {}, {}, {}
+    Y = {}
+    for li in range(layers):
+        for j, (name, (N, K)) in enumerate(shapes):
+            W.append(synth.weight(N, K, seed=10_000 + 4 * li + j, device=dev))
+            Wq.append(torch.empty((N, K), dtype=torch.uint8, device=dev))
+            Ws.append(torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev))
+            for M in Ms:
+                X[(li, j, M)] = synth.act_col_outliers(M, K, seed=20_000 + 8 * li + 2 * j + M,
+                                                       device=dev)
+                Xq[(li, j, M)] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                Xs[(li, j, M)] = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    for j, (name, (N, K)) in enumerate(shapes):
+        for M in Ms:
+            Y[(j, M)] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    descs = (fp8._WeightDesc * len(W))()
+    for i in range(len(W)):
+        descs[i] = fp8._WeightDesc(W[i].data_ptr(), Wq[i].data_ptr(), Ws[i].data_ptr(),
+                                   W[i].shape[0], W[i].shape[1])
+    torch.cuda.synchronize(dev)
+
+    # ---- pre-marshalled calls of one step, grouped by kernel category ----
+    calls = [("requant", L.fp8_requantize_weights, (descs, len(W), fp8.SCALE_F32, sptr))]
+    for li in range(layers):
+        for j, (name, (N, K)) in enumerate(shapes):
+            wi = 4 * li + j
+            for M in Ms:
+                key = (li, j, M)
+                calls.append((f"quant_m{M}", L.fp8_quantize_block,
+                              (vp(X[key].data_ptr()), M, K, vp(Xq[key].data_ptr()),
+                               vp(Xs[key].data_ptr()), sptr)))
+                calls.append((f"gemm_m{M}", L.fp8_gemm_a8w8_scaled,
+                              (vp(Xq[key].data_ptr()), vp(Wq[wi].data_ptr()),
+                               vp(Xs[key].data_ptr()), vp(Ws[wi].data_ptr()), None,
+                               vp(Y[(j, M)].data_ptr()), M, N, K, fp8.GRAN_BLOCK, sptr)))
+
+    # algorithmic work per step, per category
+    work = {"requant": {"bytes": 0.0}, "gemm_m8192": {"flops": 0.0, "bytes": 0.0},
+            "gemm_m256": {"flops": 0.0, "bytes": 0.0}, "quant_m8192": {"bytes": 0.0},
+            "quant_m256": {"bytes": 0.0}}
+    for li in range(layers):
+        for (name, (N, K)) in shapes:
+            work["requant"]["bytes"] += 2 * N * K + N * K + 4 * (N // 128) * (K // 128)
+            for M in Ms:
+                work[f"quant_m{M}"]["bytes"] += 2 * M * K + M * K + 4 * M * (K // 128)
+                g = work[f"gemm_m{M}"]
+                g["flops"] += 2.0 * M * N * K
+                g["bytes"] += M * K + N * K + 4 * (M * (K // 128) + (N // 128) * (K // 128)) \
+                    + 2 * M * N
+    launches = {"requant": 1}
+    for M in Ms:
+        launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
+
+    def run_step(events=None):
+        for cat, fn, a in calls:
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            rc = fn(*a)
+            if rc != 0:
+                raise fp8.Fp8Error(cat, rc, fp8.status_string(rc))
+            if events is not None:
+                e1.record(stream)
+                events.append((cat, e0, e1))
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize(dev)
+
+    # ---- timed region: exactly `steps` steps, wall clock, synchronized ----
+    events = []
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(events)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+
+    per_cat_ms = {}
+    for cat, e0, e1 in events:
+        per_cat_ms[cat] = per_cat_ms.get(cat, 0.0) + e0.elapsed_time(e1)
+    ms_per_step = elapsed * 1e3 / args.steps
+    total_flops = work["gemm_m8192"]["flops"] + work["gemm_m256"]["flops"]
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    breakdown = {}
+    for cat, w in work.items():
+        ms = per_cat_ms.get(cat, 0.0) / args.steps  # per step, summed over launches
+        d = {"ms_per_step": round(ms, 4), "launches_per_step": launches[cat],
+             "avg_launch_us": round(ms * 1e3 / launches[cat], 3)}
+        if "flops" in w:
+            d["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 2)
+            d["frac_fp8_peak"] = round(d["tflops"] / PEAK_FP8_TFLOPS, 4)
+        d["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
+        d["frac_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        breakdown[cat] = d
+
+    dom = breakdown["gemm_m8192"]
+    flops_per_launch = work["gemm_m8192"]["flops"] / launches["gemm_m8192"]
+    achieved = flops_per_launch / (dom["avg_launch_us"] * 1e-6) / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+        "kernel": "block-scaled FP8 GEMM (k_gemm<BLOCK>), M=8192 launches",
+    }
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {
+            "workload": ("qwen3-8b-shaped dense linears, block-scaled W8A8: per step, "
+                         "128x128 re-quantization of the 36-layer bf16 policy, then for "
+                         "every layer and linear 1x128 activation quant + GEMM at M=8192 "
+                         "and M=256"),
+            "layers": layers, "M": list(Ms),
+            "linears": {name: {"N": N, "K": K} for name, (N, K) in shapes},
+            "parallelism": "single-gpu",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,40 +125,52 @@ def _as_u8(t: torch.Tensor) -> torch.Tensor:
 
 
 # ------------------------------------------------------------ quantizers --
-def quantize_block(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M, K/128])."""
+def quantize_block(x: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M, K/128]).
+    ``out`` may supply the (q, s) buffers."""
     _need(x, torch.bfloat16, 2, "x")
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M, K // 128 if K % 128 == 0 else 0), dtype=torch.float32, device=x.device)
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 128 if K % 128 == 0 else 0), dtype=torch.float32,
+                        device=x.device)
     L = load_library()
     _check("fp8_quantize_block", L.fp8_quantize_block(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
     return q, s
 
 
-def quantize_token(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M])."""
+def quantize_token(x: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], fp32 scales [M]).
+    ``out`` may supply the (q, s) buffers."""
     _need(x, torch.bfloat16, 2, "x")
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M,), dtype=torch.float32, device=x.device)
     L = load_library()
     _check("fp8_quantize_token", L.fp8_quantize_token(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
     return q, s
 
 
 def rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
-                  group_size: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                  group_size: int = 0, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Fused RMSNorm + FP8 quantization.  group_size 0: scales [M];
-    group_size 128: scales [M, K/128]."""
+    group_size 128: scales [M, K/128].  ``out`` may supply the (q, s) buffers."""
     _need(x, torch.bfloat16, 2, "x")
     _need(gamma, torch.bfloat16, 1, "gamma")
     M, K = x.shape
     if gamma.shape[0] != K:
         raise ValueError("gamma must have K elements")
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    sshape = (M,) if group_size == 0 else (M, K // 128 if K % 128 == 0 else 0)
-    s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        sshape = (M,) if group_size == 0 else (M, K // 128 if K % 128 == 0 else 0)
+        s = torch.empty(sshape, dtype=torch.float32, device=x.device)
     L = load_library()
     _check("fp8_rmsnorm_quant", L.fp8_rmsnorm_quant(_ptr(q), _ptr(x), _ptr(s), _ptr(gamma),
                                                    float(eps), M, K, group_size, _stream(x)))
