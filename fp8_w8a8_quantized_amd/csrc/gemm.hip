@@ -27,8 +27,8 @@
 //     loaded into registers (16-byte loads, one 128-byte row segment per 8
 //     threads) while the current one is multiplied, then written to the other
 //     buffer; one barrier per K block.  16-byte chunks of each 128-byte tile
-//     row are XOR-swizzled by the row index so the MFMA operand reads of 8
-//     consecutive rows hit distinct banks.
+//     row are XOR-swizzled by the row index (swz) so the MFMA operand reads
+//     of 16 consecutive rows hit distinct banks.
 //   * MFMA operand layout (16x16x128, 8-bit): lane l supplies row l % 16 of
 //     its operand and 32 consecutive K bytes starting at 32 * (l / 16); A and
 //     W use the same K assignment, so every product pairs matching k.  The
@@ -54,8 +54,14 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// byte offset of 16-byte chunk `c` of tile row `r` (128 bytes per row)
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk `c` of tile row `r` (128 bytes per row).  The
+// gfx950 LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, 64 banks) at
+// a time; the MFMA operand reads put 16 consecutive rows, same chunk, in one
+// such group.  Row parity already selects the bank half (rows are 128 bytes),
+// so XOR-ing the chunk with (r >> 1) & 7 spreads the 8 rows of each parity
+// over 8 distinct 16-byte bank groups: conflict-free.
+__device__ __forceinline__ int swz_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + (swz_pos(r, c) << 4); }
 
 // One output tile's work description.
 struct Tile {
@@ -303,6 +309,216 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(
     gemm_tile<GRAN_BLOCK>(t, K, N, lds);
 }
 
+// ---------------------------------------------------------------------------
+// Large-M kernel: workgroup tile 256 x 256, K step 128, 512 threads as 4 x 2
+// waves, each wave a 64 x 128 sub-tile (4 x 8 MFMA tiles; its 128 columns are
+// one weight scale block).  A and W tiles move HBM -> LDS with direct-to-LDS
+// 16-byte loads (global_load_lds_dwordx4: each lane's 16 bytes land at the
+// wave's LDS base + 16 * lane), so no registers stage them; the lane -> global
+// address map applies the same 16-byte-chunk XOR swizzle as above.  Two LDS
+// stages (2 x 64 KiB): the next K block streams into one while the current one
+// is multiplied.  Tiles are assigned so that each XCD (blockIdx % 8) owns a
+// contiguous range of tiles, ordered in bands of 4 row-tiles, so the
+// workgroups resident on one XCD share A rows and W columns in its L2.  The
+// epilogue stages bf16 results through LDS for 16-byte row-contiguous stores.
+// ---------------------------------------------------------------------------
+constexpr int BM2 = 256, BN2 = 256, kThreads2 = 512;
+constexpr int kStage2 = (BM2 + BN2) * BK;             // 64 KiB per stage
+constexpr int kOutPitch = 128 * 2 + 16;                // bf16 row pitch in the epilogue
+constexpr int kLdsMain2 = 2 * kStage2 + 2 * BM2 * 4;   // two stages + two sA slices
+constexpr int kLdsOut2 = (kThreads2 / 64) * 64 * kOutPitch;  // 8 waves x 64 rows
+constexpr int kLds2 = kLdsMain2 > kLdsOut2 ? kLdsMain2 : kLdsOut2;
+static_assert(kLds2 <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void g2l_16(const void* g, uint8_t* l) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l_4(const void* g, uint8_t* l) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 4, 0, 0);
+}
+
+// Stage K block kb of the A and W tiles (and the A scales) into LDS stage st.
+template <int GRAN>
+__device__ __forceinline__ void stage_big(uint8_t* lds, int st, const uint8_t* A, const uint8_t* W,
+                                          const float* sA, int rows, int64_t K, int64_t KB,
+                                          int64_t kb, int wave, int lane) {
+    uint8_t* la = lds + st * kStage2;
+    uint8_t* lb = la + BM2 * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int pbase = (i * 8 + wave) * 64;  // LDS chunk of lane 0 (8 rows per wave load)
+        const int p = pbase + lane;
+        const int r = p >> 3;
+        const int c = swz_pos(r, p & 7);  // the global chunk whose LDS slot is p
+        const int ra = r < rows ? r : rows - 1;
+        g2l_16(A + ra * K + kb * BK + c * 16, la + pbase * 16);
+        g2l_16(W + r * K + kb * BK + c * 16, lb + pbase * 16);
+    }
+    if constexpr (GRAN == GRAN_BLOCK) {
+        if (wave < 4) {
+            const int r = wave * 64 + lane;
+            const int rr = r < rows ? r : rows - 1;
+            g2l_4(sA + rr * KB + kb, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256);
+        }
+    }
+}
+
+template <int GRAN>
+__global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restrict__ A,
+                                                        const uint8_t* __restrict__ W,
+                                                        const float* __restrict__ sA,
+                                                        const float* __restrict__ sW,
+                                                        uint16_t* __restrict__ Y, int64_t M,
+                                                        int64_t N, int64_t K) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
+    const int64_t tm_count = (M + BM2 - 1) / BM2, tn_count = N / BN2;
+    const int64_t T = tm_count * tn_count;
+    // XCD-contiguous tile order: XCD x = blockIdx % 8 gets logical tiles
+    // [x * q + min(x, r), ...) where T = 8 q + r.
+    const int64_t bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
+    const int64_t q = T >> 3, rem = T & 7;
+    const int64_t logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    constexpr int64_t GROUP = 4;
+    const int64_t band = logical / (GROUP * tn_count);
+    const int64_t first_m = band * GROUP;
+    const int64_t band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
+    const int64_t in_band = logical - band * GROUP * tn_count;
+    const int64_t tm = first_m + in_band % band_m, tn = in_band / band_m;
+
+    const int64_t KB = K / BK;
+    const int64_t row0 = tm * BM2, n0 = tn * BN2;
+    const int rows = (int)((M - row0) < BM2 ? (M - row0) : BM2);
+    const uint8_t* At = A + row0 * K;
+    const uint8_t* Wt = W + n0 * K;
+    const float* sAt = GRAN == GRAN_BLOCK ? sA + row0 * KB : sA + row0;
+    const float* sWt = GRAN == GRAN_BLOCK ? sW + (n0 / BK) * KB : sW + n0;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index made provably wave-uniform, so per-wave scale reads become
+    // scalar loads (a vector load would make the loop's vmcnt waits also wait
+    // for the next stage's direct-to-LDS loads)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
+    const int lr = lane & 15, lk = lane >> 4;
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    stage_big<GRAN>(lds, 0, At, Wt, sAt, rows, K, KB, 0, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's LDS-bound loads landed
+    __syncthreads();
+
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        const int cur = (int)(kb & 1);
+        if (kb + 1 < KB) stage_big<GRAN>(lds, cur ^ 1, At, Wt, sAt, rows, K, KB, kb + 1, wave, lane);
+
+        const uint8_t* la = lds + cur * kStage2;
+        const uint8_t* lb = la + BM2 * BK;
+        v8i a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 64 + i * 16 + lr;
+            const v4i lo = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk));
+            const v4i hi = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk + 1));
+            a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        // B fragments are double-buffered: the next one is read from LDS while
+        // the current one feeds the MFMAs.
+        auto load_b = [&](int j) -> v8i {
+            const int r = wn * 128 + j * 16 + lr;
+            const v4i lo = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk));
+            const v4i hi = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk + 1));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        if constexpr (GRAN == GRAN_BLOCK) {
+            const float sw = sWt[wn * KB + kb];
+            const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + cur * BM2 * 4);
+            v4f sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[i] = *reinterpret_cast<const v4f*>(lsa + wm * 64 + i * 16 + 4 * lk) * sw;
+            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            v8i bcur = load_b(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v8i bnext = bcur;
+                if (j < 7) bnext = load_b(j + 1);
+                v4f pk[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[i] = mfma_f8(a[i], bcur, zero);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j][e] = __builtin_fmaf(pk[i][e], sc[i][e], acc[i][j][e]);
+                bcur = bnext;
+            }
+            // schedule: per column tile, the next tile's two LDS reads, then its
+            // MFMAs interleaved with promotion FMAs
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                }
+            }
+        } else {
+            v8i bcur = load_b(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v8i bnext = bcur;
+                if (j < 7) bnext = load_b(j + 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(a[i], bcur, acc[i][j]);
+                bcur = bnext;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // next stage's loads landed
+        __syncthreads();
+    }
+
+    // epilogue: bf16 tile of this wave -> LDS (row pitch kOutPitch) -> 16-byte stores
+    uint8_t* lo_ = lds + wave * (64 * kOutPitch);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = i * 16 + 4 * lk + e;
+            float sa = 1.0f;
+            if constexpr (GRAN == GRAN_ROW) {
+                const int gr = wm * 64 + r;
+                sa = sAt[gr < rows ? gr : rows - 1];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = j * 16 + lr;
+                float v = acc[i][j][e];
+                if constexpr (GRAN == GRAN_ROW) v = v * (sa * sWt[wn * 128 + c]);
+                *reinterpret_cast<uint16_t*>(lo_ + r * kOutPitch + c * 2) =
+                    (uint16_t)bf16_rne_bits(v);
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int qd = it * 64 + lane;  // 16-byte chunk: 16 per 128-column row
+        const int r = qd >> 4, c16 = qd & 15;
+        const int gr = wm * 64 + r;
+        if (gr < rows) {
+            const v4i v = *reinterpret_cast<const v4i*>(lo_ + r * kOutPitch + c16 * 16);
+            *reinterpret_cast<v4i*>(Y + (row0 + gr) * N + n0 + wn * 128 + c16 * 8) = v;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
@@ -312,6 +528,16 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     const auto* A = static_cast<const uint8_t*>(a);
     const auto* Wp = static_cast<const uint8_t*>(w);
     auto* Yp = static_cast<uint16_t*>(y);
+    if (M >= 1024 && N % BN2 == 0) {
+        const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
+        if (gran == GRAN_BLOCK)
+            hipLaunchKernelGGL(k_gemm_big<GRAN_BLOCK>, dim3((unsigned)tiles2), dim3(kThreads2), 0,
+                               st, A, Wp, a_s, w_s, Yp, M, N, K);
+        else
+            hipLaunchKernelGGL(k_gemm_big<GRAN_ROW>, dim3((unsigned)tiles2), dim3(kThreads2), 0,
+                               st, A, Wp, a_s, w_s, Yp, M, N, K);
+        return hipGetLastError();
+    }
     if (gran == GRAN_BLOCK)
         hipLaunchKernelGGL(k_gemm<GRAN_BLOCK>, dim3((unsigned)tiles), dim3(kThreads), 0, st, A,
                            Wp, a_s, w_s, Yp, M, N, K);

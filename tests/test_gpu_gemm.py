@@ -55,7 +55,17 @@ def test_block_small_shapes(M, N, K):
     assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (130, 384, 512), (77, 256, 5120)])
+@pytest.mark.parametrize("M,N,K", [(1024, 256, 256), (1100, 768, 640), (2047, 512, 1152)])
+def test_block_large_m_shapes(M, N, K):
+    say(f"block GEMM (large-M kernel) {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + N + K)
+    W = synth.weight(N, K, seed=N + K + 1)
+    y, ref = _block_pipeline(X, W)
+    assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (130, 384, 512), (77, 256, 5120),
+                                   (1100, 768, 640), (1024, 256, 4096)])
 def test_row_small_shapes(M, N, K):
     say(f"row GEMM {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + 3)
