@@ -311,23 +311,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(
 
 // ---------------------------------------------------------------------------
 // Large-M kernel: workgroup tile 256 x 256, K step 128, 512 threads as 4 x 2
-// waves, each wave a 64 x 128 sub-tile (4 x 8 MFMA tiles; its 128 columns are
-// one weight scale block).  A and W tiles move HBM -> LDS with direct-to-LDS
-// 16-byte loads (global_load_lds_dwordx4: each lane's 16 bytes land at the
-// wave's LDS base + 16 * lane), so no registers stage them; the lane -> global
-// address map applies the same 16-byte-chunk XOR swizzle as above.  Two LDS
-// stages (2 x 64 KiB): the next K block streams into one while the current one
-// is multiplied.  Tiles are assigned so that each XCD (blockIdx % 8) owns a
-// contiguous range of tiles, ordered in bands of 4 row-tiles, so the
-// workgroups resident on one XCD share A rows and W columns in its L2.  The
-// epilogue stages bf16 results through LDS for 16-byte row-contiguous stores.
+// waves, each wave 64 rows x 128 columns of Y (its 128 columns are one weight
+// scale block).
+//   * The MFMA computes the transposed tile: operand A is a 16-row W
+//     fragment (16 output columns), operand B a 16-row X fragment (16 output
+//     rows), so element e of lane l is Y[row 16i + l % 16][col 16j + 4 (l/16)
+//     + e].  A lane then holds 4 consecutive columns of one row: the block
+//     promotion is acc += P * s with one activation scale per lane and row
+//     tile, and the epilogue stores 8 bytes of bf16 straight to HBM.
+//   * A and W tiles move HBM -> LDS with direct-to-LDS 16-byte loads
+//     (global_load_lds_dwordx4: the 16 bytes of lane i land at the wave's LDS
+//     base + 16 i), so no registers stage them; the lane -> global address
+//     map applies the chunk swizzle.  Two LDS stages: the next K block streams
+//     into one while the current one is multiplied.
+//   * Per K block a wave keeps its 4 X fragments in registers and streams the
+//     8 W fragments (double-buffered); the FMAs that promote one MFMA's result
+//     are issued after the next MFMA, so they never wait on the matrix core.
+//   * Tiles are assigned so that each XCD (blockIdx % 8) owns a contiguous
+//     range of tiles, ordered in bands of 4 row-tiles, so the workgroups
+//     resident on one XCD share A rows and W columns in its L2.
 // ---------------------------------------------------------------------------
 constexpr int BM2 = 256, BN2 = 256, kThreads2 = 512;
 constexpr int kStage2 = (BM2 + BN2) * BK;             // 64 KiB per stage
-constexpr int kOutPitch = 128 * 2 + 16;                // bf16 row pitch in the epilogue
-constexpr int kLdsMain2 = 2 * kStage2 + 2 * BM2 * 4;   // two stages + two sA slices
-constexpr int kLdsOut2 = (kThreads2 / 64) * 64 * kOutPitch;  // 8 waves x 64 rows
-constexpr int kLds2 = kLdsMain2 > kLdsOut2 ? kLdsMain2 : kLdsOut2;
+constexpr int kLds2 = 2 * kStage2 + 2 * BM2 * 4;       // two stages + two sA slices
 static_assert(kLds2 <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -364,6 +370,12 @@ __device__ __forceinline__ void stage_big(uint8_t* lds, int st, const uint8_t* A
             g2l_4(sA + rr * KB + kb, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256);
         }
     }
+}
+
+__device__ __forceinline__ v8i frag(const uint8_t* base, int r, int lk) {
+    const v4i lo = *reinterpret_cast<const v4i*>(base + swz(r, 2 * lk));
+    const v4i hi = *reinterpret_cast<const v4i*>(base + swz(r, 2 * lk + 1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int GRAN>
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
     const int wm = wave & 3, wn = wave >> 2;
     const int lr = lane & 15, lk = lane >> 4;
 
-    v4f acc[4][8];
+    v4f acc[4][8];  // [row tile i][column tile j]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -420,101 +432,77 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
 
         const uint8_t* la = lds + cur * kStage2;
         const uint8_t* lb = la + BM2 * BK;
-        v8i a[4];
+        v8i x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + i * 16 + lr;
-            const v4i lo = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk));
-            const v4i hi = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk + 1));
-            a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        // B fragments are double-buffered: the next one is read from LDS while
-        // the current one feeds the MFMAs.
-        auto load_b = [&](int j) -> v8i {
-            const int r = wn * 128 + j * 16 + lr;
-            const v4i lo = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk));
-            const v4i hi = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk + 1));
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
+        for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
         if constexpr (GRAN == GRAN_BLOCK) {
             const float sw = sWt[wn * KB + kb];
             const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + cur * BM2 * 4);
-            v4f sc[4];
+            float sc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sc[i] = *reinterpret_cast<const v4f*>(lsa + wm * 64 + i * 16 + 4 * lk) * sw;
+            for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * sw;
             const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            v8i bcur = load_b(0);
+            v8i wcur = frag(lb, wn * 128 + lr, lk);
+            v4f prev;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                v8i bnext = bcur;
-                if (j < 7) bnext = load_b(j + 1);
-                v4f pk[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = mfma_f8(a[i], bcur, zero);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[i][j][e] = __builtin_fmaf(pk[i][e], sc[i][e], acc[i][j][e]);
-                bcur = bnext;
-            }
-            // schedule: per column tile, the next tile's two LDS reads, then its
-            // MFMAs interleaved with promotion FMAs
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+                v8i wnext = wcur;
+                if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                    const v4f p = mfma_f8(wcur, x[i], zero);
+                    // promote the previous MFMA's result (tile (i-1, j) or (3, j-1))
+                    if (i > 0 || j > 0) {
+                        const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? j : j - 1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
+                    }
+                    prev = p;
                 }
+                wcur = wnext;
+                // keep each column tile's MFMAs in their step: hoisting them
+                // further only raises register pressure past 256 VGPRs
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[3][7][e] = __builtin_fmaf(prev[e], sc[3], acc[3][7][e]);
         } else {
-            v8i bcur = load_b(0);
+            v8i wcur = frag(lb, wn * 128 + lr, lk);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                v8i bnext = bcur;
-                if (j < 7) bnext = load_b(j + 1);
+                v8i wnext = wcur;
+                if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(a[i], bcur, acc[i][j]);
-                bcur = bnext;
+                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(wcur, x[i], acc[i][j]);
+                wcur = wnext;
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // next stage's loads landed
         __syncthreads();
     }
 
-    // epilogue: bf16 tile of this wave -> LDS (row pitch kOutPitch) -> 16-byte stores
-    uint8_t* lo_ = lds + wave * (64 * kOutPitch);
+    // epilogue: lane holds Y[row][col .. col+3] per tile -> one 8-byte bf16 store
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + lr;
+        if (r >= rows) continue;
+        float sa = 1.0f;
+        if constexpr (GRAN == GRAN_ROW) sa = sAt[r];
+        uint16_t* yrow = Y + (row0 + r) * N + n0 + wn * 128 + 4 * lk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = i * 16 + 4 * lk + e;
-            float sa = 1.0f;
+        for (int j = 0; j < 8; ++j) {
+            v4f v = acc[i][j];
             if constexpr (GRAN == GRAN_ROW) {
-                const int gr = wm * 64 + r;
-                sa = sAt[gr < rows ? gr : rows - 1];
-            }
+                const v4f s4 = *reinterpret_cast<const v4f*>(sWt + wn * 128 + j * 16 + 4 * lk);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = j * 16 + lr;
-                float v = acc[i][j][e];
-                if constexpr (GRAN == GRAN_ROW) v = v * (sa * sWt[wn * 128 + c]);
-                *reinterpret_cast<uint16_t*>(lo_ + r * kOutPitch + c * 2) =
-                    (uint16_t)bf16_rne_bits(v);
+                for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
             }
-        }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int qd = it * 64 + lane;  // 16-byte chunk: 16 per 128-column row
-        const int r = qd >> 4, c16 = qd & 15;
-        const int gr = wm * 64 + r;
-        if (gr < rows) {
-            const v4i v = *reinterpret_cast<const v4i*>(lo_ + r * kOutPitch + c16 * 16);
-            *reinterpret_cast<v4i*>(Y + (row0 + gr) * N + n0 + wn * 128 + c16 * 8) = v;
+            uint2 o;
+            o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+            o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(yrow + j * 16) = o;
         }
     }
 }
