@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     return ap.parse_args()
 
 
