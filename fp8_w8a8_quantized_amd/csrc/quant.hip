@@ -43,6 +43,16 @@ __device__ __forceinline__ GroupDiv group_div(float amax) {
     return g;
 }
 
+// Load vector idx of an n-vector array, or zeros when idx >= n, without a
+// branch: the address is clamped to the last vector (always in bounds) and the
+// value selected afterwards.  A branch around each load makes the compiler
+// wait for every load before issuing the next one.
+__device__ __forceinline__ uint4 load_or_zero(const uint4* __restrict__ p, int64_t idx, int64_t n) {
+    const uint4 t = p[idx < n ? idx : n - 1];
+    const bool in = idx < n;
+    return make_uint4(in ? t.x : 0u, in ? t.y : 0u, in ? t.z : 0u, in ? t.w : 0u);
+}
+
 __device__ __forceinline__ uint2 encode8(const float (&f)[8], const GroupDiv& g) {
     float t[8];
     if (g.fast) {
@@ -71,8 +81,7 @@ __global__ __launch_bounds__(256) void k_quant_block(const uint4* __restrict__ x
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
-        v[u] = gid < G ? x[(chunk0 + u) * 64 + lane] : make_uint4(0, 0, 0, 0);
+        v[u] = load_or_zero(x, (chunk0 + u) * 64 + lane, G * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -105,10 +114,7 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint4* __restrict__ x
     if constexpr (VPL > 0) {
         uint4 v[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int64_t idx = lane + 64 * i;
-            v[i] = idx < V ? xr[idx] : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < VPL; ++i) v[i] = load_or_zero(xr, lane + 64 * i, V);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
@@ -196,10 +202,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(uint2* __restrict__ q,
     if constexpr (VPL > 0) {
         uint4 v[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int64_t idx = lane + 64 * i;
-            v[i] = idx < V ? xr[idx] : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < VPL; ++i) v[i] = load_or_zero(xr, lane + 64 * i, V);
         float p = 0.0f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(uint2* __restrict__ q,
         for (int i = 0; i < VPL; ++i) {
             const int64_t idx = lane + 64 * i;
             float y[8];
-            rms_y8(v[i], idx < V ? gamma[idx] : make_uint4(0, 0, 0, 0), inv, y);
+            rms_y8(v[i], load_or_zero(gamma, idx, V), inv, y);
             v[i] = pack_bf16x8(y);  // keep y (bf16) in place of x
             if constexpr (GROUP == 0) m = fmaxf(m, amax8(y));
         }
@@ -267,8 +270,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(uint2* __restrict__ q,
             for (int64_t base = 0; base < V; base += 64) {
                 const int64_t idx = base + lane;
                 float y[8];
-                rms_y8(idx < V ? xr[idx] : make_uint4(0, 0, 0, 0),
-                       idx < V ? gamma[idx] : make_uint4(0, 0, 0, 0), inv, y);
+                rms_y8(load_or_zero(xr, idx, V), load_or_zero(gamma, idx, V), inv, y);
                 const GroupDiv g = group_div(max_16lanes(amax8(y)));
                 if (idx < V) {
                     qr[idx] = encode8(y, g);
@@ -398,10 +400,20 @@ hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, f
     const int64_t V = K / 8, blocks = (M + 3) / 4;
     const uint4* xv = static_cast<const uint4*>(x);
     uint2* qv = static_cast<uint2*>(q);
-    if (V <= 64 * 4) return launch(k_quant_token<4>, blocks, st, xv, qv, s, M, V);
-    if (V <= 64 * 8) return launch(k_quant_token<8>, blocks, st, xv, qv, s, M, V);
-    if (V <= 64 * 16) return launch(k_quant_token<16>, blocks, st, xv, qv, s, M, V);
-    if (V <= 64 * 32) return launch(k_quant_token<32>, blocks, st, xv, qv, s, M, V);
+    // vectors per lane: the smallest instantiation that holds the row, so short
+    // rows keep few registers and many waves per SIMD
+#define FP8_TOKEN_CASE(VPL) \
+    if (V <= 64 * VPL) return launch(k_quant_token<VPL>, blocks, st, xv, qv, s, M, V);
+    FP8_TOKEN_CASE(2)
+    FP8_TOKEN_CASE(4)
+    FP8_TOKEN_CASE(6)
+    FP8_TOKEN_CASE(8)
+    FP8_TOKEN_CASE(10)
+    FP8_TOKEN_CASE(12)
+    FP8_TOKEN_CASE(16)
+    FP8_TOKEN_CASE(24)
+    FP8_TOKEN_CASE(32)
+#undef FP8_TOKEN_CASE
     return launch(k_quant_token<0>, blocks, st, xv, qv, s, M, V);
 }
 
@@ -417,9 +429,14 @@ hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* ga
             return launch(k_rmsnorm_quant<VPL, 0>, blocks, st, qv, xv, s, gv, eps, M, V);   \
         return launch(k_rmsnorm_quant<VPL, 128>, blocks, st, qv, xv, s, gv, eps, M, V);     \
     }
+    FP8_RMS_CASE(2)
     FP8_RMS_CASE(4)
+    FP8_RMS_CASE(6)
     FP8_RMS_CASE(8)
+    FP8_RMS_CASE(10)
+    FP8_RMS_CASE(12)
     FP8_RMS_CASE(16)
+    FP8_RMS_CASE(24)
     FP8_RMS_CASE(32)
     FP8_RMS_CASE(0)
 #undef FP8_RMS_CASE
