@@ -160,7 +160,7 @@ int fp8_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s, const f
 int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
                                  const float* w_s, const int32_t* offsets, void* y, int64_t T,
                                  int64_t E, int64_t N, int64_t K, void* stream) {
-    if (T < 0 || E < 1) return FP8_ERR_ARG;
+    if (T < 0 || E < 1 || E > 1024 || T > INT32_MAX) return FP8_ERR_ARG;
     if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
     if (T == 0) return FP8_OK;
     if (!a || !w || !a_s || !w_s || !offsets || !y) return FP8_ERR_ARG;

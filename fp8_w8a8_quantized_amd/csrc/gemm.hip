@@ -15,24 +15,25 @@
 //          fp32 sum over the 128-wide K block kb.
 //   ROW:   Y[m,n] = sA[m] sW[n] sum_k X[m,k] W[n,k].
 //
-// Design (CDNA4):
-//   * Workgroup tile 128 x 128, K step 128 = one scale block; 256 threads as
-//     2 x 2 waves, each wave a 64 x 64 sub-tile of 4 x 4 MFMA tiles.
-//   * v_mfma_f32_16x16x128_f8f6f4 (both operands E4M3): one instruction is a
+// Two kernels share one tile recipe (CDNA4):
+//   * v_mfma_f32_16x16x128_f8f6f4 with both operands E4M3: one instruction is a
 //     16 x 16 tile over a whole 128-wide K block, so BLOCK mode gets P_kb from
 //     one MFMA with a zero accumulator and promotes it with one fp32 FMA per
-//     output element: acc += P_kb * (sA * sW).  ROW mode accumulates in the
+//     output element, acc += P_kb * (sA * sW); ROW mode accumulates in the
 //     MFMA and scales once in the epilogue.
-//   * A and W tiles are staged in LDS, double buffered: the next K block is
-//     loaded into registers (16-byte loads, one 128-byte row segment per 8
-//     threads) while the current one is multiplied, then written to the other
-//     buffer; one barrier per K block.  16-byte chunks of each 128-byte tile
-//     row are XOR-swizzled by the row index (swz) so the MFMA operand reads
-//     of 16 consecutive rows hit distinct banks.
 //   * MFMA operand layout (16x16x128, 8-bit): lane l supplies row l % 16 of
-//     its operand and 32 consecutive K bytes starting at 32 * (l / 16); A and
-//     W use the same K assignment, so every product pairs matching k.  The
-//     result holds D[4 * (l / 16) + i][l % 16] in element i of lane l.
+//     its operand and 32 consecutive K bytes starting at 32 * (l / 16); both
+//     operands use the same K assignment, so every product pairs matching k.
+//     The result holds D[4 * (l / 16) + i][l % 16] in element i of lane l.
+//     The kernels put the W fragment in operand A and the X fragment in
+//     operand B (they compute the transposed tile), so a lane holds four
+//     consecutive output columns of one row.
+//   * Operand tiles are staged in LDS by direct-to-LDS 16-byte loads, with
+//     16-byte chunks of each 128-byte tile row XOR-swizzled (swz) so the
+//     operand reads of 16 consecutive rows hit distinct banks.
+//   k_gemm_big  (M >= 1024): 256 x 256 tile, 8 waves, two LDS stages.
+//   k_gemm_pipe (small M, and the MoE grouped GEMM): 128 x 128 tile, 4 waves,
+//     a ring of four LDS stages with three in flight.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -45,8 +46,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kThreads = 256;
+constexpr int BK = 128;  // K step: one scale block
 constexpr int GRAN_BLOCK = 0, GRAN_ROW = 1;
 
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
@@ -72,242 +72,6 @@ struct Tile {
     uint16_t* Y;        // &Y[row0][n0]
     int rows;           // valid rows in this tile (1..128)
 };
-
-template <int GRAN>
-__device__ __forceinline__ void stage_load(const Tile& t, int64_t K, int64_t KB, int64_t kb,
-                                           int gr, int gc, int tid, v4i (&ra)[4],
-                                           v4i (&rb)[4], float& rsa) {
-    // Rows past the tile's end (ragged M) re-read the last valid row: a row of
-    // A only reaches its own output row, and those rows are never stored.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = gr + 32 * i;
-        const int ra_row = r < t.rows ? r : t.rows - 1;
-        ra[i] = *reinterpret_cast<const v4i*>(t.A + ra_row * K + kb * BK + gc * 16);
-        rb[i] = *reinterpret_cast<const v4i*>(t.W + r * K + kb * BK + gc * 16);
-    }
-    if constexpr (GRAN == GRAN_BLOCK) {
-        if (tid < BM) rsa = t.sA[(tid < t.rows ? tid : t.rows - 1) * KB + kb];
-    }
-}
-
-template <int GRAN>
-__device__ __forceinline__ void stage_store(uint8_t* lds_a, uint8_t* lds_b, float* lds_sa,
-                                            int buf, int gr, int gc, int tid,
-                                            const v4i (&ra)[4], const v4i (&rb)[4],
-                                            float rsa) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = gr + 32 * i;
-        *reinterpret_cast<v4i*>(lds_a + buf * BM * BK + swz(r, gc)) = ra[i];
-        *reinterpret_cast<v4i*>(lds_b + buf * BN * BK + swz(r, gc)) = rb[i];
-    }
-    if constexpr (GRAN == GRAN_BLOCK) {
-        if (tid < BM) lds_sa[buf * BM + tid] = rsa;
-    }
-}
-
-template <int GRAN>
-__device__ __forceinline__ void gemm_tile(const Tile& t, int64_t K, int64_t ldy, uint8_t* lds) {
-    uint8_t* lds_a = lds;                       // [2][BM * BK]
-    uint8_t* lds_b = lds + 2 * BM * BK;         // [2][BN * BK]
-    float* lds_sa = reinterpret_cast<float*>(lds + 2 * (BM + BN) * BK);  // [2][BM]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 15, lk = lane >> 4;
-    const int64_t KB = K / BK;
-
-    // global -> register staging: thread loads chunk (tid & 7) of rows tid/8 + 32 i
-    const int gc = tid & 7, gr = tid >> 3;
-    v4i ra[4], rb[4];
-    float rsa = 0.0f;
-    v4f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    stage_load<GRAN>(t, K, KB, 0, gr, gc, tid, ra, rb, rsa);
-    stage_store<GRAN>(lds_a, lds_b, lds_sa, 0, gr, gc, tid, ra, rb, rsa);
-    __syncthreads();
-
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int cur = (int)(kb & 1);
-        if (kb + 1 < KB) stage_load<GRAN>(t, K, KB, kb + 1, gr, gc, tid, ra, rb, rsa);
-
-        const uint8_t* la = lds_a + cur * BM * BK;
-        const uint8_t* lb = lds_b + cur * BN * BK;
-        v8i a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + i * 16 + lr;
-            const v4i lo = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk));
-            const v4i hi = *reinterpret_cast<const v4i*>(la + swz(r, 2 * lk + 1));
-            a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wn * 64 + j * 16 + lr;
-            const v4i lo = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk));
-            const v4i hi = *reinterpret_cast<const v4i*>(lb + swz(r, 2 * lk + 1));
-            b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        if constexpr (GRAN == GRAN_BLOCK) {
-            const float sw = t.sW[kb];
-            v4f sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4f s4 = *reinterpret_cast<const v4f*>(lds_sa + cur * BM + wm * 64 +
-                                                             i * 16 + 4 * lk);
-                sc[i] = s4 * sw;
-            }
-            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4f p = mfma_f8(a[i], b[j], zero);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[i][j][e] = __builtin_fmaf(p[e], sc[i][e], acc[i][j][e]);
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(a[i], b[j], acc[i][j]);
-        }
-
-        if (kb + 1 < KB) stage_store<GRAN>(lds_a, lds_b, lds_sa, cur ^ 1, gr, gc, tid, ra, rb, rsa);
-        __syncthreads();
-    }
-
-    // epilogue: bf16 (nearest even) stores; ROW mode applies sA[m] * sW[n]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = wm * 64 + i * 16 + 4 * lk + e;
-            if (r >= t.rows) continue;
-            float sa = 1.0f;
-            if constexpr (GRAN == GRAN_ROW) sa = t.sA[r];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = wn * 64 + j * 16 + lr;
-                float v = acc[i][j][e];
-                if constexpr (GRAN == GRAN_ROW) v = v * (sa * t.sW[c]);
-                t.Y[(int64_t)r * ldy + c] = (uint16_t)bf16_rne_bits(v);
-            }
-        }
-    }
-}
-
-constexpr int kLdsBytes = 2 * (BM + BN) * BK + 2 * BM * 4;
-
-// Dense: tiles ordered in bands of 8 row-tiles so consecutive workgroups share
-// weight tiles.
-template <int GRAN>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(const uint8_t* __restrict__ A,
-                                                   const uint8_t* __restrict__ W,
-                                                   const float* __restrict__ sA,
-                                                   const float* __restrict__ sW,
-                                                   uint16_t* __restrict__ Y, int64_t M,
-                                                   int64_t N, int64_t K) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    const int64_t tm_count = (M + BM - 1) / BM, tn_count = N / BN;
-    const int64_t bid = blockIdx.x;
-    constexpr int64_t GROUP = 8;
-    const int64_t band = bid / (GROUP * tn_count);
-    const int64_t first_m = band * GROUP;
-    const int64_t band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
-    const int64_t in_band = bid - band * GROUP * tn_count;
-    const int64_t tm = first_m + in_band % band_m;
-    const int64_t tn = in_band / band_m;
-
-    const int64_t KB = K / BK;
-    const int64_t row0 = tm * BM, n0 = tn * BN;
-    Tile t;
-    t.A = A + row0 * K;
-    t.W = W + n0 * K;
-    t.Y = Y + row0 * N + n0;
-    t.rows = (int)((M - row0) < BM ? (M - row0) : BM);
-    if constexpr (GRAN == GRAN_BLOCK) {
-        t.sA = sA + row0 * KB;
-        t.sW = sW + tn * KB;
-    } else {
-        t.sA = sA + row0;
-        t.sW = sW + n0;
-    }
-    gemm_tile<GRAN>(t, K, N, lds);
-}
-
-// Grouped (MoE): blockIdx.x enumerates row tiles of all experts in expert
-// order (an upper bound of them; surplus workgroups exit), blockIdx.y the
-// column tile.  Wave 0 locates the expert of its row tile with a prefix sum of
-// ceil(rows_e / 128) over the experts.
-__global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
-    const float* __restrict__ sA, const float* __restrict__ sW,
-    const int32_t* __restrict__ offsets, uint16_t* __restrict__ Y, int64_t T, int64_t E,
-    int64_t N, int64_t K) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    __shared__ int64_t s_task[3];  // expert (-1: none), first row, rows
-    const int64_t tile = blockIdx.x;
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int64_t base = 0, found = -1, frow = 0, nrows = 0;
-        for (int64_t e0 = 0; e0 < E && found < 0; e0 += 64) {
-            const int64_t e = e0 + lane;
-            int64_t lo = 0, hi = 0;
-            if (e < E) {
-                lo = offsets[e];
-                hi = offsets[e + 1];
-                lo = lo < 0 ? 0 : (lo > T ? T : lo);
-                hi = hi < lo ? lo : (hi > T ? T : hi);
-            }
-            const int64_t cnt = (hi - lo + BM - 1) / BM;
-            int64_t incl = cnt;  // inclusive prefix over the 64 lanes
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int64_t up = __shfl_up(incl, o);
-                if (lane >= o) incl += up;
-            }
-            const int64_t excl = incl - cnt;
-            const bool mine = cnt > 0 && tile >= base + excl && tile < base + incl;
-            const unsigned long long bal = __ballot(mine);
-            if (bal) {
-                const int src = __ffsll((long long)bal) - 1;
-                const int64_t lt = tile - base - excl;  // meaningful in lane src
-                const int64_t r0 = lo + lt * BM;
-                const int64_t rn = (hi - r0) < BM ? (hi - r0) : BM;
-                found = __shfl(e, src);
-                frow = __shfl(r0, src);
-                nrows = __shfl(rn, src);
-            }
-            base += __shfl(incl, 63);
-        }
-        if (lane == 0) {
-            s_task[0] = found;
-            s_task[1] = frow;
-            s_task[2] = nrows;
-        }
-    }
-    __syncthreads();
-    const int64_t e = s_task[0];
-    if (e < 0) return;  // whole workgroup leaves together
-    const int64_t row0 = s_task[1];
-    const int64_t KB = K / BK, tn = blockIdx.y, n0 = tn * BN;
-    Tile t;
-    t.A = A + row0 * K;
-    t.sA = sA + row0 * KB;
-    t.W = W + (e * N + n0) * K;
-    t.sW = sW + (e * (N / BN) + tn) * KB;
-    t.Y = Y + row0 * N + n0;
-    t.rows = (int)s_task[2];
-    gemm_tile<GRAN_BLOCK>(t, K, N, lds);
-}
 
 // ---------------------------------------------------------------------------
 // Large-M kernel: workgroup tile 256 x 256, K step 128, 512 threads as 4 x 2
@@ -507,12 +271,329 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M and grouped kernel: tile 128 x 128, K step 128, 512 threads as 2 x 4
+// waves of 64 x 32 (two waves per SIMD), the same transposed MFMA, promotion
+// and 8-byte stores as
+// k_gemm_big, and a ring of 4 LDS stages filled by direct-to-LDS loads with 3
+// stages in flight.  At small M (decode, MoE experts) a tile's loads come
+// mostly from HBM, so the latency of one stage is far longer than its
+// multiply; three stages of lookahead keep ~96 KiB in flight per CU.
+// Every wave issues the same number of loads per stage (4 tile chunks plus,
+// in BLOCK mode, one scale: the eight waves load the 128 row scales in four
+// copies), so the waits are immediates: before multiplying stage kb a wave
+// waits until only the stages issued after kb may be outstanding, then a bare
+// s_barrier publishes everyone's loads.  (A barrier with a fence would wait for
+// every outstanding direct-to-LDS load and collapse the ring to one stage.)
+// ---------------------------------------------------------------------------
+constexpr int BMP = 128, BNP = 128, kThreadsP = 512, NSTP = 4;
+constexpr int64_t kPersistentGrid = 256;  // one workgroup per CU (LDS bound)
+constexpr int64_t kMaxExperts = 1024;     // prefix array size of the grouped kernel
+constexpr int kStageTileP = (BMP + BNP) * BK;            // 32 KiB of operands
+constexpr int kStageP = kStageTileP + 4 * BMP * 4;        // + four copies of sA
+constexpr int kLdsP = NSTP * kStageP;
+static_assert(kLdsP <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left unconstrained (gfx9)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int GRAN>
+__device__ __forceinline__ void stage_pipe(uint8_t* lds, int st, const Tile& t, int64_t K,
+                                           int64_t KB, int kb, int wave, int lane) {
+    uint8_t* la = lds + st * kStageP;
+    uint8_t* lb = la + BMP * BK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pbase = (i * 8 + wave) * 64;  // LDS chunk of lane 0 (8 rows per wave load)
+        const int p = pbase + lane;
+        const int r = p >> 3;
+        const int c = swz_pos(r, p & 7);
+        const int ra = r < t.rows ? r : t.rows - 1;
+        g2l_16(t.A + ra * K + kb * BK + c * 16, la + pbase * 16);
+        g2l_16(t.W + r * K + kb * BK + c * 16, lb + pbase * 16);
+    }
+    if constexpr (GRAN == GRAN_BLOCK) {
+        const int r = (wave & 1) * 64 + lane;
+        const int rr = r < t.rows ? r : t.rows - 1;
+        g2l_4(t.sA + rr * KB + kb, la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256);
+    }
+}
+
+template <int GRAN>
+__device__ __forceinline__ void wait_stage(int kb, int KB) {
+    constexpr int per = GRAN == GRAN_BLOCK ? 5 : 4;  // loads per stage per thread
+    if (kb + 2 < KB)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
+    else if (kb + 1 < KB)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(per));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// Scalar load of a wave-uniform element of a read-only device array: the
+// pointer and index go through readfirstlane (provably uniform) and the load
+// goes through the constant address space, which the backend lowers to
+// s_load.  A vector or flat load here would count in vmcnt, and its wait
+// would drain the whole stage ring.
+__device__ __forceinline__ float uniform_load(const float* p, int idx) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    typedef const __attribute__((address_space(4))) float cfloat;
+    cfloat* c = (cfloat*)(((uint64_t)hi << 32) | lo);
+    return c[__builtin_amdgcn_readfirstlane(idx)];
+}
+
+// Where a persistent workgroup's tiles come from.  Dense: a tm_count x
+// tn_count grid, row tiles of one column tile adjacent.  Grouped (MoE): expert
+// by expert, then column tile by column tile with that expert's row tiles
+// adjacent; pre[] (in LDS) is the prefix over experts of ceil(rows_e/128) * NT.
+struct TileSpace {
+    const uint8_t* A;
+    const uint8_t* W;
+    const float* sA;
+    const float* sW;
+    uint16_t* Y;
+    const int32_t* offsets;  // grouped only (device)
+    const int32_t* pre;      // grouped only (LDS), E + 1 entries
+    const int32_t* rlo;      // grouped only (LDS): expert e's rows [rlo[e], rhi[e])
+    const int32_t* rhi;
+    int64_t M, N, K, E;
+    int64_t tm_count;        // dense only
+};
+
+template <int GRAN, bool GROUPED>
+__device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
+    const int64_t KB = S.K / BK, NT = S.N / BNP;
+    Tile t;
+    int64_t row0, n0, e = 0, rows;
+    if constexpr (GROUPED) {
+        int lo = 0, hi = (int)S.E - 1;  // last expert whose prefix start <= logical
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (S.pre[mid] <= logical) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+        const int64_t r_lo = S.rlo[e], r_hi = S.rhi[e];
+        const int64_t mt = (r_hi - r_lo + BMP - 1) / BMP;
+        const int64_t lt = logical - S.pre[e];
+        const int64_t tn = lt / mt, tm = lt % mt;
+        row0 = r_lo + tm * BMP;
+        n0 = tn * BNP;
+        rows = (r_hi - row0) < BMP ? (r_hi - row0) : BMP;
+        t.W = S.W + (e * S.N + n0) * S.K;
+        t.sW = S.sW + (e * NT + tn) * KB;
+    } else {
+        const int64_t tm = logical % S.tm_count, tn = logical / S.tm_count;
+        row0 = tm * BMP;
+        n0 = tn * BNP;
+        rows = (S.M - row0) < BMP ? (S.M - row0) : BMP;
+        t.W = S.W + n0 * S.K;
+        t.sW = GRAN == GRAN_BLOCK ? S.sW + tn * KB : S.sW + n0;
+    }
+    t.A = S.A + row0 * S.K;
+    t.sA = GRAN == GRAN_BLOCK ? S.sA + row0 * KB : S.sA + row0;
+    t.Y = S.Y + row0 * S.N + n0;
+    t.rows = (int)rows;
+    return t;
+}
+
+// Persistent small-M / grouped kernel.  The grid holds one workgroup per CU
+// (at most); XCD x = blockIdx % 8 owns the x-th eighth of the tile order and
+// its workgroups take every nx-th tile of it, so the workgroups of one XCD
+// work on adjacent tiles together.  A workgroup's K steps over all of its
+// tiles form one sequence g = (tile i, k block) that the 4-stage ring walks
+// without a break: the next tile's first stages load while the current tile
+// finishes.
+template <int GRAN, bool GROUPED>
+__global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t dense_tiles) {
+    // one LDS object for the stage ring and (grouped) the expert tables: with
+    // separate __shared__ arrays the compiler can no longer tell the
+    // direct-to-LDS stage writes from the operand reads and waits for every
+    // outstanding load before each read
+    constexpr int kTab = GROUPED ? (3 * kMaxExperts + 1) * 4 : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP + kTab];
+    int32_t* s_pre = reinterpret_cast<int32_t*>(lds + kLdsP);
+    int32_t* s_rlo = s_pre + kMaxExperts + 1;
+    int32_t* s_rhi = s_rlo + kMaxExperts;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;  // wn in 0..3: 32 columns each
+    const int lr = lane & 15, lk = lane >> 4;
+    const int64_t KB = S.K / BK;
+
+    int64_t T = dense_tiles;
+    if constexpr (GROUPED) {
+        // prefix over experts of their tile counts, into LDS (wave 0)
+        const int64_t NT = S.N / BNP;
+        if (wave == 0) {
+            int64_t base = 0;
+            for (int64_t e0 = 0; e0 < S.E; e0 += 64) {
+                const int64_t e = e0 + lane;
+                int64_t cnt = 0;
+                if (e < S.E) {
+                    int64_t lo = S.offsets[e], hi = S.offsets[e + 1];
+                    lo = lo < 0 ? 0 : (lo > S.M ? S.M : lo);
+                    hi = hi < lo ? lo : (hi > S.M ? S.M : hi);
+                    cnt = (hi - lo + BMP - 1) / BMP * NT;
+                    s_rlo[e] = (int32_t)lo;
+                    s_rhi[e] = (int32_t)hi;
+                }
+                int64_t incl = cnt;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int64_t up = __shfl_up(incl, o);
+                    if (lane >= o) incl += up;
+                }
+                if (e < S.E) s_pre[e] = (int32_t)(base + incl - cnt);
+                base += __shfl(incl, 63);
+            }
+            if (lane == 0) s_pre[S.E] = (int32_t)base;
+        }
+        __syncthreads();
+        S.pre = s_pre;
+        S.rlo = s_rlo;
+        S.rhi = s_rhi;
+        T = s_pre[S.E];
+    }
+    // this workgroup's tiles: first, first + nx, ... (< last)
+    const int64_t G = gridDim.x, bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+    const int64_t nx = (G - xcd + 7) >> 3;  // workgroups on this XCD
+    const int64_t q = T >> 3, rem = T & 7;
+    const int64_t first_x = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+    const int64_t last_x = first_x + (xcd < rem ? q + 1 : q);
+    const int64_t first = first_x + j;
+    const int64_t ntiles = first < last_x ? (last_x - first + nx - 1) / nx : 0;
+    const int64_t NG = ntiles * KB;  // K steps of all this workgroup's tiles
+    if (NG == 0) return;  // whole workgroup leaves together
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Loop counters are 32-bit and advanced incrementally: a 64-bit division
+    // in the loop is expanded on the vector ALU, its result (and any address
+    // built from it) lands in VGPRs, and a weight-scale read then becomes a
+    // vector load whose wait drains the whole stage ring.
+    const int kbn = (int)KB, ng = (int)NG;
+    Tile lt = tile_at<GRAN, GROUPED>(S, first);  // tile being loaded
+    int l_ti = 0, l_kb = 0;                      // (tile, k block) of the next stage to load
+#pragma unroll
+    for (int st = 0; st < NSTP - 1; ++st) {
+        if (st < ng) {
+            stage_pipe<GRAN>(lds, st, lt, S.K, KB, l_kb, wave, lane);
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_ti;
+                if (l_ti < ntiles) lt = tile_at<GRAN, GROUPED>(S, first + l_ti * nx);
+            }
+        }
+    }
+    Tile ct = tile_at<GRAN, GROUPED>(S, first);  // tile being multiplied
+    int c_ti = 0, kb = 0;
+
+    for (int g = 0; g < ng; ++g) {
+        asm volatile("" ::: "memory");
+        wait_stage<GRAN>(g, ng);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (g + NSTP - 1 < ng) {  // refill the stage consumed at g - 1
+            stage_pipe<GRAN>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_ti;
+                if (l_ti < ntiles) lt = tile_at<GRAN, GROUPED>(S, first + l_ti * nx);
+            }
+        }
+
+        const uint8_t* la = lds + (g % NSTP) * kStageP;
+        const uint8_t* lb = la + BMP * BK;
+        v8i x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
+        if constexpr (GRAN == GRAN_BLOCK) {
+            const float sw = uniform_load(ct.sW, kb);
+            const float* lsa = reinterpret_cast<const float*>(la + kStageTileP);
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * sw;
+            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            v8i wcur = frag(lb, wn * 32 + lr, lk);
+            v4f prev;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                v8i wnext = wcur;
+                if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4f pk = mfma_f8(wcur, x[i], zero);
+                    if (i > 0 || jj > 0) {
+                        const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? jj : jj - 1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
+                    }
+                    prev = pk;
+                }
+                wcur = wnext;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[3][1][e] = __builtin_fmaf(prev[e], sc[3], acc[3][1][e]);
+        } else {
+            v8i wcur = frag(lb, wn * 32 + lr, lk);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                v8i wnext = wcur;
+                if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i][jj] = mfma_f8(wcur, x[i], acc[i][jj]);
+                wcur = wnext;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        if (kb == kbn - 1) {  // tile done: bf16 stores, fresh accumulators
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * 64 + i * 16 + lr;
+                float sa = 1.0f;
+                if constexpr (GRAN == GRAN_ROW) sa = ct.sA[r < ct.rows ? r : ct.rows - 1];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    v4f v = acc[i][jj];
+                    acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (GRAN == GRAN_ROW) {
+                        const v4f s4 =
+                            *reinterpret_cast<const v4f*>(ct.sW + wn * 32 + jj * 16 + 4 * lk);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+                    }
+                    if (r < ct.rows) {
+                        uint2 o;
+                        o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+                        o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + wn * 32 + jj * 16 +
+                                                  4 * lk) = o;
+                    }
+                }
+            }
+        }
+        if (++kb == kbn) {
+            kb = 0;
+            ++c_ti;
+            if (c_ti < ntiles) ct = tile_at<GRAN, GROUPED>(S, first + c_ti * nx);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                        void* y, int64_t M, int64_t N, int64_t K, int gran, hipStream_t st) {
-    const int64_t tiles = ((M + BM - 1) / BM) * (N / BN);
-    if (tiles == 0) return hipSuccess;
+    if (M == 0) return hipSuccess;
     const auto* A = static_cast<const uint8_t*>(a);
     const auto* Wp = static_cast<const uint8_t*>(w);
     auto* Yp = static_cast<uint16_t*>(y);
@@ -526,23 +607,34 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
                                st, A, Wp, a_s, w_s, Yp, M, N, K);
         return hipGetLastError();
     }
+    TileSpace S{};
+    S.A = A; S.W = Wp; S.sA = a_s; S.sW = w_s; S.Y = Yp;
+    S.M = M; S.N = N; S.K = K; S.E = 0;
+    S.tm_count = (M + BMP - 1) / BMP;
+    const int64_t tiles = S.tm_count * (N / BNP);
+    const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
     if (gran == GRAN_BLOCK)
-        hipLaunchKernelGGL(k_gemm<GRAN_BLOCK>, dim3((unsigned)tiles), dim3(kThreads), 0, st, A,
-                           Wp, a_s, w_s, Yp, M, N, K);
+        hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, false>), dim3((unsigned)grid), dim3(kThreadsP),
+                           0, st, S, tiles);
     else
-        hipLaunchKernelGGL(k_gemm<GRAN_ROW>, dim3((unsigned)tiles), dim3(kThreads), 0, st, A,
-                           Wp, a_s, w_s, Yp, M, N, K);
+        hipLaunchKernelGGL((k_gemm_pipe<GRAN_ROW, false>), dim3((unsigned)grid), dim3(kThreadsP), 0,
+                           st, S, tiles);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                                const int32_t* offsets, void* y, int64_t T, int64_t E,
                                int64_t N, int64_t K, hipStream_t st) {
-    const int64_t mt = (T + BM - 1) / BM + E;  // >= sum_e ceil(rows_e / 128)
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_grouped_gemm, dim3((unsigned)mt, (unsigned)(N / BN)), dim3(kThreads), 0,
-                       st, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w), a_s,
-                       w_s, offsets, static_cast<uint16_t*>(y), T, E, N, K);
+    TileSpace S{};
+    S.A = static_cast<const uint8_t*>(a);
+    S.W = static_cast<const uint8_t*>(w);
+    S.sA = a_s; S.sW = w_s;
+    S.Y = static_cast<uint16_t*>(y);
+    S.offsets = offsets;
+    S.M = T; S.N = N; S.K = K; S.E = E;
+    hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
+                       dim3(kThreadsP), 0, st, S, (int64_t)0);
     return hipGetLastError();
 }
 

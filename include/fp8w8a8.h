@@ -171,7 +171,8 @@ int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_
  *             offsets[E] = T (empty experts allowed).  The kernel reads and
  *             writes only rows in [0, T) whatever the offsets hold.
  *   y   : bf16 [T, N] (out); rows covered by no expert are left untouched.
- *   K % 128 != 0 or N % 128 != 0 -> FP8_ERR_SHAPE; E < 1 -> FP8_ERR_ARG.
+ *   K % 128 != 0 or N % 128 != 0 -> FP8_ERR_SHAPE; E < 1, E > 1024 or
+ *   T > 2^31 - 1 -> FP8_ERR_ARG.
  */
 int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
                                  const float* w_s, const int32_t* offsets, void* y_bf16,

@@ -102,6 +102,8 @@ def test_gemm_validation(L):
     assert L.fp8_gemm_a8w8_scaled(None, None, None, None, None, None, 0, 256, 256, 0, None) == OK
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 0, 256, 256, None) == ARG
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 4, 256, 100, None) == SHAPE
+    assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 1025, 256, 256, None) == ARG
+    assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 2**31, 4, 256, 256, None) == ARG
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, vp(FAKE + 2), f, 64, 4, 256, 256,
                                           None) == ALIGN
     if not _gpu():
