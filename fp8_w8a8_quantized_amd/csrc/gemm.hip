@@ -60,7 +60,7 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
 // such group.  Row parity already selects the bank half (rows are 128 bytes),
 // so XOR-ing the chunk with (r >> 1) & 7 spreads the 8 rows of each parity
 // over 8 distinct 16-byte bank groups: conflict-free.
-__device__ __forceinline__ int swz_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz_pos(int r, int c) { return c ^ ((r & 4) | ((r >> 1) & 1)); }
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + (swz_pos(r, c) << 4); }
 
 // One output tile's work description.
@@ -97,7 +97,8 @@ struct Tile {
 // ---------------------------------------------------------------------------
 constexpr int BM2 = 256, BN2 = 256, kThreads2 = 512;
 constexpr int kStage2 = (BM2 + BN2) * BK;             // 64 KiB per stage
-constexpr int kLds2 = 2 * kStage2 + 2 * BM2 * 4;       // two stages + two sA slices
+constexpr int kSw2 = 2 * kStage2 + 2 * BM2 * 4;        // after two stages + two sA slices
+constexpr int kLds2 = kSw2 + 2 * 256;                  // + two 256-byte sW slices
 static_assert(kLds2 <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -110,29 +111,78 @@ __device__ __forceinline__ void g2l_4(const void* g, uint8_t* l) {
     __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 4, 0, 0);
 }
 
-// Stage K block kb of the A and W tiles (and the A scales) into LDS stage st.
+// Buffer resource over `bytes` bytes at p (gfx9 raw buffer: stride 0, 32-bit
+// data format word).  Loads through it take 32-bit offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Direct-to-LDS load through a buffer resource: lane i's `size` bytes from
+// byte voff + soff land at l + size * i.  Unlike the global form, the buffer
+// form is not a FLAT instruction, so the compiler keeps counted lgkmcnt waits
+// for the LDS reads that run while it is in flight.
+__device__ __forceinline__ void b2l(__amdgpu_buffer_rsrc_t r, uint8_t* l, int size, int voff,
+                                    int soff) {
+    if (size == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 4, voff, soff, 0, 0);
+}
+
+// Per-tile load sources of the large-M kernel: buffer resources over the
+// tile's A rows, W rows and scales, and each lane's loop-invariant offsets.
+struct BigSrc {
+    __amdgpu_buffer_rsrc_t a, w, sa, sw;
+    int offa[4], offw[4];  // byte offsets of this lane's 16-byte chunks at kb = 0
+    int offsa, offsw;      // byte offsets of this lane's scale at kb = 0
+};
+
 template <int GRAN>
-__device__ __forceinline__ void stage_big(uint8_t* lds, int st, const uint8_t* A, const uint8_t* W,
-                                          const float* sA, int rows, int64_t K, int64_t KB,
-                                          int64_t kb, int wave, int lane) {
+__device__ __forceinline__ BigSrc big_src(const uint8_t* A, const uint8_t* W, const float* sA,
+                                          const float* sW, int rows, int K, int KB, int wave,
+                                          int lane) {
+    BigSrc S;
+    S.a = buffer_rsrc(A, rows * K);
+    S.w = buffer_rsrc(W, BN2 * K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = (i * 8 + wave) * 64 + lane;  // LDS chunk this lane fills
+        const int r = p >> 3;
+        const int c = swz_pos(r, p & 7);           // the tile chunk whose LDS slot is p
+        const int ra = r < rows ? r : rows - 1;
+        S.offa[i] = ra * K + c * 16;
+        S.offw[i] = r * K + c * 16;
+    }
+    if constexpr (GRAN == GRAN_BLOCK) {
+        S.sa = buffer_rsrc(sA, rows * KB * 4);
+        S.sw = buffer_rsrc(sW, 2 * KB * 4);
+        const int r = (wave & 3) * 64 + lane;
+        S.offsa = (r < rows ? r : rows - 1) * KB * 4;
+        S.offsw = (lane & 1) * KB * 4;  // lane l: weight block l & 1 of the tile
+    } else {
+        S.sa = S.sw = S.a;
+        S.offsa = S.offsw = 0;
+    }
+    return S;
+}
+
+// Stage K block kb of the A and W tiles (and, for block scales, the A and W
+// scales of kb) into LDS stage st.
+template <int GRAN>
+__device__ __forceinline__ void stage_big(uint8_t* lds, int st, const BigSrc& S, int kb, int wave) {
     uint8_t* la = lds + st * kStage2;
     uint8_t* lb = la + BM2 * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int pbase = (i * 8 + wave) * 64;  // LDS chunk of lane 0 (8 rows per wave load)
-        const int p = pbase + lane;
-        const int r = p >> 3;
-        const int c = swz_pos(r, p & 7);  // the global chunk whose LDS slot is p
-        const int ra = r < rows ? r : rows - 1;
-        g2l_16(A + ra * K + kb * BK + c * 16, la + pbase * 16);
-        g2l_16(W + r * K + kb * BK + c * 16, lb + pbase * 16);
+        b2l(S.a, la + pbase * 16, 16, S.offa[i], kb * BK);
+        b2l(S.w, lb + pbase * 16, 16, S.offw[i], kb * BK);
     }
     if constexpr (GRAN == GRAN_BLOCK) {
-        if (wave < 4) {
-            const int r = wave * 64 + lane;
-            const int rr = r < rows ? r : rows - 1;
-            g2l_4(sA + rr * KB + kb, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256);
-        }
+        if (wave < 4)
+            b2l(S.sa, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256, 4, S.offsa, kb * 4);
+        else if (wave == 4)
+            b2l(S.sw, lds + kSw2 + st * 256, 4, S.offsw, kb * 4);
     }
 }
 
@@ -142,6 +192,172 @@ __device__ __forceinline__ v8i frag(const uint8_t* base, int r, int lk) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Tile coordinates of logical tile `logical` of the large-M kernel: bands of
+// 4 row tiles, column-major inside a band, so consecutive logical tiles share
+// A rows and W columns.
+struct BigTile {
+    int tm, tn, rows;
+};
+
+__device__ __forceinline__ BigTile big_tile(int logical, int tm_count, int tn_count, int64_t M) {
+    constexpr int GROUP = 4;
+    const int band = logical / (GROUP * tn_count);
+    const int first_m = band * GROUP;
+    const int band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
+    const int in_band = logical - band * GROUP * tn_count;
+    BigTile t;
+    t.tm = first_m + in_band % band_m;
+    t.tn = in_band / band_m;
+    const int64_t left = M - (int64_t)t.tm * BM2;
+    t.rows = left < BM2 ? (int)left : BM2;
+    return t;
+}
+
+template <int GRAN>
+__device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* A, const uint8_t* W,
+                                               const float* sA, const float* sW, int64_t K, int KB,
+                                               int wave, int lane) {
+    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const float* sAt = GRAN == GRAN_BLOCK ? sA + row0 * KB : sA + row0;
+    const float* sWt = GRAN == GRAN_BLOCK ? sW + (n0 / BK) * KB : sW + n0;
+    return big_src<GRAN>(A + row0 * K, W + n0 * K, sAt, sWt, t.rows, (int)K, KB, wave, lane);
+}
+
+// One K block of a wave's 64 x 128 output on LDS stage `cur`.
+template <int GRAN>
+__device__ __forceinline__ void big_kblock(const uint8_t* lds, int cur, v4f (&acc)[4][8], int wm,
+                                           int wn, int lr, int lk) {
+    const uint8_t* la = lds + cur * kStage2;
+    const uint8_t* lb = la + BM2 * BK;
+    v8i x[4];
+    if constexpr (GRAN == GRAN_BLOCK) {
+        // Every operand and scale comes from LDS, so each wait below is a
+        // counted lgkmcnt on in-order LDS reads (a scalar load in flight
+        // would force lgkmcnt(0) on every wait).
+        const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + cur * BM2 * 4);
+        const float sw = reinterpret_cast<const float*>(lds + kSw2 + cur * 256)[wn];
+        float sa4[4], sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa4[i] = lsa[wm * 64 + i * 16 + lr];
+        v8i wcur = frag(lb, wn * 128 + lr, lk);
+        x[0] = frag(la, wm * 64 + lr, lk);
+        x[1] = frag(la, wm * 64 + 16 + lr, lk);
+        __builtin_amdgcn_sched_barrier(0);
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        // Column step 0: the remaining X fragments and the next W fragment
+        // are read while the first MFMAs run.
+        x[2] = frag(la, wm * 64 + 32 + lr, lk);
+        x[3] = frag(la, wm * 64 + 48 + lr, lk);
+        v4f prev = mfma_f8(wcur, x[0], zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = sa4[i] * sw;
+        v8i wnext = frag(lb, wn * 128 + 16 + lr, lk);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            const v4f p = mfma_f8(wcur, x[i], zero);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i - 1][0][e] = __builtin_fmaf(prev[e], sc[i - 1], acc[i - 1][0][e]);
+            prev = p;
+        }
+        wcur = wnext;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            wnext = wcur;
+            if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v4f p = mfma_f8(wcur, x[i], zero);
+                // promote the previous MFMA's result (tile (i-1, j) or (3, j-1))
+                const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? j : j - 1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
+                prev = p;
+            }
+            wcur = wnext;
+            // Issue order per column step: MFMA, the next W fragment's LDS
+            // reads, then the 4 FMAs that promote the previous MFMA after
+            // each further MFMA.  A promotion never reads the result of
+            // the MFMA issued just before it, so the VALU co-issues with
+            // the matrix core instead of waiting on it.
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (j < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                if (t < 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[3][7][e] = __builtin_fmaf(prev[e], sc[3], acc[3][7][e]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
+        v8i wcur = frag(lb, wn * 128 + lr, lk);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v8i wnext = wcur;
+            if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(wcur, x[i], acc[i][j]);
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Store a wave's 64 x 128 block of tile t (bf16, 8 bytes per lane and column
+// tile) and clear the accumulators for the next tile.
+template <int GRAN>
+__device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
+                                          const float* sA, const float* sW, int64_t N, int wm,
+                                          int wn, int lr, int lk) {
+    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + lr;
+        if (r < t.rows) {
+            float sa = 1.0f;
+            if constexpr (GRAN == GRAN_ROW) sa = sA[row0 + r];
+            uint16_t* yrow = Y + (row0 + r) * N + n0 + wn * 128 + 4 * lk;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                v4f v = acc[i][j];
+                if constexpr (GRAN == GRAN_ROW) {
+                    const v4f s4 =
+                        *reinterpret_cast<const v4f*>(sW + n0 + wn * 128 + j * 16 + 4 * lk);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+                }
+                uint2 o;
+                o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+                o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                *reinterpret_cast<uint2*>(yrow + j * 16) = o;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+// Persistent: workgroup b runs on XCD b % 8; the XCD's workgroups share a
+// contiguous range of logical tiles and take them round-robin.  The steps
+// (tile, K block) of one workgroup form one stream through the two LDS
+// stages, so the first K block of the next tile loads while the last K block
+// of the current one is multiplied and its output stored.
 template <int GRAN>
 __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ W,
@@ -150,32 +366,19 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
                                                         uint16_t* __restrict__ Y, int64_t M,
                                                         int64_t N, int64_t K) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
-    const int64_t tm_count = (M + BM2 - 1) / BM2, tn_count = N / BN2;
-    const int64_t T = tm_count * tn_count;
-    // XCD-contiguous tile order: XCD x = blockIdx % 8 gets logical tiles
-    // [x * q + min(x, r), ...) where T = 8 q + r.
-    const int64_t bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
-    const int64_t q = T >> 3, rem = T & 7;
-    const int64_t logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-    constexpr int64_t GROUP = 4;
-    const int64_t band = logical / (GROUP * tn_count);
-    const int64_t first_m = band * GROUP;
-    const int64_t band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
-    const int64_t in_band = logical - band * GROUP * tn_count;
-    const int64_t tm = first_m + in_band % band_m, tn = in_band / band_m;
-
-    const int64_t KB = K / BK;
-    const int64_t row0 = tm * BM2, n0 = tn * BN2;
-    const int rows = (int)((M - row0) < BM2 ? (M - row0) : BM2);
-    const uint8_t* At = A + row0 * K;
-    const uint8_t* Wt = W + n0 * K;
-    const float* sAt = GRAN == GRAN_BLOCK ? sA + row0 * KB : sA + row0;
-    const float* sWt = GRAN == GRAN_BLOCK ? sW + (n0 / BK) * KB : sW + n0;
+    const int tm_count = (int)((M + BM2 - 1) / BM2), tn_count = (int)(N / BN2);
+    const int T = tm_count * tn_count;
+    const int KB = (int)(K / BK);
+    const int x = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int nwg = ((int)gridDim.x - x + 7) >> 3;  // workgroups on XCD x
+    const int q = T >> 3, rem = T & 7;
+    const int xbeg = x * q + (x < rem ? x : rem), tx = q + (x < rem ? 1 : 0);
+    if (idx >= tx) return;
+    const int nt = (tx - idx + nwg - 1) / nwg;  // tiles of this workgroup
+    const int first = xbeg + idx;               // its k-th tile: first + k * nwg
 
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave index made provably wave-uniform, so per-wave scale reads become
-    // scalar loads (a vector load would make the loop's vmcnt waits also wait
-    // for the next stage's direct-to-LDS loads)
+    // wave index made provably wave-uniform, so per-wave LDS bases are scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 3, wn = wave >> 2;
     const int lr = lane & 15, lk = lane >> 4;
@@ -186,88 +389,38 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    stage_big<GRAN>(lds, 0, At, Wt, sAt, rows, K, KB, 0, wave, lane);
+    int lt = 0, lkb = 0;  // load cursor: tile, K block
+    BigSrc S = big_tile_src<GRAN>(big_tile(first, tm_count, tn_count, M), A, W, sA, sW, K, KB,
+                                  wave, lane);
+    stage_big<GRAN>(lds, 0, S, 0, wave);
+    // Materialize the output pointer now: a scalar load still in flight
+    // during the loop would turn every LDS wait into lgkmcnt(0).
+    asm volatile("" ::"s"(Y));
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's LDS-bound loads landed
     __syncthreads();
 
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int cur = (int)(kb & 1);
-        if (kb + 1 < KB) stage_big<GRAN>(lds, cur ^ 1, At, Wt, sAt, rows, K, KB, kb + 1, wave, lane);
-
-        const uint8_t* la = lds + cur * kStage2;
-        const uint8_t* lb = la + BM2 * BK;
-        v8i x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
-        if constexpr (GRAN == GRAN_BLOCK) {
-            const float sw = sWt[wn * KB + kb];
-            const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + cur * BM2 * 4);
-            float sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * sw;
-            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            v8i wcur = frag(lb, wn * 128 + lr, lk);
-            v4f prev;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                v8i wnext = wcur;
-                if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4f p = mfma_f8(wcur, x[i], zero);
-                    // promote the previous MFMA's result (tile (i-1, j) or (3, j-1))
-                    if (i > 0 || j > 0) {
-                        const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? j : j - 1;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
-                    }
-                    prev = p;
-                }
-                wcur = wnext;
-                // keep each column tile's MFMAs in their step: hoisting them
-                // further only raises register pressure past 256 VGPRs
-                __builtin_amdgcn_sched_barrier(0);
+    int ct = 0, ckb = 0;  // compute cursor
+    const int NS = nt * KB;
+    for (int g = 0; g < NS; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < NS) {
+            if (++lkb == KB) {
+                lkb = 0;
+                ++lt;
+                S = big_tile_src<GRAN>(big_tile(first + lt * nwg, tm_count, tn_count, M), A, W,
+                                       sA, sW, K, KB, wave, lane);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[3][7][e] = __builtin_fmaf(prev[e], sc[3], acc[3][7][e]);
-        } else {
-            v8i wcur = frag(lb, wn * 128 + lr, lk);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                v8i wnext = wcur;
-                if (j < 7) wnext = frag(lb, wn * 128 + (j + 1) * 16 + lr, lk);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = mfma_f8(wcur, x[i], acc[i][j]);
-                wcur = wnext;
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            stage_big<GRAN>(lds, cur ^ 1, S, lkb, wave);
+        }
+        big_kblock<GRAN>(lds, cur, acc, wm, wn, lr, lk);
+        if (++ckb == KB) {
+            ckb = 0;
+            big_store<GRAN>(acc, big_tile(first + ct * nwg, tm_count, tn_count, M), Y, sA, sW, N,
+                            wm, wn, lr, lk);
+            ++ct;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // next stage's loads landed
         __syncthreads();
-    }
-
-    // epilogue: lane holds Y[row][col .. col+3] per tile -> one 8-byte bf16 store
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + lr;
-        if (r >= rows) continue;
-        float sa = 1.0f;
-        if constexpr (GRAN == GRAN_ROW) sa = sAt[r];
-        uint16_t* yrow = Y + (row0 + r) * N + n0 + wn * 128 + 4 * lk;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v4f v = acc[i][j];
-            if constexpr (GRAN == GRAN_ROW) {
-                const v4f s4 = *reinterpret_cast<const v4f*>(sWt + wn * 128 + j * 16 + 4 * lk);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
-            }
-            uint2 o;
-            o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-            o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
-            *reinterpret_cast<uint2*>(yrow + j * 16) = o;
-        }
     }
 }
 
@@ -597,14 +750,18 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     const auto* A = static_cast<const uint8_t*>(a);
     const auto* Wp = static_cast<const uint8_t*>(w);
     auto* Yp = static_cast<uint16_t*>(y);
-    if (M >= 1024 && N % BN2 == 0) {
-        const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
+    // The large-M kernel addresses a tile with 32-bit buffer offsets
+    // (256 rows x K bytes, so K <= 2^22) and counts tiles and steps in int.
+    const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
+    if (M >= 1024 && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
+        (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
+        const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
         if (gran == GRAN_BLOCK)
-            hipLaunchKernelGGL(k_gemm_big<GRAN_BLOCK>, dim3((unsigned)tiles2), dim3(kThreads2), 0,
-                               st, A, Wp, a_s, w_s, Yp, M, N, K);
+            hipLaunchKernelGGL(k_gemm_big<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
+                               a_s, w_s, Yp, M, N, K);
         else
-            hipLaunchKernelGGL(k_gemm_big<GRAN_ROW>, dim3((unsigned)tiles2), dim3(kThreads2), 0,
-                               st, A, Wp, a_s, w_s, Yp, M, N, K);
+            hipLaunchKernelGGL(k_gemm_big<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
+                               a_s, w_s, Yp, M, N, K);
         return hipGetLastError();
     }
     TileSpace S{};

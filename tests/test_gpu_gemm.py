@@ -55,8 +55,11 @@ def test_block_small_shapes(M, N, K):
     assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1024, 256, 256), (1100, 768, 640), (2047, 512, 1152)])
+@pytest.mark.parametrize("M,N,K", [(1024, 256, 256), (1100, 768, 640), (2047, 512, 1152),
+                                   (8200, 2304, 256)])
 def test_block_large_m_shapes(M, N, K):
+    # 8200 x 2304: 33 x 9 = 297 tiles of 256 x 256 on 256 workgroups, so some
+    # workgroups run two tiles; the last row tile holds 8 rows
     say(f"block GEMM (large-M kernel) {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + N + K)
     W = synth.weight(N, K, seed=N + K + 1)
@@ -65,7 +68,7 @@ def test_block_large_m_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (130, 384, 512), (77, 256, 5120),
-                                   (1100, 768, 640), (1024, 256, 4096)])
+                                   (1100, 768, 640), (1024, 256, 4096), (8200, 2304, 256)])
 def test_row_small_shapes(M, N, K):
     say(f"row GEMM {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + 3)
