@@ -1,13 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of the FP8 W8A8 hot path on one MI355X.
 
-One step = one RL step's worth of the hot path over a 36-layer Qwen3-8B-shaped
-policy (qkv 4096->6144, o 4096->4096, gate_up 4096->24576, down 12288->4096):
-  1. re-quantize all 144 bf16 policy weights into E4M3 128x128 blocks with fp32
-     scales (one batched library call);
-  2. for every layer and linear, quantize that layer's bf16 activations in 1x128
-     groups and run the block-scaled W8A8 GEMM, bf16 out -- at M = 8192 (prefill)
-     and at M = 256 (decode).
+One step = one pass of every step of the hot path:
+  1. re-quantize all 144 bf16 weights of a 36-layer Qwen3-8B-shaped policy
+     (qkv 4096->6144, o 4096->4096, gate_up 4096->24576, down 12288->4096) into
+     E4M3 128x128 blocks with fp32 scales (one batched library call), and the
+     two stacked expert weights of a Qwen3-30B-A3B-shaped MoE layer (a second);
+  2. for every layer and linear of the dense policy, quantize that layer's bf16
+     activations in 1x128 groups and run the block-scaled W8A8 GEMM, bf16 out,
+     at M = 8192 (prefill) and at M = 256 (decode);
+  3. the per-token path: fused RMSNorm + per-token quantization of h [4096,
+     5120], per-row quantization of a [12288, 5120] weight, row-scaled GEMM;
+  4. the MoE path: 1x128 quantization of the 32768 routed rows and the grouped
+     block-scaled GEMMs gate_up (N=1536, K=2048) and down (N=2048, K=768) over
+     128 experts with top-8 routing.
 Every (layer, linear) has its own weight and activation tensors, so weights
 and activations stream from HBM as they would in a real forward pass.  Inputs
 are seeded synthetic tensors generated on the device before timing.
@@ -15,13 +21,19 @@ are seeded synthetic tensors generated on the device before timing.
 Prints one JSON line.  ``value`` = all GEMM flops of a step / wall time of a
 step (the quantization work in the step is not counted as flops but its time
 is).  ``roofline`` is for the dominant kernel, the block-scaled GEMM at
-M = 8192, timed with HIP events on the launch stream inside the timed steps.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same work.
+M = 8192, timed with HIP events on the launch stream inside the timed steps;
+its ``traffic`` comes from the HBM counter summary committed under profiles/
+and is reported only while the GEMM sources still hash to the value recorded
+there.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the work.
+
+``--calibrate-copy`` instead runs a plain device copy of 1 GiB a few times,
+the reference kernel whose counter reading scales FETCH_SIZE / WRITE_SIZE.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +46,49 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 METRIC = "block-scaled FP8 GEMM TFLOPS (% FP8 MFMA peak); quantize/requant GB/s (% HBM)"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_big_m8192.md")
+GEMM_SOURCES = ["fp8_w8a8_quantized_amd/csrc/gemm.hip", "fp8_w8a8_quantized_amd/csrc/device.hpp",
+                "fp8_w8a8_quantized_amd/csrc/launch.hpp"]
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per M=8192 GEMM launch from the committed counter summary, or
+    None when the summary is missing or was taken on other GEMM sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("- `") and "`: " in line:
+                    k, v = line[3:].split("`: ", 1)
+                    fields[k] = v.strip().strip("`")
+        if fields.get("source_sha256") != gemm_source_hash():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy, three times (for the counter runs)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.full((n,), 3, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
 def parse():
@@ -44,15 +99,16 @@ def parse():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    ap.add_argument("--cpu-sample-layers", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true")
     return ap.parse_args()
 
 
-def cpu_baseline(rows: int):
-    """The oracle (as it stands) on a bounded sample of one step: re-quantize
-    one layer's four bf16 weights, quantize `rows` rows of each M = 8192
-    activation, fp64 GEMM of those rows.  Reported in GEMM TFLOP/s."""
-    import numpy as np
-
+def cpu_baseline(rows: int, layers: int):
+    """The oracle (as it stands) on a bounded sample of a step: for `layers`
+    layers, re-quantize the four bf16 weights, quantize `rows` rows of each
+    M = 8192 activation and run the fp64 GEMM of those rows.  Reported in GEMM
+    TFLOP/s."""
     import oracle
     import synth
 
@@ -63,34 +119,39 @@ def cpu_baseline(rows: int):
     except Exception:
         blas = 1
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    inputs = []
-    for j, name in enumerate(synth.DENSE_SHAPES):
-        N, K = synth.DENSE_SHAPES[name]
-        X = synth.act_col_outliers(rows, K, seed=500 + j)
-        W = synth.weight(N, K, seed=600 + j)
-        inputs.append((X, W))
     flops = 0.0
-    t0 = time.perf_counter()
-    for X, W in inputs:
-        qw, sw = oracle.quantize_weight_block(W, 0)
-        qa, sa = oracle.quantize_block(X)
-        y = oracle.gemm(qa, qw, sa, sw, oracle.GRAN_BLOCK)
-        flops += 2.0 * y.shape[0] * y.shape[1] * qa.shape[1]
-    dt = time.perf_counter() - t0
+    elapsed = 0.0
+    for li in range(layers):
+        inputs = []
+        for j, name in enumerate(synth.DENSE_SHAPES):
+            N, K = synth.DENSE_SHAPES[name]
+            X = synth.act_col_outliers(rows, K, seed=500 + 8 * li + j)
+            W = synth.weight(N, K, seed=600 + 8 * li + j)
+            inputs.append((X, W))
+        t0 = time.perf_counter()
+        for X, W in inputs:
+            qw, sw = oracle.quantize_weight_block(W, 0)
+            qa, sa = oracle.quantize_block(X)
+            y = oracle.gemm(qa, qw, sa, sw, oracle.GRAN_BLOCK)
+            flops += 2.0 * y.shape[0] * y.shape[1] * qa.shape[1]
+        elapsed += time.perf_counter() - t0
     return {
-        "value": flops / dt / 1e12,
+        "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": max(omp, blas),
         "kind": "oracle",
-        "sample": (f"one layer of the step: requantize the 4 bf16 weights (128x128, fp32 "
-                   f"scales), 1x128-quantize {rows} rows of each M=8192 activation, fp64 "
-                   f"dequantize-then-matmul of those rows; {flops / 1e9:.1f} GFLOP in "
-                   f"{dt:.1f} s"),
+        "sample": (f"{layers} layers of the step: requantize each layer's 4 bf16 weights "
+                   f"(128x128, fp32 scales), 1x128-quantize {rows} rows of each M=8192 "
+                   f"activation, fp64 dequantize-then-matmul of those rows; "
+                   f"{flops / 1e9:.1f} GFLOP in {elapsed:.1f} s (input generation not timed)"),
     }
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the sharded path is described in DESIGN.md, not built)"}))
@@ -133,6 +194,36 @@ def main():
     for i in range(len(W)):
         descs[i] = fp8._WeightDesc(W[i].data_ptr(), Wq[i].data_ptr(), Ws[i].data_ptr(),
                                    W[i].shape[0], W[i].shape[1])
+
+    # per-token path: RMSNorm + per-token quant -> row-scaled GEMM
+    RM, RK, RN = synth.RMS_M, synth.RMS_K, synth.RMS_N
+    h, gamma = synth.rms_inputs(seed=1, device=dev)
+    Wr = synth.weight(RN, RK, seed=31, device=dev)
+    hq = torch.empty((RM, RK), dtype=torch.uint8, device=dev)
+    hs = torch.empty((RM,), dtype=torch.float32, device=dev)
+    Wrq = torch.empty((RN, RK), dtype=torch.uint8, device=dev)
+    Wrs = torch.empty((RN,), dtype=torch.float32, device=dev)
+    Yr = torch.empty((RM, RN), dtype=torch.bfloat16, device=dev)
+
+    # MoE path: routed rows, stacked expert weights, grouped GEMMs
+    moe = {}
+    for which in ("gate_up", "down"):
+        A, Wm, offsets = synth.moe_inputs(which, seed=0, device=dev)
+        E, N, K = Wm.shape
+        T = A.shape[0]
+        moe[which] = dict(
+            A=A, W=Wm.reshape(E * N, K), E=E, N=N, K=K, T=T,
+            off=torch.as_tensor(offsets, dtype=torch.int32, device=dev),
+            Aq=torch.empty((T, K), dtype=torch.uint8, device=dev),
+            As=torch.empty((T, K // 128), dtype=torch.float32, device=dev),
+            Wq=torch.empty((E * N, K), dtype=torch.uint8, device=dev),
+            Ws=torch.empty((E * N // 128, K // 128), dtype=torch.float32, device=dev),
+            Y=torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+    mdescs = (fp8._WeightDesc * 2)()
+    for i, which in enumerate(("gate_up", "down")):
+        m = moe[which]
+        mdescs[i] = fp8._WeightDesc(m["W"].data_ptr(), m["Wq"].data_ptr(), m["Ws"].data_ptr(),
+                                    m["E"] * m["N"], m["K"])
     torch.cuda.synchronize(dev)
 
     # ---- pre-marshalled calls of one step, grouped by kernel category ----
@@ -149,6 +240,24 @@ def main():
                               (vp(Xq[key].data_ptr()), vp(Wq[wi].data_ptr()),
                                vp(Xs[key].data_ptr()), vp(Ws[wi].data_ptr()), None,
                                vp(Y[(j, M)].data_ptr()), M, N, K, fp8.GRAN_BLOCK, sptr)))
+    calls.append(("rmsnorm_quant", L.fp8_rmsnorm_quant,
+                  (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hs.data_ptr()), vp(gamma.data_ptr()),
+                   synth.RMS_EPS, RM, RK, 0, sptr)))
+    calls.append(("quant_token_w", L.fp8_quantize_token,
+                  (vp(Wr.data_ptr()), RN, RK, vp(Wrq.data_ptr()), vp(Wrs.data_ptr()), sptr)))
+    calls.append(("gemm_row", L.fp8_gemm_a8w8_scaled,
+                  (vp(hq.data_ptr()), vp(Wrq.data_ptr()), vp(hs.data_ptr()), vp(Wrs.data_ptr()),
+                   None, vp(Yr.data_ptr()), RM, RN, RK, fp8.GRAN_ROW, sptr)))
+    calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
+    for which in ("gate_up", "down"):
+        m = moe[which]
+        calls.append(("quant_moe", L.fp8_quantize_block,
+                      (vp(m["A"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
+                       vp(m["As"].data_ptr()), sptr)))
+        calls.append(("gemm_moe", L.fp8_grouped_gemm_a8w8_scaled,
+                      (vp(m["Aq"].data_ptr()), vp(m["Wq"].data_ptr()), vp(m["As"].data_ptr()),
+                       vp(m["Ws"].data_ptr()), vp(m["off"].data_ptr()), vp(m["Y"].data_ptr()),
+                       m["T"], m["E"], m["N"], m["K"], sptr)))
 
     # algorithmic work per step, per category
     work = {"requant": {"bytes": 0.0}, "gemm_m8192": {"flops": 0.0, "bytes": 0.0},
@@ -163,7 +272,22 @@ def main():
                 g["flops"] += 2.0 * M * N * K
                 g["bytes"] += M * K + N * K + 4 * (M * (K // 128) + (N // 128) * (K // 128)) \
                     + 2 * M * N
-    launches = {"requant": 1}
+    work["rmsnorm_quant"] = {"bytes": 2 * RM * RK + RM * RK + 4 * RM + 2 * RK}
+    work["quant_token_w"] = {"bytes": 2 * RN * RK + RN * RK + 4 * RN}
+    work["gemm_row"] = {"flops": 2.0 * RM * RN * RK,
+                        "bytes": RM * RK + RN * RK + 4 * (RM + RN) + 2 * RM * RN}
+    work["requant_moe"] = {"bytes": 0.0}
+    work["quant_moe"] = {"bytes": 0.0}
+    work["gemm_moe"] = {"flops": 0.0, "bytes": 0.0}
+    for m in moe.values():
+        E, N, K, T = m["E"], m["N"], m["K"], m["T"]
+        work["requant_moe"]["bytes"] += 3 * E * N * K + 4 * (E * N // 128) * (K // 128)
+        work["quant_moe"]["bytes"] += 3 * T * K + 4 * T * (K // 128)
+        work["gemm_moe"]["flops"] += 2.0 * T * N * K
+        work["gemm_moe"]["bytes"] += T * K + E * N * K + 4 * (T * (K // 128) + (E * N // 128)
+                                                             * (K // 128)) + 2 * T * N
+    launches = {"requant": 1, "rmsnorm_quant": 1, "quant_token_w": 1, "gemm_row": 1,
+                "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2}
     for M in Ms:
         launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
 
@@ -197,7 +321,7 @@ def main():
     for cat, e0, e1 in events:
         per_cat_ms[cat] = per_cat_ms.get(cat, 0.0) + e0.elapsed_time(e1)
     ms_per_step = elapsed * 1e3 / args.steps
-    total_flops = work["gemm_m8192"]["flops"] + work["gemm_m256"]["flops"]
+    total_flops = sum(w.get("flops", 0.0) for w in work.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     breakdown = {}
@@ -217,8 +341,9 @@ def main():
     achieved = flops_per_launch / (dom["avg_launch_us"] * 1e-6) / 1e12
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
-        "kernel": "block-scaled FP8 GEMM (k_gemm<BLOCK>), M=8192 launches",
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+        "traffic": recorded_traffic(),
+        "kernel": "block-scaled FP8 GEMM k_gemm_big<0>, the 144 M=8192 launches of a step",
     }
 
     out = {
@@ -230,9 +355,17 @@ def main():
             "workload": ("qwen3-8b-shaped dense linears, block-scaled W8A8: per step, "
                          "128x128 re-quantization of the 36-layer bf16 policy, then for "
                          "every layer and linear 1x128 activation quant + GEMM at M=8192 "
-                         "and M=256"),
+                         "and M=256; plus once per step the per-token path (RMSNorm + "
+                         "per-token quant of [4096,5120], per-row weight quant of "
+                         "[12288,5120], row-scaled GEMM) and the qwen3-30b-a3b-shaped MoE "
+                         "path (expert re-quant, 1x128 quant of 32768 routed rows, grouped "
+                         "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts)"),
             "layers": layers, "M": list(Ms),
             "linears": {name: {"N": N, "K": K} for name, (N, K) in shapes},
+            "per_token": {"M": RM, "K": RK, "N": RN},
+            "moe": {"experts": moe["gate_up"]["E"], "rows": moe["gate_up"]["T"],
+                    "gate_up": {"N": moe["gate_up"]["N"], "K": moe["gate_up"]["K"]},
+                    "down": {"N": moe["down"]["N"], "K": moe["down"]["K"]}},
             "parallelism": "single-gpu",
         },
         "roofline": roofline,
@@ -240,7 +373,7 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows, args.cpu_sample_layers)
     print(json.dumps(out), flush=True)
 
 
