@@ -77,6 +77,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
         "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
         "fp8_encode_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),
+        "fp8_bf16_round_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -246,6 +247,16 @@ def grouped_gemm_a8w8_scaled(a: Tuple[torch.Tensor, torch.Tensor],
            L.fp8_grouped_gemm_a8w8_scaled(_ptr(qa), _ptr(qw), _ptr(sa), _ptr(sw), _ptr(offsets),
                                           _ptr(y), T, E, N, K, _stream(qa)))
     return y
+
+
+def bf16_round_f32_bits(first_bits: int, n: int, device="cuda") -> torch.Tensor:
+    """Diagnostic: bf16 bit patterns (as int16) of the rounded fp32 bit
+    patterns first_bits .. +n-1."""
+    out = torch.empty((n,), dtype=torch.int16, device=device)
+    L = load_library()
+    _check("fp8_bf16_round_f32_bits",
+           L.fp8_bf16_round_f32_bits(first_bits, n, _ptr(out), _stream(out)))
+    return out
 
 
 def encode_f32_bits(first_bits: int, n: int, device="cuda") -> torch.Tensor:

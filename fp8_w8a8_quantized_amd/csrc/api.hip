@@ -182,4 +182,14 @@ int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream) {
     return launched(fp8k::launch_encode_bits(first_bits, n, q, as_stream(stream)));
 }
 
+int fp8_bf16_round_f32_bits(uint64_t first_bits, int64_t n, void* out, void* stream) {
+    if (n < 0 || first_bits > 0xFFFFFFFFull || (uint64_t)n > 0x100000000ull - first_bits)
+        return FP8_ERR_ARG;
+    if (n == 0) return FP8_OK;
+    if (!out) return FP8_ERR_ARG;
+    if (!aligned(out, 16)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_bf16_bits(first_bits, n, out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -24,19 +24,19 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
     f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (a in the low half), round to nearest even, by the
+// gfx950 conversion v_cvt_pk_bf16_f32.  It matches the bit-level definition
+// (add 0x7FFF plus the kept LSB, truncate) on every non-NaN fp32 pattern,
+// subnormals included; fp8_bf16_round_f32_bits exposes it to that test.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
-// fp32 -> the fp32 value of its bf16 rounding (round to nearest even).
-__device__ __forceinline__ float bf16_round(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return __uint_as_float(u & 0xFFFF0000u);
-}
+// fp32 -> bf16 bit pattern, round to nearest even.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return bf16x2_rne(f, 0.0f) & 0xFFFFu; }
 
 // Four floats -> four E4M3FN bytes (byte i encodes element i).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {

@@ -412,8 +412,8 @@ __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, ui
                     for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
                 }
                 uint2 o;
-                o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-                o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                o.x = bf16x2_rne(v[0], v[1]);
+                o.y = bf16x2_rne(v[2], v[3]);
                 *reinterpret_cast<uint2*>(yrow + j * 16) = o;
             }
         }
@@ -819,8 +819,8 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
                     }
                     if (r < ct.rows) {
                         uint2 o;
-                        o.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-                        o.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                        o.x = bf16x2_rne(v[0], v[1]);
+                        o.y = bf16x2_rne(v[2], v[3]);
                         *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + wn * 32 + jj * 16 +
                                                   4 * lk) = o;
                     }

@@ -33,6 +33,7 @@ hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* ga
                                 int64_t M, int64_t K, int group_size, hipStream_t st);
 hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, hipStream_t st);
 hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st);
+hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                        void* y, int64_t M, int64_t N, int64_t K, int gran, hipStream_t st);

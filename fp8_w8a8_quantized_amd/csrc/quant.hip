@@ -166,7 +166,11 @@ __device__ __forceinline__ void rms_y8(const uint4& xv, const uint4& gv, float i
     unpack8(xv, f);
     unpack8(gv, g);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = bf16_round((f[j] * inv) * g[j]);
+    for (int j = 0; j < 8; j += 2) {
+        const uint32_t p = bf16x2_rne((f[j] * inv) * g[j], (f[j + 1] * inv) * g[j + 1]);
+        y[j] = bf16_lo(p);
+        y[j + 1] = bf16_hi(p);
+    }
 }
 
 __device__ __forceinline__ uint4 pack_bf16x8(const float (&y)[8]) {
@@ -188,7 +192,7 @@ __device__ __forceinline__ float sumsq8(float p, const uint4& xv) {
 }
 
 template <int VPL, int GROUP>
-__global__ __launch_bounds__(256) void k_rmsnorm_quant(uint2* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VPL <= 10 ? 4 : 1))) void k_rmsnorm_quant(uint2* __restrict__ q,
                                                        const uint4* __restrict__ x,
                                                        float* __restrict__ s,
                                                        const uint4* __restrict__ gamma,
@@ -384,6 +388,22 @@ hipError_t launch(Kern k, int64_t blocks, hipStream_t st, Args... args) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Diagnostic: bf16 rounding (the device helper every bf16 output uses) of the
+// fp32 bit patterns first .. first + n - 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
+                                                   uint32_t* __restrict__ out) {
+    const int64_t i2 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+    if (i2 >= n) return;
+    const uint32_t p = bf16x2_rne(__uint_as_float((uint32_t)(first + i2)),
+                                  __uint_as_float((uint32_t)(first + i2 + 1)));
+    if (i2 + 2 <= n)
+        out[i2 >> 1] = p;
+    else
+        reinterpret_cast<uint16_t*>(out)[i2] = (uint16_t)p;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s,
@@ -447,6 +467,11 @@ hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt,
                           hipStream_t st) {
     if (fmt == 0) return launch(k_requant<0>, total_blocks, st, batch);
     return launch(k_requant<1>, total_blocks, st, batch);
+}
+
+hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st) {
+    const int64_t blocks = (n + 511) / 512;
+    return launch(k_bf16_bits, blocks, st, first, n, static_cast<uint32_t*>(out));
 }
 
 hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st) {

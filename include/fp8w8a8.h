@@ -187,6 +187,15 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const f
  */
 int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream);
 
+/*
+ * Diagnostic: the device bf16 rounding alone.  out[i] = bf16 bit pattern of
+ * the float with bit pattern first_bits + i, round to nearest even (the
+ * rounding of the RMSNorm output y and of every bf16 GEMM output), for
+ * 0 <= i < n (n <= 2^32 - first_bits).
+ *   out : uint16 [n] device memory, 16-byte aligned.
+ */
+int fp8_bf16_round_f32_bits(uint64_t first_bits, int64_t n, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

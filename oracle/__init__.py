@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.orc_bf16_to_f32.restype = ctypes.c_float
         L.orc_f32_to_bf16_rne.argtypes = [ctypes.c_float]
         L.orc_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.orc_bf16_rne_array.argtypes = [f32p, i64, u16p]
+        L.orc_bf16_rne_array.restype = None
         L.orc_scale_f32.argtypes = [ctypes.c_float]
         L.orc_scale_f32.restype = ctypes.c_float
         L.orc_e8m0_exponent.argtypes = [ctypes.c_float]
@@ -135,6 +137,14 @@ def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     out = np.empty(v.shape, np.uint8)
     lib().orc_e4m3_encode_array(_p(v, ctypes.c_float), v.size, _p(out, ctypes.c_uint8))
+    return out
+
+
+def bf16_rne_array(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) of the fp32 values v, round to nearest even."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_rne_array(_p(v, ctypes.c_float), v.size, _p(out, ctypes.c_uint16))
     return out
 
 

@@ -159,6 +159,12 @@ uint16_t orc_f32_to_bf16_rne(float f) {
     return (uint16_t)hi;
 }
 
+void orc_bf16_rne_array(const float* v, int64_t n, uint16_t* out) {
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) out[i] = orc_f32_to_bf16_rne(v[i]);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scales                                                                   */
 /* ------------------------------------------------------------------------ */

@@ -61,6 +61,7 @@ void orc_e4m3_encode_array(const float* v, int64_t n, uint8_t* out);
 /* ---- bf16 helpers ---- */
 float    orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16_rne(float f);
+void     orc_bf16_rne_array(const float* v, int64_t n, uint16_t* out);
 
 /* ---- scales ---- */
 

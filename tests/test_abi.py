@@ -38,7 +38,7 @@ def test_header_declares_the_calls():
     for required in ("fp8_quantize_block", "fp8_quantize_token", "fp8_rmsnorm_quant",
                      "fp8_requantize_weights", "fp8_gemm_a8w8_scaled",
                      "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
-                     "fp8_encode_f32_bits"):
+                     "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits"):
         assert required in names
 
 
@@ -132,6 +132,10 @@ def test_encode_validation(L):
     assert L.fp8_encode_f32_bits(1 << 32, 1, vp(FAKE), None) == ARG
     assert L.fp8_encode_f32_bits(0xFFFFFFFF, 2, vp(FAKE), None) == ARG
     assert L.fp8_encode_f32_bits(0, 16, vp(FAKE + 3), None) == ALIGN
+    assert L.fp8_bf16_round_f32_bits(1 << 32, 1, vp(FAKE), None) == ARG
+    assert L.fp8_bf16_round_f32_bits(0xFFFFFFFF, 2, vp(FAKE), None) == ARG
+    assert L.fp8_bf16_round_f32_bits(0, 16, vp(FAKE + 2), None) == ALIGN
+    assert L.fp8_bf16_round_f32_bits(0, 0, None, None) == OK
 
 
 def test_quotient_path_equals_ieee_division_exhaustively(tmp_path):

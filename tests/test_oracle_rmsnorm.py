@@ -69,6 +69,21 @@ def test_fixed_order_sum_within_fp32_bound_of_exact(K):
         assert abs(got - exact) <= (K - 1) * Fraction(1, 2 ** 24) * exact * Fraction(11, 10)
 
 
+def test_bf16_rne_array_matches_torch_conversion():
+    """The array form (used against the device rounding on all 2^32 patterns)
+    equals torch's fp32 -> bf16 conversion (round to nearest even) on every
+    1021st fp32 pattern, on exact ties and on subnormals; NaNs excluded."""
+    bits = np.arange(0, 1 << 32, 1021, dtype=np.uint64).astype(np.uint32)
+    ties = (np.arange(0, 1 << 16, dtype=np.uint32) << 16) | 0x8000
+    sub = np.arange(1, 1 << 23, 4099, dtype=np.uint32)
+    bits = np.concatenate([bits, ties, ties | 0x80000000, sub, sub | 0x80000000])
+    bits = bits[~(((bits & 0x7F800000) == 0x7F800000) & ((bits & 0x7FFFFF) != 0))]
+    v = bits.view(np.float32)
+    ref = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne_array(v)
+    assert np.array_equal(got, ref)
+
+
 def test_matches_torch_rms_norm_in_fp64_within_one_bf16_ulp():
     h, gamma = synth.rms_inputs(M=64, K=5120, seed=2)
     y = oracle.rmsnorm_bf16(h, gamma, 1e-6)
