@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.orc_e8m0_lossless.restype = ctypes.c_int
         L.orc_quantize_block.argtypes = [u16p, i64, i64, u8p, f32p]
         L.orc_quantize_block.restype = None
+        L.orc_quantize_block_e8m0.argtypes = [u16p, i64, i64, u8p, u8p]
+        L.orc_quantize_block_e8m0.restype = None
         L.orc_quantize_token.argtypes = [u16p, i64, i64, u8p, f32p]
         L.orc_quantize_token.restype = None
         L.orc_quantize_weight_block.argtypes = [u16p, i64, i64, ctypes.c_int, u8p,
@@ -194,6 +196,24 @@ def quantize_block(x):
     return q, s
 
 
+def quantize_block_e8m0(x):
+    """1x128 groups with E8M0 scale bytes ([vllm-54894] §1 format, §3 group
+    size 128): returns (codes uint8 [M, K], bytes uint8 [M, K/128])."""
+    xb = _bits16(x)
+    M, K = xb.shape
+    assert K % 128 == 0
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // 128), np.uint8)
+    lib().orc_quantize_block_e8m0(_p(xb, ctypes.c_uint16), M, K, _p(q, ctypes.c_uint8),
+                                  _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def e8m0_value(b: np.ndarray) -> np.ndarray:
+    """The power of two an E8M0 byte stands for, 2^(b - 127), as fp64 (exact)."""
+    return np.ldexp(1.0, np.asarray(b, dtype=np.int64) - 127)
+
+
 def quantize_token(x):
     """One scale per row (per-token activations, per-row weights)."""
     xb = _bits16(x)
@@ -282,6 +302,31 @@ def gemm(qa, qw, sa, sw, gran: int, rows=None) -> np.ndarray:
     A = dequant_act(qa, sa, gran)
     W = dequant_weight(qw, sw, gran)
     return A @ W.T
+
+
+def mx_gemm(qa, qw, sa8, sw8, rows=None) -> np.ndarray:
+    """Block-scaled GEMM with E8M0 scale bytes ([vllm-54894] §3
+    batched_gemm_a8w8_mxscale, one batch): activation bytes sa8 [M, K/128],
+    weight bytes sw8 [N/128, K/128]; each byte stands for 2^(b - 127), so this
+    is gemm() with those powers of two as the block scales.  fp64."""
+    return gemm(qa, qw, e8m0_value(sa8), e8m0_value(sw8), GRAN_BLOCK, rows=rows)
+
+
+def batched_mx_gemm(qa, qw, sa8, sw8, rows=None) -> np.ndarray:
+    """Batched form over groups b ([vllm-54894] §2 weight view (groups, out,
+    in), scales (groups, out/128, in/128)): A [M, B, K] with bytes [M, B, K/128],
+    W [B, N, K] with bytes [B, N/128, K/128]; Y[m, b, :] = mx_gemm of batch b.
+    Returns [len(rows) or M, B, N] fp64."""
+    M, B, K = qa.shape
+    N = qw.shape[1]
+    if rows is None:
+        rows = np.arange(M)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, B, N), np.float64)
+    for b in range(B):
+        out[:, b, :] = mx_gemm(np.ascontiguousarray(qa[rows, b, :]), qw[b],
+                               np.ascontiguousarray(sa8[rows, b, :]), sw8[b])
+    return out
 
 
 def grouped_gemm(qa, qw, sa, sw, offsets, rows=None) -> np.ndarray:

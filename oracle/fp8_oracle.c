@@ -244,6 +244,26 @@ void orc_quantize_block(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, flo
     }
 }
 
+/* 1x128 groups with E8M0 scales ([vllm-54894] §1 scale format, §3 group size
+ * 128): per group e = ceil(log2(amax / 448)) (amax / 448 the fp32 scale),
+ * clamped to [-127, 127]; byte e + 127; each element encoded from x / 2^e,
+ * an exact division. */
+void orc_quantize_block_e8m0(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s) {
+    int64_t G = K / 128, m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        int64_t g, k;
+        for (g = 0; g < G; ++g) {
+            const uint16_t* xg = x + m * K + g * 128;
+            int e = orc_e8m0_exponent(orc_scale_f32(group_amax(xg, 128, 0, 1)));
+            float p2 = ldexpf(1.0f, e); /* exact, subnormal for e = -127 */
+            s[m * G + g] = (uint8_t)(e + 127);
+            for (k = 0; k < 128; ++k)
+                q[m * K + g * 128 + k] = orc_e4m3_encode(orc_bf16_to_f32(xg[k]) / p2);
+        }
+    }
+}
+
 void orc_quantize_token(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s) {
     int64_t m;
 #pragma omp parallel for schedule(static)

@@ -125,3 +125,46 @@ def test_grouped_reduces_to_per_expert_dense():
     rows = np.array([0, 4, 11])
     Yr = oracle.grouped_gemm(qa, qw, sa, sw, offsets, rows=rows)
     assert np.allclose(Yr, Y[rows], rtol=0, atol=1e-13 * np.abs(Y).max())
+
+
+def test_mx_gemm_against_exact_rationals():
+    """E8M0 bytes stand for 2^(b - 127): exact rational sums on a tiny shape."""
+    rng = np.random.default_rng(77)
+    tab = oracle.decode_table()
+    M, N, K = 3, 256, 384
+    qa, qw = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    sa8 = rng.integers(110, 140, (M, K // 128)).astype(np.uint8)
+    sw8 = rng.integers(100, 135, (N // 128, K // 128)).astype(np.uint8)
+    Y = oracle.mx_gemm(qa, qw, sa8, sw8)
+    for m in range(M):
+        for n in (0, 5, 127, 128, 255):
+            ex = Fraction(0)
+            for k in range(K):
+                ex += (Fraction(tab[qa[m, k]]) * Fraction(2) ** (int(sa8[m, k // 128]) - 127) *
+                       Fraction(tab[qw[n, k]]) * Fraction(2) ** (int(sw8[n // 128, k // 128]) - 127))
+            assert abs(Fraction(Y[m, n]) - ex) <= abs(ex) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 200)
+
+
+def test_batched_mx_gemm_equals_block_diagonal_dense():
+    """Batch b of [M, B, K] x [B, N, K] -> [M, B, N] equals the dense product of
+    A laid out as [M, B*K] with a block-diagonal [B*N, B*K] weight (zero codes
+    off the diagonal)."""
+    rng = np.random.default_rng(78)
+    M, B, N, K = 5, 3, 128, 256
+    qa = _rand_codes(rng, (M, B, K))
+    qw = _rand_codes(rng, (B, N, K))
+    sa8 = rng.integers(115, 135, (M, B, K // 128)).astype(np.uint8)
+    sw8 = rng.integers(110, 130, (B, N // 128, K // 128)).astype(np.uint8)
+    Y = oracle.batched_mx_gemm(qa, qw, sa8, sw8)
+    A = qa.reshape(M, B * K)
+    SA = sa8.reshape(M, B * K // 128)
+    W = np.zeros((B * N, B * K), np.uint8)
+    SW = np.full((B * N // 128, B * K // 128), 127, np.uint8)
+    for b in range(B):
+        W[b * N:(b + 1) * N, b * K:(b + 1) * K] = qw[b]
+        SW[b * N // 128:(b + 1) * N // 128, b * K // 128:(b + 1) * K // 128] = sw8[b]
+    D = oracle.mx_gemm(A, W, SA, SW).reshape(M, B, N)
+    assert np.allclose(Y, D, rtol=1e-12, atol=0.0)
+    Y1 = oracle.batched_mx_gemm(qa[:, 1:2], qw[1:2], sa8[:, 1:2], sw8[1:2])
+    assert np.array_equal(Y1[:, 0], oracle.mx_gemm(np.ascontiguousarray(qa[:, 1]), qw[1],
+                                                    np.ascontiguousarray(sa8[:, 1]), sw8[1]))

@@ -215,3 +215,54 @@ def test_e8m0_weight_quant_bytes_and_lossless():
             for k in range(0, 128, 13):
                 v = blk[r, k] / sc
                 assert q[128 * i + r, 128 * j + k] == nearest_e4m3_exhaustive(v, tab)
+
+
+# ------------------------------------------------------- E8M0 1x128 groups --
+def test_e8m0_block_codes_match_exact_arithmetic():
+    """Byte = ceil(log2(s)) + 127 of the correctly rounded fp32 scale s, found
+    with exact rationals; codes = the exhaustive-search nearest E4M3 value of
+    the exact quotient x / 2^e."""
+    tab = oracle.decode_table()
+    xb = _random_groups(23, M=6, K=256)
+    q, s8 = oracle.quantize_block_e8m0(xb)
+    xf = _f32(xb)
+    for m in range(xb.shape[0]):
+        for g in range(2):
+            grp = xf[m, 128 * g:128 * g + 128]
+            s_exact = Fraction(frac_to_f32(Fraction(float(np.abs(grp).max())) / 448))
+            e = -127
+            while e < 127 and Fraction(2) ** e < s_exact:
+                e += 1
+            assert s8[m, g] == e + 127, (m, g)
+            for k in range(0, 128, 3):
+                v = frac_to_f32(Fraction(float(grp[k])) / Fraction(2) ** e)
+                assert q[m, 128 * g + k] == nearest_e4m3_exhaustive(v, tab), (m, g, k)
+
+
+def test_e8m0_block_equals_weight_block_of_repeated_rows():
+    """A 1x128 group quantizes like a 128x128 block whose 128 rows are copies
+    of it (same amax, so the same byte and the same codes)."""
+    xb = _random_groups(29, M=5, K=256)
+    q, s8 = oracle.quantize_block_e8m0(xb)
+    for m in range(xb.shape[0]):
+        w = np.ascontiguousarray(np.repeat(xb[m:m + 1], 128, axis=0))
+        qw, sw = oracle.quantize_weight_block(w, fmt=1)
+        assert np.array_equal(sw[0], s8[m])
+        assert np.all(qw == q[m][None, :])
+
+
+def test_e8m0_block_zero_group_and_lossless_bytes():
+    x = np.zeros((3, 256), np.float32)
+    x[0, 128:] = -0.0
+    x[1, :] = np.float32(2.0 ** -133)   # bf16 subnormal: byte 0 territory
+    x[2, :128] = 1000.0
+    x[2, 3] = -1000.0
+    q, s8 = oracle.quantize_block_e8m0(_bits(x))
+    assert s8[0, 0] == 0 and s8[0, 1] == 0          # e = -127 for amax 0
+    assert np.all(q[0, :128] == 0x00) and np.all(q[0, 128:] == 0x80)
+    assert s8[2, 0] == 2 + 127                      # s = 1000 / 448 ~ 2.23: 2^1 < s <= 2^2
+    assert q[2, 0] == oracle.e4m3_encode(250.0) and q[2, 3] == oracle.e4m3_encode(-250.0)
+    assert q[2, 0] == 0x78  # 250 lies nearer 256 than 240
+    p2 = np.ldexp(np.float32(1.0), s8.astype(np.int32) - 127).astype(np.float32)
+    codes = oracle.e8m0_lossless(p2)
+    assert codes is not None and np.array_equal(codes.reshape(s8.shape), s8)
