@@ -71,7 +71,9 @@ def load_library() -> ctypes.CDLL:
         "fp8_abi_version": ([], i32),
         "fp8_status_string": ([i32], ctypes.c_char_p),
         "fp8_quantize_block": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_quantize_block_e8m0": ([vp, i64, i64, vp, vp, vp], i32),
         "fp8_quantize_token": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_batched_gemm_a8w8_mxscale": ([vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
         "fp8_rmsnorm_quant": ([vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
@@ -139,6 +141,23 @@ def quantize_block(x: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tenso
                         device=x.device)
     L = load_library()
     _check("fp8_quantize_block", L.fp8_quantize_block(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
+    return q, s
+
+
+def quantize_block_e8m0(x: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (E4M3 bytes uint8 [M, K], E8M0 scale bytes uint8 [M, K/128]).
+    ``out`` may supply the (q, s) buffers."""
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    if out is not None:
+        q, s = _as_u8(out[0]), _as_u8(out[1])
+    else:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 128 if K % 128 == 0 else 0), dtype=torch.uint8,
+                        device=x.device)
+    L = load_library()
+    _check("fp8_quantize_block_e8m0",
+           L.fp8_quantize_block_e8m0(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x)))
     return q, s
 
 
@@ -224,6 +243,39 @@ def gemm_a8w8_scaled(a: Tuple[torch.Tensor, torch.Tensor], w: Tuple[torch.Tensor
     _check("fp8_gemm_a8w8_scaled",
            L.fp8_gemm_a8w8_scaled(_ptr(qa), _ptr(qw), _ptr(sa), _ptr(sw), None, _ptr(y), M, N, K,
                                   gran, _stream(qa)))
+    return y
+
+
+def batched_gemm_a8w8_mxscale(a: Tuple[torch.Tensor, torch.Tensor],
+                              w: Tuple[torch.Tensor, torch.Tensor],
+                              out: torch.Tensor = None) -> torch.Tensor:
+    """E8M0-scaled GEMM.  Batched: a = (E4M3 [M, B, K], bytes [M, B, K/128]),
+    w = (E4M3 [B, N, K], bytes [B, N/128, K/128]) -> bf16 [M, B, N].  Dense:
+    a = ([M, K], [M, K/128]), w = ([N, K], [N/128, K/128]) -> [M, N]."""
+    qa, sa = _as_u8(a[0]), _as_u8(a[1])
+    qw, sw = _as_u8(w[0]), _as_u8(w[1])
+    dense = qa.dim() == 2
+    if dense:
+        _need(qa, torch.uint8, 2, "a")
+        _need(qw, torch.uint8, 2, "w")
+        M, K = qa.shape
+        B, N = 1, qw.shape[0]
+        shape = (M, N)
+    else:
+        _need(qa, torch.uint8, 3, "a")
+        _need(qw, torch.uint8, 3, "w")
+        M, B, K = qa.shape
+        N = qw.shape[1]
+        if qw.shape[0] != B:
+            raise ValueError("a and w disagree on the batch count")
+        shape = (M, B, N)
+    if qw.shape[-1] != K:
+        raise ValueError("a and w disagree on K")
+    y = out if out is not None else torch.empty(shape, dtype=torch.bfloat16, device=qa.device)
+    L = load_library()
+    _check("fp8_batched_gemm_a8w8_mxscale",
+           L.fp8_batched_gemm_a8w8_mxscale(_ptr(qa), _ptr(qw), _ptr(sa), _ptr(sw), _ptr(y), B, M,
+                                           N, K, _stream(qa)))
     return y
 
 

@@ -73,7 +73,18 @@ int fp8_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s, v
     if (!x || !q || !s) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
     if (int st = device_check()) return st;
-    return launched(fp8k::launch_quantize_block(x, M, K, q, s, as_stream(stream)));
+    return launched(fp8k::launch_quantize_block(x, M, K, q, s, 0, as_stream(stream)));
+}
+
+int fp8_quantize_block_e8m0(const void* x, int64_t M, int64_t K, void* q, void* s,
+                            void* stream) {
+    if (M < 0 || K <= 0) return K <= 0 ? FP8_ERR_SHAPE : FP8_ERR_ARG;
+    if (K % 128 != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!x || !q || !s) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_quantize_block(x, M, K, q, s, 1, as_stream(stream)));
 }
 
 int fp8_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s, void* stream) {
@@ -170,6 +181,24 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
     if (int st = device_check()) return st;
     return launched(fp8k::launch_grouped_gemm(a, w, a_s, w_s, offsets, y, T, E, N, K,
                                               as_stream(stream)));
+}
+
+int fp8_batched_gemm_a8w8_mxscale(const void* a, const void* w, const void* a_s, const void* w_s,
+                                  void* y, int64_t B, int64_t M, int64_t N, int64_t K,
+                                  void* stream) {
+    if (M < 0 || B < 0) return FP8_ERR_ARG;
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (M == 0 || B == 0) return FP8_OK;
+    // 32-bit tile offsets: 256 rows of B * K bytes; tile and step counts in int
+    if (B * K > (int64_t(1) << 22)) return FP8_ERR_SHAPE;
+    const int64_t tiles = B * ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles > INT32_MAX || (tiles / 256 + 1) * (K / 128) > INT32_MAX) return FP8_ERR_SHAPE;
+    if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_batched_gemm_mx(a, w, static_cast<const uint8_t*>(a_s),
+                                                 static_cast<const uint8_t*>(w_s), y, B, M, N, K,
+                                                 as_stream(stream)));
 }
 
 int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream) {

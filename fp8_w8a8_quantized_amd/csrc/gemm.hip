@@ -48,7 +48,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;  // K step: one scale block
-constexpr int GRAN_BLOCK = 0, GRAN_ROW = 1;
+constexpr int GRAN_BLOCK = 0, GRAN_ROW = 1, GRAN_MX = 2;  // MX: E8M0 block scales
 
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
     // cbsz = blgp = 0: both operands E4M3; scale operands 0 -> unscaled form
@@ -129,9 +129,19 @@ __device__ __forceinline__ void b2l(__amdgpu_buffer_rsrc_t r, uint8_t* l, int si
                                     int soff) {
     if (size == 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
-    else
+    else if (size == 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 4, voff, soff, 0, 0);
+    else  // one byte, written zero-extended as the lane's 32-bit word
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 1, voff, soff, 0, 0);
 }
+
+// Shape of a large-M GEMM: B batches of A [M, B, K] x W [B, N, K] -> Y [M, B,
+// N]; batch b of A is every B-th K-row (the token-major layout of the page's
+// batched MX GEMM).  B = 1 is the dense GEMM (A [M, K], Y [M, N]).
+struct BigGeom {
+    int64_t M, N, K;
+    int B;
+};
 
 // Per-tile load sources of the large-M kernel: buffer resources over the
 // tile's A rows, W rows and scales, and each lane's loop-invariant offsets.
@@ -141,28 +151,74 @@ struct BigSrc {
     int offsa, offsw;      // byte offsets of this lane's scale at kb = 0
 };
 
+// Tile coordinates of logical tile `logical`: batch-major; inside a batch,
+// bands of 4 row tiles, column-major inside a band, so consecutive logical
+// tiles share A rows and W columns.  The last column tile may hold 128 valid
+// columns (N % 256 == 128).
+struct BigTile {
+    int b, tm, tn, rows, cols;
+};
+
+__device__ __forceinline__ BigTile big_tile(int logical, int tm_count, int tn_count,
+                                            const BigGeom& G) {
+    constexpr int GROUP = 4;
+    BigTile t;
+    const int per_batch = tm_count * tn_count;
+    t.b = logical / per_batch;
+    logical -= t.b * per_batch;
+    const int band = logical / (GROUP * tn_count);
+    const int first_m = band * GROUP;
+    const int band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
+    const int in_band = logical - band * GROUP * tn_count;
+    t.tm = first_m + in_band % band_m;
+    t.tn = in_band / band_m;
+    const int64_t left = G.M - (int64_t)t.tm * BM2, cleft = G.N - (int64_t)t.tn * BN2;
+    t.rows = left < BM2 ? (int)left : BM2;
+    t.cols = cleft < BN2 ? (int)cleft : BN2;
+    return t;
+}
+
+// Load sources of tile t.  Rows past M (and columns past N) read the last
+// valid row (column): their results are never stored.
 template <int GRAN>
-__device__ __forceinline__ BigSrc big_src(const uint8_t* A, const uint8_t* W, const float* sA,
-                                          const float* sW, int rows, int K, int KB, int wave,
-                                          int lane) {
+__device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* A, const uint8_t* W,
+                                               const void* sA, const void* sW, const BigGeom& G,
+                                               int wave, int lane) {
+    const int K = (int)G.K, KB = K / BK, B = G.B;
+    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const int lda = B * K;  // bytes between consecutive rows of one batch of A
     BigSrc S;
-    S.a = buffer_rsrc(A, rows * K);
-    S.w = buffer_rsrc(W, BN2 * K);
+    S.a = buffer_rsrc(A + (row0 * B + t.b) * (int64_t)K, (t.rows - 1) * lda + K);
+    S.w = buffer_rsrc(W + ((int64_t)t.b * G.N + n0) * K, t.cols * K);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = (i * 8 + wave) * 64 + lane;  // LDS chunk this lane fills
         const int r = p >> 3;
         const int c = swz_pos(r, p & 7);           // the tile chunk whose LDS slot is p
-        const int ra = r < rows ? r : rows - 1;
-        S.offa[i] = ra * K + c * 16;
-        S.offw[i] = r * K + c * 16;
+        const int ra = r < t.rows ? r : t.rows - 1;
+        const int rw = r < t.cols ? r : t.cols - 1;
+        S.offa[i] = ra * lda + c * 16;
+        S.offw[i] = rw * K + c * 16;
     }
-    if constexpr (GRAN == GRAN_BLOCK) {
-        S.sa = buffer_rsrc(sA, rows * KB * 4);
-        S.sw = buffer_rsrc(sW, 2 * KB * 4);
-        const int r = (wave & 3) * 64 + lane;
-        S.offsa = (r < rows ? r : rows - 1) * KB * 4;
-        S.offsw = (lane & 1) * KB * 4;  // lane l: weight block l & 1 of the tile
+    const int r = (wave & 3) * 64 + lane;
+    const int rr = r < t.rows ? r : t.rows - 1;
+    const int nb = t.cols / BK;                              // weight blocks in the tile
+    const int wbl = (lane & 1) < nb ? (lane & 1) : nb - 1;  // lane l: weight block l & 1
+    if constexpr (GRAN == GRAN_BLOCK) {  // fp32 scales (B == 1)
+        const float* sa = static_cast<const float*>(sA) + row0 * KB;
+        const float* sw = static_cast<const float*>(sW) + (n0 / BK) * KB;
+        S.sa = buffer_rsrc(sa, t.rows * KB * 4);
+        S.sw = buffer_rsrc(sw, nb * KB * 4);
+        S.offsa = rr * KB * 4;
+        S.offsw = wbl * KB * 4;
+    } else if constexpr (GRAN == GRAN_MX) {  // E8M0 bytes [M, B, KB] and [B, N/128, KB]
+        const uint8_t* sa = static_cast<const uint8_t*>(sA) + (row0 * B + t.b) * KB;
+        const uint8_t* sw =
+            static_cast<const uint8_t*>(sW) + ((int64_t)t.b * (G.N / BK) + n0 / BK) * KB;
+        S.sa = buffer_rsrc(sa, (t.rows - 1) * B * KB + KB);
+        S.sw = buffer_rsrc(sw, nb * KB);
+        S.offsa = rr * B * KB;
+        S.offsw = wbl * KB;
     } else {
         S.sa = S.sw = S.a;
         S.offsa = S.offsw = 0;
@@ -171,7 +227,8 @@ __device__ __forceinline__ BigSrc big_src(const uint8_t* A, const uint8_t* W, co
 }
 
 // Stage K block kb of the A and W tiles (and, for block scales, the A and W
-// scales of kb) into LDS stage st.
+// scales of kb) into LDS stage st.  Scales land one 32-bit word per row (an
+// E8M0 byte zero-extended) and one word per weight block.
 template <int GRAN>
 __device__ __forceinline__ void stage_big(uint8_t* lds, int st, const BigSrc& S, int kb, int wave) {
     uint8_t* la = lds + st * kStage2;
@@ -182,49 +239,21 @@ __device__ __forceinline__ void stage_big(uint8_t* lds, int st, const BigSrc& S,
         b2l(S.a, la + pbase * 16, 16, S.offa[i], kb * BK);
         b2l(S.w, lb + pbase * 16, 16, S.offw[i], kb * BK);
     }
-    if constexpr (GRAN == GRAN_BLOCK) {
+    if constexpr (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) {
+        constexpr int size = GRAN == GRAN_BLOCK ? 4 : 1;
         if (wave < 4)
-            b2l(S.sa, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256, 4, S.offsa, kb * 4);
+            b2l(S.sa, lds + 2 * kStage2 + st * BM2 * 4 + wave * 256, size, S.offsa, kb * size);
         else if (wave == 4)
-            b2l(S.sw, lds + kSw2 + st * 256, 4, S.offsw, kb * 4);
+            b2l(S.sw, lds + kSw2 + st * 256, size, S.offsw, kb * size);
     }
 }
 
+// The MFMA fragment of tile row r for lane group lk: K bytes 32 lk .. +31, the
+// two 16-byte chunks 2 lk and 2 lk + 1 of the (swizzled) row.
 __device__ __forceinline__ v8i frag(const uint8_t* base, int r, int lk) {
     const v4i lo = *reinterpret_cast<const v4i*>(base + swz(r, 2 * lk));
     const v4i hi = *reinterpret_cast<const v4i*>(base + swz(r, 2 * lk + 1));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Tile coordinates of logical tile `logical` of the large-M kernel: bands of
-// 4 row tiles, column-major inside a band, so consecutive logical tiles share
-// A rows and W columns.
-struct BigTile {
-    int tm, tn, rows;
-};
-
-__device__ __forceinline__ BigTile big_tile(int logical, int tm_count, int tn_count, int64_t M) {
-    constexpr int GROUP = 4;
-    const int band = logical / (GROUP * tn_count);
-    const int first_m = band * GROUP;
-    const int band_m = (tm_count - first_m) < GROUP ? (tm_count - first_m) : GROUP;
-    const int in_band = logical - band * GROUP * tn_count;
-    BigTile t;
-    t.tm = first_m + in_band % band_m;
-    t.tn = in_band / band_m;
-    const int64_t left = M - (int64_t)t.tm * BM2;
-    t.rows = left < BM2 ? (int)left : BM2;
-    return t;
-}
-
-template <int GRAN>
-__device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* A, const uint8_t* W,
-                                               const float* sA, const float* sW, int64_t K, int KB,
-                                               int wave, int lane) {
-    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
-    const float* sAt = GRAN == GRAN_BLOCK ? sA + row0 * KB : sA + row0;
-    const float* sWt = GRAN == GRAN_BLOCK ? sW + (n0 / BK) * KB : sW + n0;
-    return big_src<GRAN>(A + row0 * K, W + n0 * K, sAt, sWt, t.rows, (int)K, KB, wave, lane);
 }
 
 // A K block runs in two parts.  Column steps 6 and 7 of each K block are
@@ -233,14 +262,25 @@ __device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* 
 // head runs them X-fragment by X-fragment, so each X register is free after
 // its second MFMA and the next block's fragment is read into it right away:
 // the matrix core stays busy while the next block's X fragments arrive from
-// LDS.  The body then runs column steps 0..5.  Promotions run one MFMA behind
-// their product throughout, so the last product of a part is promoted at the
-// start of the next one.
+// LDS.  The body then runs column steps 0..5.  Promotions (BLOCK) run one
+// MFMA behind their product throughout, so the last product of a part is
+// promoted at the start of the next one.
 struct BigCarry {
     v8i w6, w7;  // W fragments of column steps 6 and 7 of the previous K block
     float sc[4]; // the previous block's promotion scales (BLOCK)
-    v4f p;       // last product not yet promoted
+    v4f p;       // last product not yet promoted (BLOCK)
     float psc;   // its scale
+    int sa[4];   // the previous block's E8M0 row scales (MX)
+    int sw;      // and its E8M0 weight-block scale
+};
+
+// The scales of the current K block: BLOCK uses sc (sA * sW per X
+// fragment), MX the E8M0 words sa (per X fragment) and sw (the wave's weight
+// block).
+struct BigScales {
+    float sc[4];
+    int sa[4];
+    int sw;
 };
 
 // sched_group_barrier masks
@@ -251,13 +291,20 @@ __device__ __forceinline__ void promote(v4f& acc, const v4f& p, float s) {
     for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(p[e], s, acc[e]);
 }
 
+// MX-scaled MFMA: W fragment (operand A) scaled by 2^(sw - 127), X fragment
+// (operand B) by 2^(sa - 127); every lane of a row or column gives the same
+// byte, so the scale covers the whole 128-wide K block.
+__device__ __forceinline__ v4f mfma_mx(const v8i& w, const v8i& x, const v4f& c, int sw, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, 0, 0, 0, sw, 0, sa);
+}
+
 // Head of K block `cur`: the previous block's deferred steps 6 and 7, and
 // this block's scales, first W fragment (returned in w0) and X fragments.
-// c.p enters as the previous block's product of tile (3, 5) and leaves as its
-// product of tile (3, 7).
+// BLOCK: c.p enters as the previous block's product of tile (3, 5) and leaves
+// as its product of tile (3, 7).
 template <int GRAN>
 __device__ __forceinline__ void big_head(const uint8_t* lds, int cur, v4f (&acc)[4][8],
-                                         v8i (&x)[4], v8i& w0, float (&sc)[4], BigCarry& c,
+                                         v8i (&x)[4], v8i& w0, BigScales& bs, BigCarry& c,
                                          int wm, int wn, int lr, int lk) {
     const uint8_t* la = lds + cur * kStage2;
     const uint8_t* lb = la + BM2 * BK;
@@ -299,31 +346,40 @@ __device__ __forceinline__ void big_head(const uint8_t* lds, int cur, v4f (&acc)
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = sa4[i] * sw;
+        for (int i = 0; i < 4; ++i) bs.sc[i] = sa4[i] * sw;
     } else {
-        w0 = frag(lb, wn * 128 + lr, lk);
+        if constexpr (GRAN == GRAN_MX) {
+            const int* lsa = reinterpret_cast<const int*>(lds + 2 * kStage2 + cur * BM2 * 4);
+            bs.sw = reinterpret_cast<const int*>(lds + kSw2 + cur * 256)[wn];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i][6] = mfma_f8(c.w6, x[i], acc[i][6]);
-            acc[i][7] = mfma_f8(c.w7, x[i], acc[i][7]);
-            x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
+            for (int i = 0; i < 4; ++i) bs.sa[i] = lsa[wm * 64 + i * 16 + lr];
         }
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        w0 = frag(lb, wn * 128 + lr, lk);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if constexpr (GRAN == GRAN_MX) {
+                acc[i][6] = mfma_mx(c.w6, x[i], acc[i][6], c.sw, c.sa[i]);
+                acc[i][7] = mfma_mx(c.w7, x[i], acc[i][7], c.sw, c.sa[i]);
+            } else {
+                acc[i][6] = mfma_f8(c.w6, x[i], acc[i][6]);
+                acc[i][7] = mfma_f8(c.w7, x[i], acc[i][7]);
+            }
+            x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
             __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
             __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Body of K block `cur`: column steps 0..5; steps 6 and 7's W fragments go to
-// c.w6 and c.w7.  c.p enters as the previous block's product of tile (3, 7)
-// and leaves as this block's product of tile (3, 5).
+// c.w6 and c.w7, this block's scales to the carry.  BLOCK: c.p enters as the
+// previous block's product of tile (3, 7) and leaves as this block's product
+// of tile (3, 5).
 template <int GRAN>
 __device__ __forceinline__ void big_body(const uint8_t* lds, int cur, v4f (&acc)[4][8],
-                                         const v8i (&x)[4], v8i w0, const float (&sc)[4],
+                                         const v8i (&x)[4], v8i w0, const BigScales& bs,
                                          BigCarry& c, int wn, int lr, int lk) {
     const uint8_t* lb = lds + cur * kStage2 + BM2 * BK;
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -339,9 +395,11 @@ __device__ __forceinline__ void big_body(const uint8_t* lds, int cur, v4f (&acc)
                 const v4f p = mfma_f8(wcur, x[i], zero);
                 promote(acc[pi][pj], c.p, c.psc);
                 c.p = p;
-                c.psc = sc[i];
+                c.psc = bs.sc[i];
                 pi = i;
                 pj = j;
+            } else if constexpr (GRAN == GRAN_MX) {
+                acc[i][j] = mfma_mx(wcur, x[i], acc[i][j], bs.sw, bs.sa[i]);
             } else {
                 acc[i][j] = mfma_f8(wcur, x[i], acc[i][j]);
             }
@@ -362,10 +420,12 @@ __device__ __forceinline__ void big_body(const uint8_t* lds, int cur, v4f (&acc)
         __builtin_amdgcn_sched_barrier(0);
     }
     c.w6 = wcur;
-    if constexpr (GRAN == GRAN_BLOCK) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c.sc[i] = sc[i];
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (GRAN == GRAN_BLOCK) c.sc[i] = bs.sc[i];
+        if constexpr (GRAN == GRAN_MX) c.sa[i] = bs.sa[i];
     }
+    if constexpr (GRAN == GRAN_MX) c.sw = bs.sw;
 }
 
 // The last block's deferred steps 6 and 7 (no next block to read).
@@ -382,44 +442,55 @@ __device__ __forceinline__ void big_tail(v4f (&acc)[4][8], const v8i (&x)[4], Bi
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[i][6] = mfma_f8(c.w6, x[i], acc[i][6]);
-            acc[i][7] = mfma_f8(c.w7, x[i], acc[i][7]);
+            if constexpr (GRAN == GRAN_MX) {
+                acc[i][6] = mfma_mx(c.w6, x[i], acc[i][6], c.sw, c.sa[i]);
+                acc[i][7] = mfma_mx(c.w7, x[i], acc[i][7], c.sw, c.sa[i]);
+            } else {
+                acc[i][6] = mfma_f8(c.w6, x[i], acc[i][6]);
+                acc[i][7] = mfma_f8(c.w7, x[i], acc[i][7]);
+            }
         }
     }
 }
 
 // Store a wave's 64 x 128 block of tile t (bf16, 8 bytes per lane and column
-// tile) and clear the accumulators for the next tile.
+// tile) and clear the accumulators for the next tile.  ROW applies the per-row
+// and per-column fp32 scales here (B == 1).
 template <int GRAN>
 __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
-                                          const float* sA, const float* sW, int64_t N, int wm,
-                                          int wn, int lr, int lk) {
+                                          const void* sA, const void* sW, const BigGeom& G,
+                                          int wm, int wn, int lr, int lk) {
     const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const int64_t ldy = (int64_t)G.B * G.N;
+    if (wn * 128 < t.cols) {  // the wave's 128 columns exist
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + lr;
-        if (r < t.rows) {
-            float sa = 1.0f;
-            if constexpr (GRAN == GRAN_ROW) sa = sA[row0 + r];
-            uint16_t* yrow = Y + (row0 + r) * N + n0 + wn * 128 + 4 * lk;
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 64 + i * 16 + lr;
+            if (r < t.rows) {
+                float sa = 1.0f;
+                if constexpr (GRAN == GRAN_ROW) sa = static_cast<const float*>(sA)[row0 + r];
+                uint16_t* yrow = Y + (row0 + r) * ldy + (int64_t)t.b * G.N + n0 + wn * 128 + 4 * lk;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                v4f v = acc[i][j];
-                if constexpr (GRAN == GRAN_ROW) {
-                    const v4f s4 =
-                        *reinterpret_cast<const v4f*>(sW + n0 + wn * 128 + j * 16 + 4 * lk);
+                for (int j = 0; j < 8; ++j) {
+                    v4f v = acc[i][j];
+                    if constexpr (GRAN == GRAN_ROW) {
+                        const v4f s4 = *reinterpret_cast<const v4f*>(
+                            static_cast<const float*>(sW) + n0 + wn * 128 + j * 16 + 4 * lk);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+                        for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+                    }
+                    uint2 o;
+                    o.x = bf16x2_rne(v[0], v[1]);
+                    o.y = bf16x2_rne(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(yrow + j * 16) = o;
                 }
-                uint2 o;
-                o.x = bf16x2_rne(v[0], v[1]);
-                o.y = bf16x2_rne(v[2], v[3]);
-                *reinterpret_cast<uint2*>(yrow + j * 16) = o;
             }
         }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
 }
 
 // Persistent: workgroup b runs on XCD b % 8; the XCD's workgroups share a
@@ -430,14 +501,13 @@ __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, ui
 template <int GRAN>
 __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ W,
-                                                        const float* __restrict__ sA,
-                                                        const float* __restrict__ sW,
-                                                        uint16_t* __restrict__ Y, int64_t M,
-                                                        int64_t N, int64_t K) {
+                                                        const void* __restrict__ sA,
+                                                        const void* __restrict__ sW,
+                                                        uint16_t* __restrict__ Y, BigGeom G) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
-    const int tm_count = (int)((M + BM2 - 1) / BM2), tn_count = (int)(N / BN2);
-    const int T = tm_count * tn_count;
-    const int KB = (int)(K / BK);
+    const int tm_count = (int)((G.M + BM2 - 1) / BM2), tn_count = (int)((G.N + BN2 - 1) / BN2);
+    const int T = G.B * tm_count * tn_count;
+    const int KB = (int)(G.K / BK);
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int nwg = ((int)gridDim.x - xcd + 7) >> 3;  // workgroups on this XCD
     const int q = T >> 3, rem = T & 7;
@@ -458,22 +528,24 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     // The wave's X fragments of the current K block, and what a block hands
-    // to the next (all zero at the start, so the first head's deferred step
-    // adds exact zeros).
+    // to the next (zero operands at the start, so the first head's deferred
+    // steps add exact zeros).
     v8i x[4];
     BigCarry c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         x[i] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         c.sc[i] = 0.0f;
+        c.sa[i] = 127;
     }
+    c.sw = 127;
     c.w6 = c.w7 = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     c.p = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     c.psc = 0.0f;
 
     int lt = 0, lkb = 0;  // load cursor: tile, K block
-    BigSrc S = big_tile_src<GRAN>(big_tile(first, tm_count, tn_count, M), A, W, sA, sW, K, KB,
-                                  wave, lane);
+    BigSrc S = big_tile_src<GRAN>(big_tile(first, tm_count, tn_count, G), A, W, sA, sW, G, wave,
+                                  lane);
     stage_big<GRAN>(lds, 0, S, 0, wave);
     // Materialize the output pointer now: a scalar load still in flight
     // during the loop would turn every LDS wait into lgkmcnt(0).
@@ -489,31 +561,31 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
             if (++lkb == KB) {
                 lkb = 0;
                 ++lt;
-                S = big_tile_src<GRAN>(big_tile(first + lt * nwg, tm_count, tn_count, M), A, W,
-                                       sA, sW, K, KB, wave, lane);
+                S = big_tile_src<GRAN>(big_tile(first + lt * nwg, tm_count, tn_count, G), A, W,
+                                       sA, sW, G, wave, lane);
             }
             stage_big<GRAN>(lds, cur ^ 1, S, lkb, wave);
         }
         v8i w0;
-        float sc[4];
-        big_head<GRAN>(lds, cur, acc, x, w0, sc, c, wm, wn, lr, lk);
+        BigScales bs;
+        big_head<GRAN>(lds, cur, acc, x, w0, bs, c, wm, wn, lr, lk);
         if (ckb == 0 && g > 0) {
             // the head finished the previous tile's last block: store it
             if constexpr (GRAN == GRAN_BLOCK) {
                 promote(acc[3][7], c.p, c.psc);
                 c.p = v4f{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, M), Y, sA,
-                            sW, N, wm, wn, lr, lk);
+            big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, G), Y, sA,
+                            sW, G, wm, wn, lr, lk);
         }
-        big_body<GRAN>(lds, cur, acc, x, w0, sc, c, wn, lr, lk);
+        big_body<GRAN>(lds, cur, acc, x, w0, bs, c, wn, lr, lk);
         if (++ckb == KB) {
             ckb = 0;
             ++ct;
         }
     }
     big_tail<GRAN>(acc, x, c);
-    big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, M), Y, sA, sW, N,
+    big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, G), Y, sA, sW, G,
                     wm, wn, lr, lk);
 }
 
@@ -849,12 +921,15 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     if (M >= 1024 && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
         (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
         const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
+        const BigGeom G{M, N, K, 1};
         if (gran == GRAN_BLOCK)
             hipLaunchKernelGGL(k_gemm_big<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
-                               a_s, w_s, Yp, M, N, K);
+                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
+                               G);
         else
             hipLaunchKernelGGL(k_gemm_big<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
-                               a_s, w_s, Yp, M, N, K);
+                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
+                               G);
         return hipGetLastError();
     }
     TileSpace S{};
@@ -885,6 +960,20 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
     S.M = T; S.N = N; S.K = K; S.E = E;
     hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
                        dim3(kThreadsP), 0, st, S, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a_s,
+                                  const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
+                                  int64_t K, hipStream_t st) {
+    if (M == 0 || B == 0) return hipSuccess;
+    const int64_t tiles = B * ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
+    const unsigned grid = (unsigned)(tiles < 256 ? tiles : 256);  // one per CU
+    const BigGeom G{M, N, K, (int)B};
+    hipLaunchKernelGGL(k_gemm_big<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
+                       static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
+                       static_cast<const void*>(a_s), static_cast<const void*>(w_s),
+                       static_cast<uint16_t*>(y), G);
     return hipGetLastError();
 }
 

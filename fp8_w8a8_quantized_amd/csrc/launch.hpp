@@ -25,13 +25,18 @@ struct ReqBatch {
     int32_t pad;
 };
 
-hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s,
+hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, void* s, int fmt,
                                  hipStream_t st);
 hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s,
                                  hipStream_t st);
 hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps,
                                 int64_t M, int64_t K, int group_size, hipStream_t st);
 hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, hipStream_t st);
+// B batches: A [M, B, K], W [B, N, K], E8M0 scales [M, B, K/128] and
+// [B, N/128, K/128], Y [M, B, N].  Requires B * K <= 2^22 and int tile counts.
+hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a_s,
+                                  const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
+                                  int64_t K, hipStream_t st);
 hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st);
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 

@@ -65,16 +65,37 @@ __device__ __forceinline__ uint2 encode8(const float (&f)[8], const GroupDiv& g)
     return e4m3x8(t);
 }
 
+// E8M0 exponent of an fp32 scale: ceil(log2 s) from its bits, clamped to
+// [-127, 127] (-127 for s == 0).
+__device__ __forceinline__ int e8m0_exponent(float s) {
+    const uint32_t u = __float_as_uint(s) & 0x7FFFFFFFu;
+    int e;
+    if (u == 0) return -127;
+    const int eb = (int)(u >> 23);
+    const uint32_t m = u & 0x7FFFFFu;
+    if (eb == 0)  // subnormal: s = m * 2^-149; ceil(log2 m) - 149
+        e = (m == 1u ? 0 : 32 - __clz((int)(m - 1u))) - 149;
+    else
+        e = eb - 127 + (m != 0u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^-e as a float for the exponents bf16 data can produce (e <= 120, so
+// 127 - e >= 7 and 2^-e is a normal number): x * 2^-e == x / 2^e exactly.
+__device__ __forceinline__ float e8m0_inv(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
 // ---------------------------------------------------------------------------
 // 1x128 groups.  The M x K/128 groups are contiguous 256-byte runs in memory,
 // so the kernel treats x as a flat array of groups: a wave covers 4 groups
 // (16 lanes x 16 bytes each) per step and takes U steps, all loads issued
 // before any compute.
 // ---------------------------------------------------------------------------
-template <int U>
+// FMT 0: fp32 scale amax / 448; FMT 1: E8M0 byte e + 127, e the ceiling
+// exponent of that scale, elements encoded from x * 2^-e.
+template <int U, int FMT>
 __global__ __launch_bounds__(256) void k_quant_block(const uint4* __restrict__ x,
                                                      uint2* __restrict__ q,
-                                                     float* __restrict__ s, int64_t G) {
+                                                     void* __restrict__ s, int64_t G) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t chunk0 = wave * U;
@@ -88,10 +109,23 @@ __global__ __launch_bounds__(256) void k_quant_block(const uint4* __restrict__ x
         const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
         float f[8];
         unpack8(v[u], f);
-        const GroupDiv g = group_div(max_16lanes(amax8(f)));
-        if (gid < G) {
-            q[(chunk0 + u) * 64 + lane] = encode8(f, g);
-            if ((lane & 15) == 0) s[gid] = g.s;
+        const float amax = max_16lanes(amax8(f));
+        if constexpr (FMT == 0) {
+            const GroupDiv g = group_div(amax);
+            if (gid < G) {
+                q[(chunk0 + u) * 64 + lane] = encode8(f, g);
+                if ((lane & 15) == 0) static_cast<float*>(s)[gid] = g.s;
+            }
+        } else {
+            const int e = e8m0_exponent(amax / 448.0f);
+            const float inv = e8m0_inv(e);
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = f[j] * inv;
+            if (gid < G) {
+                q[(chunk0 + u) * 64 + lane] = e4m3x8(t);
+                if ((lane & 15) == 0) static_cast<uint8_t*>(s)[gid] = (uint8_t)(e + 127);
+            }
         }
     }
 }
@@ -291,19 +325,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VPL <= 10 ?
 // chunk t % 16, so each wave reads four whole 256-byte row segments per step.
 // FMT 0: fp32 scale; FMT 1: E8M0 byte e + 127 with e = ceil(log2(amax / 448)).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int e8m0_exponent(float s) {
-    const uint32_t u = __float_as_uint(s) & 0x7FFFFFFFu;
-    int e;
-    if (u == 0) return -127;
-    const int eb = (int)(u >> 23);
-    const uint32_t m = u & 0x7FFFFFu;
-    if (eb == 0)  // subnormal: s = m * 2^-149; ceil(log2 m) - 149
-        e = (m == 1u ? 0 : 32 - __clz((int)(m - 1u))) - 149;
-    else
-        e = eb - 127 + (m != 0u ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
 template <int FMT>
 __global__ __launch_bounds__(256) void k_requant(ReqBatch batch) {
     __shared__ float red[4];
@@ -348,8 +369,7 @@ __global__ __launch_bounds__(256) void k_requant(ReqBatch batch) {
         if (t == 0) static_cast<float*>(d.s)[local] = g.s;
     } else {
         const int e = e8m0_exponent(amax / 448.0f);
-        // x / 2^e == x * 2^-e exactly (both are the rounding of the same real)
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 127]
+        const float inv = e8m0_inv(e);  // x * 2^-e == x / 2^e exactly
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float f[8], tq[8];
@@ -406,12 +426,15 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
 
 }  // namespace
 
-hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s,
+hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, void* s, int fmt,
                                  hipStream_t st) {
     constexpr int U = 4;
     const int64_t G = M * (K / 128);
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
-    return launch(k_quant_block<U>, (waves + 3) / 4, st, static_cast<const uint4*>(x),
+    if (fmt == 0)
+        return launch(k_quant_block<U, 0>, (waves + 3) / 4, st, static_cast<const uint4*>(x),
+                      static_cast<uint2*>(q), s, G);
+    return launch(k_quant_block<U, 1>, (waves + 3) / 4, st, static_cast<const uint4*>(x),
                   static_cast<uint2*>(q), s, G);
 }
 

@@ -99,6 +99,17 @@ int fp8_quantize_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, f
                        void* stream);
 
 /*
+ * 1x128 group quantization with E8M0 scale bytes (DeepSeek V4 page §1 E8M0
+ * format, §3 group size 128; the activation side of the MX-scaled GEMM).
+ *   x : bf16 [M, K]            q : E4M3 [M, K]            s : uint8 [M, K/128]
+ *   s[m][g] = e + 127, e = ceil(log2(amax / 448)) of the fp32 scale amax / 448,
+ *   clamped to [-127, 127] (0 for an all-zero group); q = E4M3(x / 2^e), an
+ *   exact division.  K % 128 != 0 -> FP8_ERR_SHAPE.  s needs no alignment.
+ */
+int fp8_quantize_block_e8m0(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, void* s_e8m0,
+                            void* stream);
+
+/*
  * Per-row quantization: per-token activations, or per-output-channel weights
  * (torchao PerRow of the verl "Test" section; CHANNEL strategy of the SGLang
  * page §2).
@@ -177,6 +188,27 @@ int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_
 int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
                                  const float* w_s, const int32_t* offsets, void* y_bf16,
                                  int64_t T, int64_t E, int64_t N, int64_t K, void* stream);
+
+/*
+ * Batched W8A8 GEMM with E8M0 block scales (DeepSeek V4 page §3
+ * batched_gemm_a8w8_mxscale(A, W, A-scale, W-scale, bf16); §2 weight view
+ * (groups, out, in) and scale view (groups, out/128, in/128)), on the gfx950
+ * MX-scaled matrix instruction.  B batches (groups), token-major:
+ *   a   : E4M3 [M, B, K]          a_s : uint8 [M, B, K/128]  (E8M0 bytes)
+ *   w   : E4M3 [B, N, K]          w_s : uint8 [B, N/128, K/128]
+ *   y   : bf16 [M, B, N] (out)
+ *   Y[m,b,n] = sum_kb 2^(a_s[m,b,kb] - 127) * 2^(w_s[b,n/128,kb] - 127)
+ *              * sum_{k in kb} a[m,b,k] w[b,n,k]
+ *   Products exact; sums fp32 in the matrix core, which applies the power-of-
+ *   two scales; bf16 out, round to nearest even.  B = 1 is the dense GEMM
+ *   (a [M, K], y [M, N]).
+ *   N % 128 != 0, K % 128 != 0 or B * K > 2^22 -> FP8_ERR_SHAPE; M, B < 0 ->
+ *   FP8_ERR_ARG; M == 0 or B == 0 launch nothing.  Scale pointers need no
+ *   alignment.
+ */
+int fp8_batched_gemm_a8w8_mxscale(const void* a_e4m3, const void* w_e4m3, const void* a_s,
+                                  const void* w_s, void* y_bf16, int64_t B, int64_t M, int64_t N,
+                                  int64_t K, void* stream);
 
 /*
  * Diagnostic: the device E4M3 encoder alone.  q[i] = E4M3(float with bit

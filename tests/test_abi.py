@@ -38,7 +38,8 @@ def test_header_declares_the_calls():
     for required in ("fp8_quantize_block", "fp8_quantize_token", "fp8_rmsnorm_quant",
                      "fp8_requantize_weights", "fp8_gemm_a8w8_scaled",
                      "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
-                     "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits"):
+                     "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
+                     "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale"):
         assert required in names
 
 
@@ -78,6 +79,12 @@ def test_quantize_validation(L):
     assert L.fp8_quantize_block(None, 4, 128, vp(FAKE), vp(FAKE), None) == ARG
     assert L.fp8_quantize_block(vp(FAKE + 2), 4, 128, vp(FAKE), vp(FAKE), None) == ALIGN
     assert L.fp8_quantize_block(vp(FAKE), 0, 128, None, None, None) == OK  # empty
+    q8 = L.fp8_quantize_block_e8m0
+    assert q8(vp(FAKE), 4, 200, vp(FAKE), vp(FAKE), None) == SHAPE
+    assert q8(vp(FAKE), -1, 128, vp(FAKE), vp(FAKE), None) == ARG
+    assert q8(vp(FAKE), 4, 128, vp(FAKE), None, None) == ARG
+    assert q8(vp(FAKE), 4, 128, vp(FAKE + 4), vp(FAKE + 1), None) == ALIGN
+    assert q8(vp(FAKE), 0, 128, None, None, None) == OK
     assert L.fp8_quantize_token(vp(FAKE), 4, 12, vp(FAKE), vp(FAKE), None) == SHAPE
     assert L.fp8_quantize_token(vp(FAKE), 4, 16, vp(FAKE), vp(FAKE + 1), None) == ALIGN
     assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 16, 64,
@@ -87,6 +94,7 @@ def test_quantize_validation(L):
     assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), None, 1e-6, 4, 16, 0, None) == ARG
     if not _gpu():
         assert L.fp8_quantize_block(vp(FAKE), 4, 128, vp(FAKE), vp(FAKE), None) == DEVICE
+        assert q8(vp(FAKE), 4, 128, vp(FAKE), vp(FAKE + 1), None) == DEVICE
         assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 16, 0,
                                    None) == DEVICE
 
@@ -106,8 +114,18 @@ def test_gemm_validation(L):
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 2**31, 4, 256, 256, None) == ARG
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, vp(FAKE + 2), f, 64, 4, 256, 256,
                                           None) == ALIGN
+    mx = L.fp8_batched_gemm_a8w8_mxscale
+    assert mx(f, f, f, f, f, 1, -1, 256, 256, None) == ARG
+    assert mx(f, f, f, f, f, -1, 16, 256, 256, None) == ARG
+    assert mx(f, f, f, f, f, 1, 16, 200, 256, None) == SHAPE
+    assert mx(f, f, f, f, f, 1, 16, 256, 200, None) == SHAPE
+    assert mx(f, f, f, f, f, 4, 16, 256, 1 << 21, None) == SHAPE  # B * K > 2^22
+    assert mx(f, f, f, f, vp(FAKE + 8), 1, 16, 256, 256, None) == ALIGN
+    assert mx(None, None, None, None, None, 1, 0, 256, 256, None) == OK
+    assert mx(None, None, None, None, None, 0, 16, 256, 256, None) == OK
     if not _gpu():
         assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 256, 0, None) == DEVICE
+        assert mx(f, f, f, f, f, 1, 16, 256, 256, None) == DEVICE
 
 
 def test_requant_validation(L):

@@ -179,3 +179,56 @@ def test_grouped_moe_full_size_sampled(which):
     rows = np.unique(np.array(rows))
     y, ref, rows = _grouped_pipeline(A, W, offsets, rows=rows)
     assert_rows_close(y, ref, rows=rows, what=f"moe {which}")
+
+
+# --------------------------------------------------- E8M0 (MX) scaled GEMM --
+def _mx_pipeline(X, W, rows=None):
+    """GPU: 1x128 E8M0 activations, 128x128 E8M0 weights, MX GEMM.  Oracle:
+    the same quantization from bf16, then the fp64 GEMM with the powers of
+    two the bytes stand for."""
+    qa, sa = fp8.quantize_block_e8m0(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev()) if not W.is_cuda else W], fp8.SCALE_E8M0)
+    y = fp8.batched_gemm_a8w8_mxscale((qa, sa), (qw, sw))
+    Xh = X if rows is None else X[torch.as_tensor(rows)]
+    oqa, osa = oracle.quantize_block_e8m0(Xh)
+    oqw, osw = oracle.quantize_weight_block(W.cpu(), 1)
+    return y, oracle.mx_gemm(oqa, oqw, osa, osw)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (16, 256, 256), (130, 384, 512),
+                                   (1024, 256, 4096), (1100, 768, 640), (2047, 640, 1152),
+                                   (8200, 2304, 256)])
+def test_mx_dense_shapes(M, N, K):
+    # N = 384, 640: the last 256-column tile holds 128 columns
+    say(f"MX GEMM {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + 2 * N + K)
+    W = synth.weight(N, K, seed=N + 3 * K)
+    y, ref = _mx_pipeline(X, W)
+    assert_rows_close(y, ref, what=f"mx {M}x{N}x{K}")
+
+
+def test_mx_batched_groups():
+    M, B, N, K = 300, 3, 384, 512
+    say(f"batched MX GEMM M={M} B={B} N={N} K={K}")
+    X = synth.act_col_outliers(M * B, K, seed=91)          # rows (m, b) of [M, B, K]
+    W = synth.normal_bf16((B * N, K), seed=92, std=0.02)   # [B, N, K] as [B*N, K]
+    qa, sa = fp8.quantize_block_e8m0(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_E8M0)
+    y = fp8.batched_gemm_a8w8_mxscale((qa.view(M, B, K), sa.view(M, B, K // 128)),
+                                      (qw.view(B, N, K), sw.view(B, N // 128, K // 128)))
+    oqa, osa = oracle.quantize_block_e8m0(X)
+    oqw, osw = oracle.quantize_weight_block(W, 1)
+    ref = oracle.batched_mx_gemm(oqa.reshape(M, B, K), oqw.reshape(B, N, K),
+                                 osa.reshape(M, B, K // 128), osw.reshape(B, N // 128, K // 128))
+    assert_rows_close(y.view(M * B, N), ref.reshape(M * B, N), what="batched mx")
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_mx_dense_full_size_sampled(name):
+    N, K = synth.DENSE_SHAPES[name]
+    M = 8192
+    say(f"MX GEMM {name} M={M} ({M}x{N}x{K}), sampled rows")
+    X, W = synth.dense_linear(name, M, seed=13)
+    rows = sample_rows(M, 24, seed=N + 5)
+    y, ref = _mx_pipeline(X, W, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what=f"mx {name}")

@@ -71,6 +71,46 @@ def test_block_full_size_sampled(M, K):
     _eq_block(X, rows=sample_rows(M, 96, seed=M + K))
 
 
+def _eq_block_e8m0(xb: torch.Tensor, rows=None):
+    q, s = fp8.quantize_block_e8m0(xb.to(dev()))
+    xh = xb if rows is None else xb[torch.as_tensor(rows)]
+    oq, os_ = oracle.quantize_block_e8m0(xh)
+    gq, gs = host(q), host(s)
+    if rows is not None:
+        gq, gs = gq[rows], gs[rows]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs, os_), f"E8M0 bytes differ at {np.argwhere(gs != os_)[:5]}"
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (37, 384), (64, 4096), (130, 12288),
+                                 (5, 640)])
+def test_block_e8m0_shapes(M, K):
+    say(f"quantize_block_e8m0 [{M}, {K}]")
+    _eq_block_e8m0(synth.act_col_outliers(M, K, seed=M + K + 1))
+
+
+def test_block_e8m0_special_groups():
+    say("quantize_block_e8m0 special groups")
+    x = np.zeros((6, 512), np.float32)
+    x[0, 128:256] = -0.0
+    x[1, :128] = 3.0
+    x[1, 1:128:2] = -3.0
+    x[2, 5] = -(2.0 ** -66)
+    x[3, :] = np.float32(2.0 ** -133)            # bf16 subnormal amax: byte 0
+    x[4, :] = np.float32(448.0 * 2.0 ** 9)       # exact power-of-two scale 2^9
+    x[4, 7] = np.float32(-(448.0 * 2.0 ** 9))
+    x[5, :] = np.float32(3.3895313892515355e38)  # largest bf16
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    _eq_block_e8m0(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("M,K", [(8192, 4096), (32768, 768)])
+def test_block_e8m0_full_size_sampled(M, K):
+    say(f"quantize_block_e8m0 full [{M}, {K}] sampled rows")
+    X = synth.act_col_outliers(M, K, seed=2)
+    _eq_block_e8m0(X, rows=sample_rows(M, 96, seed=M + K + 7))
+
+
 def test_block_deterministic():
     say("quantize_block determinism")
     X = synth.act_col_outliers(512, 4096, seed=3).to(dev())
