@@ -13,7 +13,10 @@ One step = one pass of every step of the hot path:
      5120], per-row quantization of a [12288, 5120] weight, row-scaled GEMM;
   4. the MoE path: 1x128 quantization of the 32768 routed rows and the grouped
      block-scaled GEMMs gate_up (N=1536, K=2048) and down (N=2048, K=768) over
-     128 experts with top-8 routing.
+     128 experts with top-8 routing;
+  5. the E8M0 variant: the 144 policy weights re-quantized again with E8M0
+     scales, and one layer's four linears at M = 8192 through 1x128 E8M0
+     activation quantization and the MX-scaled GEMM.
 Every (layer, linear) has its own weight and activation tensors, so weights
 and activations stream from HBM as they would in a real forward pass.  Inputs
 are seeded synthetic tensors generated on the device before timing.
@@ -219,6 +222,20 @@ def main():
             Wq=torch.empty((E * N, K), dtype=torch.uint8, device=dev),
             Ws=torch.empty((E * N // 128, K // 128), dtype=torch.float32, device=dev),
             Y=torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+    # E8M0 variant: all policy weights again with E8M0 scales; layer 0 at M=8192
+    Wq8 = [torch.empty_like(w, dtype=torch.uint8) for w in W]
+    Ws8 = [torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.uint8, device=dev)
+           for w in W]
+    descs8 = (fp8._WeightDesc * len(W))()
+    for i in range(len(W)):
+        descs8[i] = fp8._WeightDesc(W[i].data_ptr(), Wq8[i].data_ptr(), Ws8[i].data_ptr(),
+                                    W[i].shape[0], W[i].shape[1])
+    MXM = 8192
+    Xq8 = {j: torch.empty((MXM, K), dtype=torch.uint8, device=dev)
+           for j, (name, (N, K)) in enumerate(shapes)}
+    Xs8 = {j: torch.empty((MXM, K // 128), dtype=torch.uint8, device=dev)
+           for j, (name, (N, K)) in enumerate(shapes)}
+
     mdescs = (fp8._WeightDesc * 2)()
     for i, which in enumerate(("gate_up", "down")):
         m = moe[which]
@@ -248,6 +265,16 @@ def main():
     calls.append(("gemm_row", L.fp8_gemm_a8w8_scaled,
                   (vp(hq.data_ptr()), vp(Wrq.data_ptr()), vp(hs.data_ptr()), vp(Wrs.data_ptr()),
                    None, vp(Yr.data_ptr()), RM, RN, RK, fp8.GRAN_ROW, sptr)))
+    calls.append(("requant_e8m0", L.fp8_requantize_weights,
+                  (descs8, len(W), fp8.SCALE_E8M0, sptr)))
+    for j, (name, (N, K)) in enumerate(shapes):
+        key = (0, j, MXM)
+        calls.append(("quant_e8m0_m8192", L.fp8_quantize_block_e8m0,
+                      (vp(X[key].data_ptr()), MXM, K, vp(Xq8[j].data_ptr()),
+                       vp(Xs8[j].data_ptr()), sptr)))
+        calls.append(("gemm_mx_m8192", L.fp8_batched_gemm_a8w8_mxscale,
+                      (vp(Xq8[j].data_ptr()), vp(Wq8[j].data_ptr()), vp(Xs8[j].data_ptr()),
+                       vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, sptr)))
     calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
     for which in ("gate_up", "down"):
         m = moe[which]
@@ -276,6 +303,17 @@ def main():
     work["quant_token_w"] = {"bytes": 2 * RN * RK + RN * RK + 4 * RN}
     work["gemm_row"] = {"flops": 2.0 * RM * RN * RK,
                         "bytes": RM * RK + RN * RK + 4 * (RM + RN) + 2 * RM * RN}
+    work["requant_e8m0"] = {"bytes": 0.0}
+    work["quant_e8m0_m8192"] = {"bytes": 0.0}
+    work["gemm_mx_m8192"] = {"flops": 0.0, "bytes": 0.0}
+    for li in range(layers):
+        for (name, (N, K)) in shapes:
+            work["requant_e8m0"]["bytes"] += 3 * N * K + (N // 128) * (K // 128)
+    for (name, (N, K)) in shapes:
+        work["quant_e8m0_m8192"]["bytes"] += 3 * MXM * K + MXM * (K // 128)
+        work["gemm_mx_m8192"]["flops"] += 2.0 * MXM * N * K
+        work["gemm_mx_m8192"]["bytes"] += (MXM * K + N * K + MXM * (K // 128)
+                                           + (N // 128) * (K // 128) + 2 * MXM * N)
     work["requant_moe"] = {"bytes": 0.0}
     work["quant_moe"] = {"bytes": 0.0}
     work["gemm_moe"] = {"flops": 0.0, "bytes": 0.0}
@@ -287,7 +325,8 @@ def main():
         work["gemm_moe"]["bytes"] += T * K + E * N * K + 4 * (T * (K // 128) + (E * N // 128)
                                                              * (K // 128)) + 2 * T * N
     launches = {"requant": 1, "rmsnorm_quant": 1, "quant_token_w": 1, "gemm_row": 1,
-                "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2}
+                "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2, "requant_e8m0": 1,
+                "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes)}
     for M in Ms:
         launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
 
@@ -359,7 +398,10 @@ def main():
                          "per-token quant of [4096,5120], per-row weight quant of "
                          "[12288,5120], row-scaled GEMM) and the qwen3-30b-a3b-shaped MoE "
                          "path (expert re-quant, 1x128 quant of 32768 routed rows, grouped "
-                         "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts)"),
+                         "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts), "
+                         "and the E8M0 variant (the policy re-quantized with E8M0 scales, one "
+                         "layer's four linears at M=8192 through E8M0 activation quant and "
+                         "the MX-scaled GEMM)"),
             "layers": layers, "M": list(Ms),
             "linears": {name: {"N": N, "K": K} for name, (N, K) in shapes},
             "per_token": {"M": RM, "K": RK, "N": RN},
