@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.orc_quantize_block.restype = None
         L.orc_quantize_block_e8m0.argtypes = [u16p, i64, i64, u8p, u8p]
         L.orc_quantize_block_e8m0.restype = None
+        L.orc_quantize_tensor.argtypes = [u16p, i64, u8p, f32p]
+        L.orc_quantize_tensor.restype = None
         L.orc_quantize_token.argtypes = [u16p, i64, i64, u8p, f32p]
         L.orc_quantize_token.restype = None
         L.orc_quantize_weight_block.argtypes = [u16p, i64, i64, ctypes.c_int, u8p,
@@ -212,6 +214,19 @@ def quantize_block_e8m0(x):
 def e8m0_value(b: np.ndarray) -> np.ndarray:
     """The power of two an E8M0 byte stands for, 2^(b - 127), as fp64 (exact)."""
     return np.ldexp(1.0, np.asarray(b, dtype=np.int64) - 127)
+
+
+def quantize_tensor(x):
+    """One scale for the whole tensor ([FP8-RL] (ii) KV cache, [E2E-FP8]
+    per-tensor dynamic scaling): returns (codes uint8 of x's shape, fp32
+    scale as a 0-d array)."""
+    xb = _bits16(x)
+    flat = np.ascontiguousarray(xb.reshape(-1))
+    q = np.empty(flat.shape, np.uint8)
+    s = np.empty((), np.float32)
+    lib().orc_quantize_tensor(_p(flat, ctypes.c_uint16), flat.size, _p(q, ctypes.c_uint8),
+                              s.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return q.reshape(xb.shape), s
 
 
 def quantize_token(x):

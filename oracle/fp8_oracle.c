@@ -264,6 +264,23 @@ void orc_quantize_block_e8m0(const uint16_t* x, int64_t M, int64_t K, uint8_t* q
     }
 }
 
+/* One scale for a whole tensor ([FP8-RL] abstract (ii): FP8 KV cache with
+ * per-step scale recalibration; [E2E-FP8] per-tensor dynamic scaling;
+ * [verl-3084] "Docs" tensorwise option): s = amax over all n elements / 448,
+ * q = E4M3(x / s). */
+void orc_quantize_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s) {
+    int64_t k;
+    float amax = 0.0f, sc;
+    for (k = 0; k < n; ++k) {
+        float a = fabsf(orc_bf16_to_f32(x[k]));
+        if (a > amax) amax = a;
+    }
+    sc = orc_scale_f32(amax);
+    *s = sc;
+#pragma omp parallel for schedule(static)
+    for (k = 0; k < n; ++k) q[k] = quant_elem(orc_bf16_to_f32(x[k]), sc);
+}
+
 void orc_quantize_token(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s) {
     int64_t m;
 #pragma omp parallel for schedule(static)

@@ -88,6 +88,8 @@ void orc_quantize_block(const uint16_t* x, int64_t M, int64_t K,
 /* One group per row: s[m] over x[m][0:K]. */
 /* 1x128 groups with E8M0 scale bytes s[M][K/128] (e + 127). */
 void orc_quantize_block_e8m0(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s);
+/* One fp32 scale for all n elements (per-tensor): *s = amax / 448. */
+void orc_quantize_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* s);
 void orc_quantize_token(const uint16_t* x, int64_t M, int64_t K,
                         uint8_t* q, float* s);
 

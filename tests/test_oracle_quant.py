@@ -266,3 +266,34 @@ def test_e8m0_block_zero_group_and_lossless_bytes():
     p2 = np.ldexp(np.float32(1.0), s8.astype(np.int32) - 127).astype(np.float32)
     codes = oracle.e8m0_lossless(p2)
     assert codes is not None and np.array_equal(codes.reshape(s8.shape), s8)
+
+
+# --------------------------------------------------------------- per-tensor --
+def test_tensor_equals_one_row_token_quant_and_exact_scale():
+    """One scale for the whole tensor: identical to the per-row quantizer on
+    the tensor flattened to a single row; the scale is the correctly rounded
+    amax / 448 of all elements and the amax element encodes to +-448."""
+    xb = _random_groups(37, M=12, K=384)
+    q, s = oracle.quantize_tensor(xb)
+    qt, st = oracle.quantize_token(np.ascontiguousarray(xb.reshape(1, -1)))
+    assert q.shape == xb.shape
+    assert np.array_equal(q.reshape(1, -1), qt) and float(s) == float(st[0])
+    xf = _f32(xb)
+    amax = float(np.abs(xf).max())
+    assert float(s) == frac_to_f32(Fraction(amax) / 448)
+    k = int(np.argmax(np.abs(xf).reshape(-1)))
+    assert q.reshape(-1)[k] in (0x7E, 0xFE)
+
+
+def test_tensor_codes_match_exact_arithmetic_and_zero_tensor():
+    tab = oracle.decode_table()
+    xb = _random_groups(41, M=3, K=256)
+    q, s = oracle.quantize_tensor(xb)
+    xf = _f32(xb).reshape(-1)
+    for k in range(0, xf.size, 7):
+        v = frac_to_f32(Fraction(float(xf[k])) / Fraction(float(s)))
+        assert q.reshape(-1)[k] == nearest_e4m3_exhaustive(v, tab), k
+    z = np.zeros((2, 64), np.float32)
+    z[1, 3] = -0.0
+    qz, sz = oracle.quantize_tensor(_bits(z))
+    assert float(sz) == 0.0 and qz[1, 3] == 0x80 and np.count_nonzero(qz) == 1
