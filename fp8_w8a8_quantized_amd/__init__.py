@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
+    "quantize_tensors", "quantize_tensor", "quantize_block_e8m0", "batched_gemm_a8w8_mxscale",
     "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
     "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
     "status_string", "abi_version",
@@ -47,6 +48,11 @@ class Fp8LibraryMissing(RuntimeError):
 class _WeightDesc(ctypes.Structure):
     _fields_ = [("w_bf16", ctypes.c_void_p), ("q_e4m3", ctypes.c_void_p),
                 ("s", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _TensorDesc(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("q_e4m3", ctypes.c_void_p),
+                ("s", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 _lib = None
@@ -78,6 +84,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
         "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
+        "fp8_quantize_tensors": ([ctypes.POINTER(_TensorDesc), i32, vp], i32),
         "fp8_encode_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),
         "fp8_bf16_round_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),
     }
@@ -223,6 +230,38 @@ def requantize_weights(weights: Sequence[torch.Tensor], scale_fmt: int = SCALE_F
     _check("fp8_requantize_weights",
            L.fp8_requantize_weights(descs, len(weights), scale_fmt, _stream(weights[0])))
     return results
+
+
+def quantize_tensors(tensors: Sequence[torch.Tensor],
+                     out: Sequence[Tuple[torch.Tensor, torch.Tensor]] = None
+                     ) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+    """Per-tensor quantization of every contiguous bf16 tensor in one batched
+    call (e.g. the K and V caches of every layer).  Returns [(E4M3 bytes of
+    the tensor's shape, fp32 scale [1])]."""
+    if len(tensors) == 0:
+        return []
+    descs = (_TensorDesc * len(tensors))()
+    results = []
+    for i, x in enumerate(tensors):
+        if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16:
+            raise TypeError(f"tensors[{i}] must be a bf16 torch.Tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"tensors[{i}] must be contiguous")
+        if out is not None:
+            q, s = out[i]
+        else:
+            q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+            s = torch.empty((1,), dtype=torch.float32, device=x.device)
+        descs[i] = _TensorDesc(x.data_ptr(), _as_u8(q).data_ptr(), s.data_ptr(), x.numel())
+        results.append((q, s))
+    L = load_library()
+    _check("fp8_quantize_tensors", L.fp8_quantize_tensors(descs, len(tensors), _stream(tensors[0])))
+    return results
+
+
+def quantize_tensor(x: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One scale for the whole bf16 tensor: (E4M3 bytes, fp32 scale [1])."""
+    return quantize_tensors([x], None if out is None else [out])[0]
 
 
 # ----------------------------------------------------------------- GEMMs --

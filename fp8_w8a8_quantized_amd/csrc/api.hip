@@ -15,6 +15,7 @@
 
 #include "../../include/fp8w8a8.h"
 #include "launch.hpp"
+#include "tensor.hpp"
 
 namespace {
 
@@ -114,6 +115,7 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
     if (n < 0 || (scale_fmt != FP8_SCALE_F32 && scale_fmt != FP8_SCALE_E8M0)) return FP8_ERR_ARG;
     if (n == 0) return FP8_OK;
     if (!descs) return FP8_ERR_ARG;
+    int work = 0;
     for (int i = 0; i < n; ++i) {
         const fp8_weight_desc& d = descs[i];
         if (d.N < 0 || d.K < 0) return FP8_ERR_ARG;
@@ -123,7 +125,9 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
         if (!aligned(d.w_bf16, 16) || !aligned(d.q_e4m3, 16) ||
             !aligned(d.s, scale_fmt == FP8_SCALE_F32 ? 4 : 1))
             return FP8_ERR_ALIGN;
+        ++work;
     }
+    if (work == 0) return FP8_OK;  // only empty weights: nothing to launch
     if (int st = device_check()) return st;
     fp8k::ReqBatch batch;
     std::memset(&batch, 0, sizeof(batch));
@@ -147,6 +151,49 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
         r.block_begin = blocks;
         blocks += (d.N / 128) * (d.K / 128);
         if (batch.n == fp8k::kReqMaxDescs)
+            if (int st = flush()) return st;
+    }
+    return flush();
+}
+
+int fp8_quantize_tensors(const fp8_tensor_desc* descs, int n, void* stream) {
+    if (n < 0) return FP8_ERR_ARG;
+    if (n == 0) return FP8_OK;
+    if (!descs) return FP8_ERR_ARG;
+    int work = 0;
+    for (int i = 0; i < n; ++i) {
+        const fp8_tensor_desc& d = descs[i];
+        if (d.n < 0) return FP8_ERR_ARG;
+        if (d.n % 8 != 0) return FP8_ERR_SHAPE;
+        if (d.n == 0) continue;
+        if (!d.x_bf16 || !d.q_e4m3 || !d.s) return FP8_ERR_ARG;
+        if (!aligned(d.x_bf16, 16) || !aligned(d.q_e4m3, 16) || !aligned(d.s, 4))
+            return FP8_ERR_ALIGN;
+        ++work;
+    }
+    if (work == 0) return FP8_OK;  // only empty tensors: nothing to launch
+    if (int st = device_check()) return st;
+    fp8k::TensBatch batch;
+    std::memset(&batch, 0, sizeof(batch));
+    int64_t chunks = 0;
+    auto flush = [&]() -> int {
+        if (batch.n == 0) return FP8_OK;
+        const int r = launched(fp8k::launch_tensor_batch(batch, chunks, as_stream(stream)));
+        std::memset(&batch, 0, sizeof(batch));
+        chunks = 0;
+        return r;
+    };
+    for (int i = 0; i < n; ++i) {
+        const fp8_tensor_desc& d = descs[i];
+        if (d.n == 0) continue;
+        fp8k::TensDesc& t = batch.d[batch.n++];
+        t.x = d.x_bf16;
+        t.q = d.q_e4m3;
+        t.s = d.s;
+        t.nvec = d.n / 8;
+        t.chunk_begin = chunks;
+        chunks += (t.nvec + fp8k::kTensChunk - 1) / fp8k::kTensChunk;
+        if (batch.n == fp8k::kTensMaxDescs || chunks > (int64_t(1) << 30))
             if (int st = flush()) return st;
     }
     return flush();

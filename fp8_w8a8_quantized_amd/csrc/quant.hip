@@ -21,6 +21,7 @@
 
 #include "device.hpp"
 #include "launch.hpp"
+#include "tensor.hpp"
 #include "quotient.hpp"
 
 namespace fp8k {
@@ -424,6 +425,79 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
         reinterpret_cast<uint16_t*>(out)[i2] = (uint16_t)p;
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor quantization (one scale per tensor), four kernels per batch:
+// clear each tensor's scale slot, reduce |x| into it (the amax's fp32 bits:
+// for non-negative floats the unsigned integer order is the numeric order, so
+// an unsigned atomic max of the bits is the max), quantize with s = amax / 448,
+// then write s itself.  The kernel boundaries order the steps.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_tens_clear(TensBatch b) {
+    if ((int)threadIdx.x < b.n) *reinterpret_cast<uint32_t*>(b.d[threadIdx.x].s) = 0u;
+}
+
+__device__ __forceinline__ int tens_find(const TensBatch& b, int64_t chunk) {
+    int lo = 0, hi = b.n - 1;  // last descriptor whose first chunk is <= chunk
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (b.d[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+constexpr int kTensVpt = (int)(kTensChunk / 256);  // vectors per thread
+
+__global__ __launch_bounds__(256) void k_tens_amax(TensBatch b) {
+    __shared__ float red[4];
+    const TensDesc& d = b.d[tens_find(b, blockIdx.x)];
+    const int64_t base = ((int64_t)blockIdx.x - d.chunk_begin) * kTensChunk + threadIdx.x;
+    const uint4* x = static_cast<const uint4*>(d.x);
+    uint4 v[kTensVpt];
+#pragma unroll
+    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero(x, base + 256 * i, d.nvec);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTensVpt; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+        m = fmaxf(m, amax8(f));
+    }
+    m = max_wave(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        atomicMax(reinterpret_cast<unsigned int*>(d.s), __float_as_uint(m));
+    }
+}
+
+__global__ __launch_bounds__(256) void k_tens_quant(TensBatch b) {
+    const TensDesc& d = b.d[tens_find(b, blockIdx.x)];
+    const int64_t base = ((int64_t)blockIdx.x - d.chunk_begin) * kTensChunk + threadIdx.x;
+    const uint4* x = static_cast<const uint4*>(d.x);
+    uint2* q = static_cast<uint2*>(d.q);
+    const GroupDiv g = group_div(__uint_as_float(*reinterpret_cast<const uint32_t*>(d.s)));
+    uint4 v[kTensVpt];
+#pragma unroll
+    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero(x, base + 256 * i, d.nvec);
+#pragma unroll
+    for (int i = 0; i < kTensVpt; ++i) {
+        const int64_t idx = base + 256 * i;
+        if (idx < d.nvec) {
+            float f[8];
+            unpack8(v[i], f);
+            q[idx] = encode8(f, g);
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void k_tens_final(TensBatch b) {
+    if ((int)threadIdx.x < b.n) {
+        float* s = b.d[threadIdx.x].s;
+        *s = __uint_as_float(*reinterpret_cast<const uint32_t*>(s)) / 448.0f;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, void* s, int fmt,
@@ -490,6 +564,17 @@ hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt,
                           hipStream_t st) {
     if (fmt == 0) return launch(k_requant<0>, total_blocks, st, batch);
     return launch(k_requant<1>, total_blocks, st, batch);
+}
+
+hipError_t launch_tensor_batch(const TensBatch& batch, int64_t chunks, hipStream_t st) {
+    if (batch.n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_tens_clear, dim3(1), dim3(64), 0, st, batch);
+    if (chunks > 0) {
+        hipLaunchKernelGGL(k_tens_amax, dim3((unsigned)chunks), dim3(256), 0, st, batch);
+        hipLaunchKernelGGL(k_tens_quant, dim3((unsigned)chunks), dim3(256), 0, st, batch);
+    }
+    hipLaunchKernelGGL(k_tens_final, dim3(1), dim3(64), 0, st, batch);
+    return hipGetLastError();
 }
 
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st) {

@@ -1,0 +1,28 @@
+// Per-tensor dynamic quantization: launch interface between the C-ABI layer
+// and the kernels.  One fp32 scale per tensor (amax / 448); up to
+// kTensMaxDescs tensors per launch sequence, with descriptors passed in kernel
+// arguments.  A tensor of nvec 16-byte vectors covers ceil(nvec / kTensChunk)
+// workgroup chunks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+constexpr int kTensMaxDescs = 64;
+constexpr int64_t kTensChunk = 2048;  // vectors (32 KiB of bf16) per workgroup
+struct TensDesc {
+    const void* x;        // bf16 [nvec * 8]
+    void* q;              // E4M3 [nvec * 8]
+    float* s;             // holds the amax bits during the sequence, then the scale
+    int64_t nvec;
+    int64_t chunk_begin;  // first chunk of this tensor in the launch
+};
+struct TensBatch {
+    TensDesc d[kTensMaxDescs];
+    int n;
+};
+hipError_t launch_tensor_batch(const TensBatch& batch, int64_t chunks, hipStream_t st);
+
+}  // namespace fp8k

@@ -144,6 +144,30 @@ typedef struct {
     int64_t K;          /* with N' % 128 == 0 is passed as N = E * N')          */
 } fp8_weight_desc;
 
+/* One tensor of a per-tensor quantization batch (all pointers device memory). */
+typedef struct {
+    const void* x_bf16; /* bf16, n elements (any shape, contiguous)             */
+    void* q_e4m3;       /* E4M3, n elements (out)                                */
+    float* s;           /* one fp32 scale (out): amax over the tensor / 448     */
+    int64_t n;          /* element count, a multiple of 8                        */
+} fp8_tensor_desc;
+
+/*
+ * Per-tensor dynamic quantization ("FP8-RL" abstract (ii): FP8 KV cache with
+ * per-step scale recalibration; "LLM FP8 ..." page: per-tensor dynamic
+ * scaling; verl "Docs": tensorwise option): each descriptor's tensor gets one
+ * scale s = amax / 448 over all its elements and codes E4M3(x / s), exactly as
+ * fp8_quantize_token would give the tensor flattened to one row.  Meant for
+ * recalibrating the K and V caches of every layer in one call.  `descs` is a
+ * host array of n entries, read during the call only; each 64 descriptors
+ * take four small kernels.  While those kernels run, *s holds the amax's
+ * bits; the last one writes the scale.
+ *   n % 8 != 0 -> FP8_ERR_SHAPE; n < 0 (count or element count) -> FP8_ERR_ARG;
+ *   x and q 16-byte aligned, s 4-byte aligned; tensors with n == 0 are skipped
+ *   (their s is not written).
+ */
+int fp8_quantize_tensors(const fp8_tensor_desc* descs, int n, void* stream);
+
 /*
  * Per-RL-step policy weight re-quantization ("FP8-RL" abstract: weights change
  * every step and are re-quantized before each sync into the engine): every

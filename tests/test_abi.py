@@ -39,7 +39,8 @@ def test_header_declares_the_calls():
                      "fp8_requantize_weights", "fp8_gemm_a8w8_scaled",
                      "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
                      "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
-                     "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale"):
+                     "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
+                     "fp8_quantize_tensors"):
         assert required in names
 
 
@@ -143,6 +144,28 @@ def test_requant_validation(L):
     if not _gpu():
         arr = (D * 1)(good)
         assert L.fp8_requantize_weights(arr, 1, 0, None) == DEVICE
+
+
+def test_tensor_quant_validation(L):
+    vp = ctypes.c_void_p
+    D = fp8._TensorDesc
+    assert L.fp8_quantize_tensors(None, 0, None) == OK
+    assert L.fp8_quantize_tensors(None, 1, None) == ARG
+    assert L.fp8_quantize_tensors(None, -1, None) == ARG
+    one = (D * 1)()
+    one[0] = D(FAKE, FAKE, FAKE, 12)
+    assert L.fp8_quantize_tensors(one, 1, None) == SHAPE
+    one[0] = D(FAKE, FAKE, FAKE, -8)
+    assert L.fp8_quantize_tensors(one, 1, None) == ARG
+    one[0] = D(FAKE + 8, FAKE, FAKE, 64)
+    assert L.fp8_quantize_tensors(one, 1, None) == ALIGN
+    one[0] = D(FAKE, FAKE, FAKE + 2, 64)
+    assert L.fp8_quantize_tensors(one, 1, None) == ALIGN
+    one[0] = D(None, None, None, 0)
+    assert L.fp8_quantize_tensors(one, 1, None) == OK  # empty tensor: skipped
+    if not _gpu():
+        one[0] = D(FAKE, FAKE, FAKE, 64)
+        assert L.fp8_quantize_tensors(one, 1, None) == DEVICE
 
 
 def test_encode_validation(L):

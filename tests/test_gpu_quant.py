@@ -111,6 +111,38 @@ def test_block_e8m0_full_size_sampled(M, K):
     _eq_block_e8m0(X, rows=sample_rows(M, 96, seed=M + K + 7))
 
 
+def _eq_tensors(xs):
+    got = fp8.quantize_tensors([x.to(dev()) for x in xs])
+    for i, (x, (q, s)) in enumerate(zip(xs, got)):
+        oq, os_ = oracle.quantize_tensor(x)
+        gq, gs = host(q), host(s)
+        assert np.array_equal(gq, oq), f"tensor {i}: codes differ at {np.argwhere(gq != oq)[:5]}"
+        assert gs.view(np.uint32)[0] == np.asarray(os_).view(np.uint32), f"tensor {i}: scale"
+
+
+@pytest.mark.parametrize("shape", [(8,), (1, 2048 * 8), (3, 2048 * 8 + 8), (37, 1000),
+                                   (1024, 1024), (5, 7, 128)])
+def test_tensor_shapes(shape):
+    say(f"quantize_tensors {shape}")
+    n = int(np.prod(shape))
+    x = synth.act_col_outliers(1, n, seed=n % 97).reshape(shape)
+    _eq_tensors([x.contiguous()])
+
+
+def test_tensor_batch_over_one_launch_and_zero_tensor():
+    say("quantize_tensors: 70 tensors (two launch groups) incl. an all-zero one")
+    xs = [synth.normal_bf16((16 + 8 * i, 128), seed=300 + i, std=0.5 + i) for i in range(70)]
+    xs[5] = torch.zeros((64, 128), dtype=torch.bfloat16)
+    _eq_tensors(xs)
+
+
+def test_tensor_kv_cache_layers():
+    say("quantize_tensors: K and V of 4 layers, [8192 tokens, 8 heads x 128]")
+    xs = [synth.normal_bf16((8192, 1024), seed=500 + i, std=1.0 + 0.25 * i) for i in range(8)]
+    xs[3][17, 5] = 4096.0  # one outlier sets its tensor's scale
+    _eq_tensors(xs)
+
+
 def test_block_deterministic():
     say("quantize_block determinism")
     X = synth.act_col_outliers(512, 4096, seed=3).to(dev())
