@@ -236,6 +236,18 @@ def main():
     Xs8 = {j: torch.empty((MXM, K // 128), dtype=torch.uint8, device=dev)
            for j, (name, (N, K)) in enumerate(shapes)}
 
+    # K/V cache recalibration: per-tensor quant of every layer's K and V
+    kv_x, kv_q, kv_s = [], [], []
+    for li in range(layers):
+        for t in synth.kv_cache(li, seed=3, device=dev):
+            kv_x.append(t)
+            kv_q.append(torch.empty_like(t, dtype=torch.uint8))
+            kv_s.append(torch.empty((), dtype=torch.float32, device=dev))
+    kvdescs = (fp8._TensorDesc * len(kv_x))()
+    for i, t in enumerate(kv_x):
+        kvdescs[i] = fp8._TensorDesc(t.data_ptr(), kv_q[i].data_ptr(), kv_s[i].data_ptr(),
+                                     t.numel())
+
     mdescs = (fp8._WeightDesc * 2)()
     for i, which in enumerate(("gate_up", "down")):
         m = moe[which]
@@ -275,6 +287,7 @@ def main():
         calls.append(("gemm_mx_m8192", L.fp8_batched_gemm_a8w8_mxscale,
                       (vp(Xq8[j].data_ptr()), vp(Wq8[j].data_ptr()), vp(Xs8[j].data_ptr()),
                        vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, sptr)))
+    calls.append(("quant_kv_tensor", L.fp8_quantize_tensors, (kvdescs, len(kv_x), sptr)))
     calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
     for which in ("gate_up", "down"):
         m = moe[which]
@@ -314,6 +327,7 @@ def main():
         work["gemm_mx_m8192"]["flops"] += 2.0 * MXM * N * K
         work["gemm_mx_m8192"]["bytes"] += (MXM * K + N * K + MXM * (K // 128)
                                            + (N // 128) * (K // 128) + 2 * MXM * N)
+    work["quant_kv_tensor"] = {"bytes": float(sum(3 * t.numel() + 4 for t in kv_x))}
     work["requant_moe"] = {"bytes": 0.0}
     work["quant_moe"] = {"bytes": 0.0}
     work["gemm_moe"] = {"flops": 0.0, "bytes": 0.0}
@@ -326,7 +340,8 @@ def main():
                                                              * (K // 128)) + 2 * T * N
     launches = {"requant": 1, "rmsnorm_quant": 1, "quant_token_w": 1, "gemm_row": 1,
                 "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2, "requant_e8m0": 1,
-                "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes)}
+                "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes),
+                "quant_kv_tensor": 1}
     for M in Ms:
         launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
 
@@ -401,10 +416,12 @@ def main():
                          "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts), "
                          "and the E8M0 variant (the policy re-quantized with E8M0 scales, one "
                          "layer's four linears at M=8192 through E8M0 activation quant and "
-                         "the MX-scaled GEMM)"),
+                         "the MX-scaled GEMM), and the K/V cache recalibration (per-tensor "
+                         "quant of every layer's K and V, [8192, 1024] each)"),
             "layers": layers, "M": list(Ms),
             "linears": {name: {"N": N, "K": K} for name, (N, K) in shapes},
             "per_token": {"M": RM, "K": RK, "N": RN},
+            "kv_cache": {"tensors": len(kv_x), "shape": list(kv_x[0].shape)},
             "moe": {"experts": moe["gate_up"]["E"], "rows": moe["gate_up"]["T"],
                     "gate_up": {"N": moe["gate_up"]["N"], "K": moe["gate_up"]["K"]},
                     "down": {"N": moe["down"]["N"], "K": moe["down"]["K"]}},

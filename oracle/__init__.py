@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.orc_f32_to_bf16_rne.restype = ctypes.c_uint16
         L.orc_bf16_rne_array.argtypes = [f32p, i64, u16p]
         L.orc_bf16_rne_array.restype = None
+        L.orc_add_bf16.argtypes = [u16p, u16p, i64, u16p]
+        L.orc_add_bf16.restype = None
         L.orc_scale_f32.argtypes = [ctypes.c_float]
         L.orc_scale_f32.restype = ctypes.c_float
         L.orc_e8m0_exponent.argtypes = [ctypes.c_float]
@@ -274,6 +276,29 @@ def rmsnorm_quant(x, gamma, eps: float):
     lib().orc_rmsnorm_quant(_p(xb, ctypes.c_uint16), _p(gb, ctypes.c_uint16), eps, M, K,
                             _p(q, ctypes.c_uint8), _p(s, ctypes.c_float))
     return q, s
+
+
+def add_bf16(x, r) -> np.ndarray:
+    """bf16 bits of the residual add: nearest bf16 to the exact x + r."""
+    xb, rb = _bits16(x), _bits16(r)
+    assert xb.shape == rb.shape
+    h = np.empty(xb.shape, np.uint16)
+    lib().orc_add_bf16(_p(xb, ctypes.c_uint16), _p(rb, ctypes.c_uint16), xb.size,
+                       _p(h, ctypes.c_uint16))
+    return h
+
+
+def add_rmsnorm_quant(x, r, gamma, eps: float, group_size: int = 0):
+    """Residual add, then fused RMSNorm + quantization of the sum (the
+    add_rmsnorm_quant entry of [sglang-21403] §1).  Returns (q, s, h): codes,
+    scales ([M] for group_size 0, [M, K/128] for 128) and h, the new residual
+    stream (bf16 bits), which is also what gets normalized."""
+    h = add_bf16(x, r)
+    if group_size == 0:
+        q, s = rmsnorm_quant(h, gamma, eps)
+    else:
+        q, s = quantize_block(rmsnorm_bf16(h, gamma, eps))
+    return q, s, h
 
 
 # ----------------------------------------------------------------- GEMM --

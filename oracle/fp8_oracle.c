@@ -165,6 +165,38 @@ void orc_bf16_rne_array(const float* v, int64_t n, uint16_t* out) {
     for (i = 0; i < n; ++i) out[i] = orc_f32_to_bf16_rne(v[i]);
 }
 
+/* Nearest bf16 to a finite double, ties to even; below the smallest normal
+ * the bf16 quantum is 2^-133.  Magnitudes past the largest finite bf16 do not
+ * occur for the sums formed here and are not handled. */
+static uint16_t f64_to_bf16_rne(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v), r;
+    int e, qe;
+    float f;
+    uint32_t u;
+    if (a == 0.0) return sign;
+    (void)frexp(a, &e); /* a = m * 2^e with 0.5 <= m < 1 */
+    qe = e - 8;         /* 8 significant bits: quantum 2^(e-8) */
+    if (qe < -133) qe = -133;
+    r = rint(ldexp(a, -qe)); /* count of quanta, ties to even (default mode) */
+    f = (float)ldexp(r, qe); /* exact: every bf16 value is an fp32 value */
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* Residual add of the fused add + RMSNorm (the add_rmsnorm_quant entry named
+ * on the SGLang RMSNorm + per-token fusion page, section 1): the new residual
+ * stream is the bf16 value nearest to the exact sum x + r.  The fp64 sum of
+ * two bf16 values is exact unless their exponents differ by 45 or more; then
+ * the smaller one is far below half a bf16 ulp of the larger and both the
+ * exact and the fp64 sum round to the larger one. */
+void orc_add_bf16(const uint16_t* x, const uint16_t* r, int64_t n, uint16_t* h) {
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        h[i] = f64_to_bf16_rne((double)orc_bf16_to_f32(x[i]) + (double)orc_bf16_to_f32(r[i]));
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scales                                                                   */
 /* ------------------------------------------------------------------------ */

@@ -63,6 +63,11 @@ float    orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16_rne(float f);
 void     orc_bf16_rne_array(const float* v, int64_t n, uint16_t* out);
 
+/* Residual add (SGLang RMSNorm + per-token fusion page, section 1, the
+ * add_rmsnorm_quant entry): h = bf16 nearest (ties to even) to the exact
+ * x + r, elementwise over n values. */
+void     orc_add_bf16(const uint16_t* x, const uint16_t* r, int64_t n, uint16_t* h);
+
 /* ---- scales ---- */
 
 /* fp32 scale of a group whose largest magnitude is amax: amax / 448 as one

@@ -29,6 +29,10 @@ Workload recipes (sizes and distributions of the pages' configurations):
                   (expert, token); X [4096, 2048] ~ N(0, 1) gathered to
                   [32768, 2048]; down-projection input [32768, 768] ~ N(0, 1);
                   W gate_up [128, 1536, 2048], down [128, 2048, 768] ~ N(0, 0.02).
+  KV cache:       per layer K and V [8192 tokens, 8 KV heads x 128] (the
+                  Qwen3-8B-shaped attention of the dense linears); K ~ N(0, 1)
+                  with one whole column x50 (an outlier channel), V ~ N(0, 1);
+                  36 layers, one per-tensor scale each for K and V.
 """
 from __future__ import annotations
 
@@ -48,6 +52,8 @@ RMS_M, RMS_K, RMS_N, RMS_EPS = 4096, 5120, 12288, 1e-6
 
 MOE_TOKENS, MOE_EXPERTS, MOE_TOPK = 4096, 128, 8
 MOE_HIDDEN, MOE_INTER = 2048, 768
+
+KV_TOKENS, KV_HEADS, KV_HEAD_DIM = 8192, 8, 128
 
 
 def _is_dev(device) -> bool:
@@ -171,3 +177,11 @@ def moe_inputs(which: str = "gate_up", seed: int = 0, tokens: int = MOE_TOKENS,
         A = normal_bf16((T, K), seed + 13, 1.0, device)
     W = normal_bf16((experts, N, K), seed + 17, 0.02, device)
     return A, W, offsets
+
+
+def kv_cache(layer: int, seed: int = 0, tokens: int = KV_TOKENS, device="cpu"):
+    """K and V of one layer, [tokens, KV_HEADS * KV_HEAD_DIM] bf16 each."""
+    width = KV_HEADS * KV_HEAD_DIM
+    k = act_col_outliers(tokens, width, seed + 2 * layer, device=device)
+    v = normal_bf16((tokens, width), seed + 2 * layer + 1, 1.0, device)
+    return k, v

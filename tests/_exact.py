@@ -39,6 +39,29 @@ def frac_to_f32(r: Fraction) -> float:
     return sign * float(fl * ulp)
 
 
+def frac_to_bf16_bits(r: Fraction) -> int:
+    """bf16 bit pattern of the nearest bf16 to the exact rational r (ties to
+    even; 7 fraction bits, subnormal quantum 2^-133); r == 0 gives +0; no
+    overflow handling (callers stay in range)."""
+    if r == 0:
+        return 0
+    sign = 0x8000 if r < 0 else 0
+    a = abs(r)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -126) - 7)
+    n = a / ulp
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = float(fl * ulp)  # a bf16 value, so exact in binary32 too
+    return sign | (struct.unpack("<I", struct.pack("<f", val))[0] >> 16)
+
+
 def bf16_all_positive_finite() -> np.ndarray:
     """All positive finite bf16 values as float32 (32,639 of them)."""
     bits = np.arange(1, 0x7F80, dtype=np.uint32)

@@ -6,7 +6,9 @@ pinned by: closed forms (x == 1, equal magnitudes), the exact sum of squares
 within the fp32 error bound of the fixed order, agreement with
 torch.nn.functional.rms_norm in fp64 (the definition the page cites) to one
 bf16 ulp, the bf16 rounding against torch's dtype conversion, and the fused ==
-composed identity.
+composed identity.  The residual add of the fused add + RMSNorm is pinned by
+exact rational arithmetic (crafted ties, wide exponent gaps, subnormals), by
+torch's bf16 add, and by its identities (r == 0, r == -x).
 """
 from fractions import Fraction
 
@@ -16,6 +18,7 @@ import torch
 
 import oracle
 import synth
+from _exact import frac_to_bf16_bits
 
 
 def _f32(bits):
@@ -101,3 +104,78 @@ def test_fused_equals_composed():
     y = oracle.rmsnorm_bf16(h, gamma, 1e-6)
     qc, sc = oracle.quantize_token(y)
     assert np.array_equal(qf, qc) and np.array_equal(sf, sc)
+
+
+def _bf16_pairs(n, seed):
+    """Random finite bf16 pairs with exponent gaps 0..60, mixed signs, plus
+    crafted exact ties, cancellations and subnormals (uint16 bits)."""
+    rng = np.random.default_rng(seed)
+    ex = rng.integers(0x30, 0x90, n).astype(np.uint32)
+    gap = rng.integers(0, 61, n).astype(np.uint32)
+    ey = np.clip(ex.astype(np.int64) - gap, 1, 254).astype(np.uint32)
+    sx = rng.integers(0, 2, n).astype(np.uint32) << 15
+    sy = rng.integers(0, 2, n).astype(np.uint32) << 15
+    x = sx | (ex << 7) | rng.integers(0, 128, n).astype(np.uint32)
+    y = sy | (ey << 7) | rng.integers(0, 128, n).astype(np.uint32)
+    # ties: 1 + m/128 plus 2^-8 (half an ulp) -> even neighbour
+    m = np.arange(128, dtype=np.uint32)
+    tx = (127 << 7) | m
+    ty = np.full(128, 0x3B80, np.uint32)  # 2^-8
+    # cancellation to exact zero and to a few ulps
+    cx = x[:64]
+    cy = cx ^ 0x8000
+    dx = x[64:128]
+    dy = (dx ^ 0x8000) + 1
+    # subnormal bf16 operands and sums
+    sub = rng.integers(1, 128, 64).astype(np.uint32)
+    sub2 = rng.integers(1, 128, 64).astype(np.uint32) | 0x8000 * rng.integers(0, 2, 64).astype(
+        np.uint32)
+    xs = np.concatenate([x, tx, cx, dx, sub, (1 << 7) | sub]).astype(np.uint16)
+    ys = np.concatenate([y, ty, cy, dy, sub2, sub2]).astype(np.uint16)
+    return xs, ys
+
+
+def test_add_bf16_against_exact_rationals():
+    """Every sum is the nearest bf16 to the exact rational x + r, found by
+    exact comparison (ties to even), on random pairs with exponent gaps up to
+    60, exact ties, cancellations and subnormal operands."""
+    xs, ys = _bf16_pairs(4000, seed=11)
+    got = oracle.add_bf16(xs, ys)
+    xf, yf = _f32(xs), _f32(ys)
+    exp = np.array([frac_to_bf16_bits(Fraction(float(a)) + Fraction(float(b)))
+                    for a, b in zip(xf, yf)], np.uint16)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+    # the crafted ties really are ties and really round both ways
+    t = slice(4000, 4128)
+    assert np.any(got[t] == xs[t]) and np.any(got[t] != xs[t])
+
+
+def test_add_bf16_matches_torch_and_identities():
+    xs, ys = _bf16_pairs(20000, seed=12)
+    tx = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16)
+    ty = torch.from_numpy(ys.view(np.int16)).view(torch.bfloat16)
+    ref = (tx.float() + ty.float()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.add_bf16(xs, ys), ref)
+    zero = np.zeros_like(xs)
+    assert np.array_equal(oracle.add_bf16(xs, zero), np.where(xs == 0x8000, 0, xs))
+    assert np.all(oracle.add_bf16(xs, xs ^ 0x8000) == 0)  # x + (-x) = +0
+
+
+@pytest.mark.parametrize("group_size", [0, 128])
+def test_add_rmsnorm_quant_is_add_then_fused(group_size):
+    """The residual form normalizes the new residual stream (the sum), not x:
+    it equals the plain fused form applied to torch's bf16 sum, and returns
+    that sum as the new residual."""
+    x, gamma = synth.rms_inputs(M=24, K=5120, seed=6)
+    r = synth.normal_bf16((24, 5120), seed=7, std=2.0)
+    q, s, h = oracle.add_rmsnorm_quant(x, r, gamma, 1e-6, group_size)
+    hs = (x.float() + r.float()).to(torch.bfloat16)
+    assert np.array_equal(h, hs.view(torch.int16).numpy().view(np.uint16))
+    if group_size == 0:
+        q2, s2 = oracle.rmsnorm_quant(hs, gamma, 1e-6)
+    else:
+        q2, s2 = oracle.quantize_block(oracle.rmsnorm_bf16(hs, gamma, 1e-6))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    q0, _ = oracle.rmsnorm_quant(x, gamma, 1e-6) if group_size == 0 else (None, None)
+    if q0 is not None:
+        assert not np.array_equal(q, q0)
