@@ -202,6 +202,7 @@ def main():
     RM, RK, RN = synth.RMS_M, synth.RMS_K, synth.RMS_N
     h, gamma = synth.rms_inputs(seed=1, device=dev)
     Wr = synth.weight(RN, RK, seed=31, device=dev)
+    hx = synth.normal_bf16((RM, RK), seed=2, std=3.0, device=dev)  # residual stream
     hq = torch.empty((RM, RK), dtype=torch.uint8, device=dev)
     hs = torch.empty((RM,), dtype=torch.float32, device=dev)
     Wrq = torch.empty((RN, RK), dtype=torch.uint8, device=dev)
@@ -272,6 +273,9 @@ def main():
     calls.append(("rmsnorm_quant", L.fp8_rmsnorm_quant,
                   (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hs.data_ptr()), vp(gamma.data_ptr()),
                    synth.RMS_EPS, RM, RK, 0, sptr)))
+    calls.append(("add_rmsnorm_quant", L.fp8_add_rmsnorm_quant,
+                  (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hx.data_ptr()), vp(hs.data_ptr()),
+                   vp(gamma.data_ptr()), synth.RMS_EPS, RM, RK, 0, sptr)))
     calls.append(("quant_token_w", L.fp8_quantize_token,
                   (vp(Wr.data_ptr()), RN, RK, vp(Wrq.data_ptr()), vp(Wrs.data_ptr()), sptr)))
     calls.append(("gemm_row", L.fp8_gemm_a8w8_scaled,
@@ -313,6 +317,7 @@ def main():
                 g["bytes"] += M * K + N * K + 4 * (M * (K // 128) + (N // 128) * (K // 128)) \
                     + 2 * M * N
     work["rmsnorm_quant"] = {"bytes": 2 * RM * RK + RM * RK + 4 * RM + 2 * RK}
+    work["add_rmsnorm_quant"] = {"bytes": 3 * 2 * RM * RK + RM * RK + 4 * RM + 2 * RK}
     work["quant_token_w"] = {"bytes": 2 * RN * RK + RN * RK + 4 * RN}
     work["gemm_row"] = {"flops": 2.0 * RM * RN * RK,
                         "bytes": RM * RK + RN * RK + 4 * (RM + RN) + 2 * RM * RN}
@@ -338,7 +343,8 @@ def main():
         work["gemm_moe"]["flops"] += 2.0 * T * N * K
         work["gemm_moe"]["bytes"] += T * K + E * N * K + 4 * (T * (K // 128) + (E * N // 128)
                                                              * (K // 128)) + 2 * T * N
-    launches = {"requant": 1, "rmsnorm_quant": 1, "quant_token_w": 1, "gemm_row": 1,
+    launches = {"requant": 1, "rmsnorm_quant": 1, "add_rmsnorm_quant": 1, "quant_token_w": 1,
+                "gemm_row": 1,
                 "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2, "requant_e8m0": 1,
                 "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes),
                 "quant_kv_tensor": 1}
@@ -410,7 +416,7 @@ def main():
                          "128x128 re-quantization of the 36-layer bf16 policy, then for "
                          "every layer and linear 1x128 activation quant + GEMM at M=8192 "
                          "and M=256; plus once per step the per-token path (RMSNorm + "
-                         "per-token quant of [4096,5120], per-row weight quant of "
+                         "per-token quant of [4096,5120], its residual-add form, per-row weight quant of "
                          "[12288,5120], row-scaled GEMM) and the qwen3-30b-a3b-shaped MoE "
                          "path (expert re-quant, 1x128 quant of 32768 routed rows, grouped "
                          "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts), "

@@ -22,7 +22,7 @@ __all__ = [
     "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
     "quantize_tensors", "quantize_tensor", "quantize_block_e8m0", "batched_gemm_a8w8_mxscale",
     "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
-    "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
+    "add_rmsnorm_quant", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
     "status_string", "abi_version",
 ]
 
@@ -81,6 +81,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_quantize_token": ([vp, i64, i64, vp, vp, vp], i32),
         "fp8_batched_gemm_a8w8_mxscale": ([vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
         "fp8_rmsnorm_quant": ([vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
+        "fp8_add_rmsnorm_quant": ([vp, vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
         "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
@@ -201,6 +202,33 @@ def rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
     L = load_library()
     _check("fp8_rmsnorm_quant", L.fp8_rmsnorm_quant(_ptr(q), _ptr(x), _ptr(s), _ptr(gamma),
                                                    float(eps), M, K, group_size, _stream(x)))
+    return q, s
+
+
+def add_rmsnorm_quant(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                      eps: float = 1e-6, group_size: int = 0, out=None
+                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Residual add + fused RMSNorm + FP8 quantization.  ``residual`` is
+    updated in place to bf16(x + residual), which is then normalized and
+    quantized as in ``rmsnorm_quant``.  Returns (q, s)."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(residual, torch.bfloat16, 2, "residual")
+    _need(gamma, torch.bfloat16, 1, "gamma")
+    M, K = x.shape
+    if tuple(residual.shape) != (M, K):
+        raise ValueError("residual must have x's shape")
+    if gamma.shape[0] != K:
+        raise ValueError("gamma must have K elements")
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        sshape = (M,) if group_size == 0 else (M, K // 128 if K % 128 == 0 else 0)
+        s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    L = load_library()
+    _check("fp8_add_rmsnorm_quant",
+           L.fp8_add_rmsnorm_quant(_ptr(q), _ptr(x), _ptr(residual), _ptr(s), _ptr(gamma),
+                                   float(eps), M, K, group_size, _stream(x)))
     return q, s
 
 

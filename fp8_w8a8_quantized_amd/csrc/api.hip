@@ -107,8 +107,27 @@ int fp8_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(gamma, 16) || !aligned(s, 4))
         return FP8_ERR_ALIGN;
     if (int st = device_check()) return st;
-    return launched(
-        fp8k::launch_rmsnorm_quant(q, x, s, gamma, eps, M, K, group_size, as_stream(stream)));
+    return launched(fp8k::launch_rmsnorm_quant(q, x, nullptr, s, gamma, eps, M, K, group_size,
+                                               as_stream(stream)));
+}
+
+int fp8_add_rmsnorm_quant(void* q, const void* x, void* residual, float* s, const void* gamma,
+                          float eps, int64_t M, int64_t K, int group_size, void* stream) {
+    if (M < 0 || (group_size != 0 && group_size != 128)) return FP8_ERR_ARG;
+    if (K <= 0 || K % (group_size == 0 ? 8 : 128) != 0) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!x || !residual || !q || !s || !gamma) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(q, 16) || !aligned(gamma, 16) ||
+        !aligned(s, 4))
+        return FP8_ERR_ALIGN;
+    if (M > INT64_MAX / 2 / K) return FP8_ERR_SHAPE;  // byte size must fit
+    const int64_t bytes = M * K * 2;
+    const char* xb = static_cast<const char*>(x);
+    const char* rb = static_cast<const char*>(residual);
+    if (xb < rb + bytes && rb < xb + bytes) return FP8_ERR_ARG;  // x and residual overlap
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_rmsnorm_quant(q, x, residual, s, gamma, eps, M, K, group_size,
+                                               as_stream(stream)));
 }
 
 int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream) {

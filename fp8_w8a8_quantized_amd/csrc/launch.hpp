@@ -29,8 +29,10 @@ hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, v
                                  hipStream_t st);
 hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s,
                                  hipStream_t st);
-hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps,
-                                int64_t M, int64_t K, int group_size, hipStream_t st);
+// res null: RMSNorm of x; else res := bf16(x + res) first, and that is normalized
+hipError_t launch_rmsnorm_quant(void* q, const void* x, void* res, float* s, const void* gamma,
+                                float eps, int64_t M, int64_t K, int group_size,
+                                hipStream_t st);
 hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, hipStream_t st);
 // B batches: A [M, B, K], W [B, N, K], E8M0 scales [M, B, K/128] and
 // [B, N/128, K/128], Y [M, B, N].  Requires B * K <= 2^22 and int tile counts.

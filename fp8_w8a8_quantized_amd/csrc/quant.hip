@@ -194,7 +194,23 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint4* __restrict__ x
 //   built without FMA contraction).  y stays in registers and is quantized per
 //   row (GROUP == 0) or per 1x128 group (GROUP == 128): with vector v held by
 //   lane v % 64, a 128-element group is 16 adjacent lanes of one step.
+//   RES: a residual add comes first.  h = bf16_rne(x + r) (one fp32 add of
+//   two bf16 values, whose bf16 rounding equals that of the exact sum) is
+//   written back over r as the new residual stream and takes x's place in
+//   everything after it.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b) {
+    float fa[8], fb[8];
+    unpack8(a, fa);
+    unpack8(b, fb);
+    uint4 o;
+    o.x = bf16x2_rne(fa[0] + fb[0], fa[1] + fb[1]);
+    o.y = bf16x2_rne(fa[2] + fb[2], fa[3] + fb[3]);
+    o.z = bf16x2_rne(fa[4] + fb[4], fa[5] + fb[5]);
+    o.w = bf16x2_rne(fa[6] + fb[6], fa[7] + fb[7]);
+    return o;
+}
+
 __device__ __forceinline__ void rms_y8(const uint4& xv, const uint4& gv, float inv,
                                        float (&y)[8]) {
     float f[8], g[8];
@@ -226,9 +242,17 @@ __device__ __forceinline__ float sumsq8(float p, const uint4& xv) {
     return p;
 }
 
-template <int VPL, int GROUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VPL <= 10 ? 4 : 1))) void k_rmsnorm_quant(uint2* __restrict__ q,
+// Waves per SIMD asked of the register allocator: rows held in registers
+// (VPL vectors per lane, twice that while x and the residual are both live)
+// need room, and 4 waves per SIMD keep enough loads in flight.
+constexpr int rms_waves(int vpl, bool res) {
+    return vpl > 10 ? 1 : (res && vpl >= 8) ? 3 : 4;
+}
+
+template <int VPL, int GROUP, bool RES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(rms_waves(VPL, RES)))) void k_rmsnorm_quant(uint2* __restrict__ q,
                                                        const uint4* __restrict__ x,
+                                                       uint4* __restrict__ res,
                                                        float* __restrict__ s,
                                                        const uint4* __restrict__ gamma,
                                                        float eps, int64_t M, int64_t V) {
@@ -236,12 +260,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VPL <= 10 ?
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
     const uint4* xr = x + row * V;
+    uint4* rr = RES ? res + row * V : nullptr;
     uint2* qr = q + row * V;
     const float kf = (float)(V * 8);
     if constexpr (VPL > 0) {
         uint4 v[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) v[i] = load_or_zero(xr, lane + 64 * i, V);
+        if constexpr (RES) {
+            uint4 r[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) r[i] = load_or_zero(rr, lane + 64 * i, V);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                v[i] = add_bf16x8(v[i], r[i]);
+                if (lane + 64 * i < V) rr[lane + 64 * i] = v[i];
+            }
+        }
         float p = 0.0f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -284,9 +319,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(VPL <= 10 ?
             }
         }
     } else {
-        // long rows: sum pass, then y recomputed (bit-identically) per pass
+        // long rows: sum pass, then y recomputed (bit-identically) per pass;
+        // with RES the sum pass stores h over r and later passes read h back
+        // (each lane reads only what it wrote itself)
         float p = 0.0f;
-        for (int64_t idx = lane; idx < V; idx += 64) p = sumsq8(p, xr[idx]);
+        if constexpr (RES) {
+            for (int64_t idx = lane; idx < V; idx += 64) {
+                const uint4 h = add_bf16x8(xr[idx], rr[idx]);
+                rr[idx] = h;
+                p = sumsq8(p, h);
+            }
+            xr = rr;
+        } else {
+            for (int64_t idx = lane; idx < V; idx += 64) p = sumsq8(p, xr[idx]);
+        }
         const float S = tree_sum_wave(p);
         const float inv = 1.0f / sqrtf(S / kf + eps);
         if constexpr (GROUP == 0) {
@@ -534,17 +580,21 @@ hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, f
     return launch(k_quant_token<0>, blocks, st, xv, qv, s, M, V);
 }
 
-hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps,
-                                int64_t M, int64_t K, int group_size, hipStream_t st) {
+hipError_t launch_rmsnorm_quant(void* q, const void* x, void* res, float* s, const void* gamma,
+                                float eps, int64_t M, int64_t K, int group_size,
+                                hipStream_t st) {
     const int64_t V = K / 8, blocks = (M + 3) / 4;
     uint2* qv = static_cast<uint2*>(q);
     const uint4* xv = static_cast<const uint4*>(x);
+    uint4* rv = static_cast<uint4*>(res);
     const uint4* gv = static_cast<const uint4*>(gamma);
-#define FP8_RMS_CASE(VPL)                                                                   \
-    if (VPL == 0 || V <= 64 * VPL) {                                                        \
-        if (group_size == 0)                                                                \
-            return launch(k_rmsnorm_quant<VPL, 0>, blocks, st, qv, xv, s, gv, eps, M, V);   \
-        return launch(k_rmsnorm_quant<VPL, 128>, blocks, st, qv, xv, s, gv, eps, M, V);     \
+#define FP8_RMS_LAUNCH(VPL, G, R) \
+    launch(k_rmsnorm_quant<VPL, G, R>, blocks, st, qv, xv, rv, s, gv, eps, M, V)
+#define FP8_RMS_CASE(VPL)                                                            \
+    if (VPL == 0 || V <= 64 * VPL) {                                                 \
+        if (group_size == 0)                                                         \
+            return rv ? FP8_RMS_LAUNCH(VPL, 0, true) : FP8_RMS_LAUNCH(VPL, 0, false);  \
+        return rv ? FP8_RMS_LAUNCH(VPL, 128, true) : FP8_RMS_LAUNCH(VPL, 128, false);  \
     }
     FP8_RMS_CASE(2)
     FP8_RMS_CASE(4)
@@ -557,6 +607,7 @@ hipError_t launch_rmsnorm_quant(void* q, const void* x, float* s, const void* ga
     FP8_RMS_CASE(32)
     FP8_RMS_CASE(0)
 #undef FP8_RMS_CASE
+#undef FP8_RMS_LAUNCH
     return hipErrorInvalidValue;
 }
 

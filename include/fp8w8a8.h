@@ -135,6 +135,22 @@ int fp8_quantize_token(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, f
 int fp8_rmsnorm_quant(void* q_e4m3, const void* x_bf16, float* s, const void* gamma_bf16,
                       float eps, int64_t M, int64_t K, int group_size, void* stream);
 
+/*
+ * Fused residual add + RMSNorm + FP8 quantization (the add_rmsnorm_quant
+ * entry named in the SGLang page §1; the page shows only the call without a
+ * residual, so the add is read as the usual pre-norm residual update).
+ *   residual : bf16 [M, K], in/out.  On return it holds h = bf16_rne(x +
+ *              residual), the nearest bf16 to the exact elementwise sum.
+ *   Then h takes x's place in fp8_rmsnorm_quant: q, s, gamma, eps, M, K and
+ *   group_size mean the same and are validated the same way.
+ *   x and residual must not overlap (FP8_ERR_ARG); q, s may not alias either.
+ *   M * K * 2 beyond INT64_MAX -> FP8_ERR_SHAPE.  On an error nothing is
+ *   launched and residual is left unchanged.
+ */
+int fp8_add_rmsnorm_quant(void* q_e4m3, const void* x_bf16, void* residual_bf16, float* s,
+                          const void* gamma_bf16, float eps, int64_t M, int64_t K,
+                          int group_size, void* stream);
+
 /* One weight of a re-quantization batch (all pointers device memory). */
 typedef struct {
     const void* w_bf16; /* [N, K] bf16                                          */

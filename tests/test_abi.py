@@ -40,7 +40,7 @@ def test_header_declares_the_calls():
                      "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
                      "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
                      "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
-                     "fp8_quantize_tensors"):
+                     "fp8_quantize_tensors", "fp8_add_rmsnorm_quant"):
         assert required in names
 
 
@@ -98,6 +98,23 @@ def test_quantize_validation(L):
         assert q8(vp(FAKE), 4, 128, vp(FAKE), vp(FAKE + 1), None) == DEVICE
         assert L.fp8_rmsnorm_quant(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1e-6, 4, 16, 0,
                                    None) == DEVICE
+
+
+def test_add_rmsnorm_quant_validation(L):
+    vp = ctypes.c_void_p
+    f, g = vp(FAKE), vp(FAKE + (1 << 20))
+    add = L.fp8_add_rmsnorm_quant
+    assert add(f, f, g, f, f, 1e-6, 4, 16, 64, None) == ARG          # group size
+    assert add(f, f, g, f, f, 1e-6, 4, 136, 128, None) == SHAPE      # K % 128
+    assert add(f, f, g, f, f, 1e-6, 4, 12, 0, None) == SHAPE         # K % 8
+    assert add(f, f, None, f, f, 1e-6, 4, 16, 0, None) == ARG        # no residual
+    assert add(f, f, vp(FAKE + (1 << 20) + 8), f, f, 1e-6, 4, 16, 0, None) == ALIGN
+    assert add(f, f, vp(FAKE + 64), f, f, 1e-6, 4, 16, 0, None) == ARG  # x, residual overlap
+    assert add(f, f, f, f, f, 1e-6, 4, 16, 0, None) == ARG              # same buffer
+    assert add(f, f, g, f, f, 1e-6, 1 << 60, 16, 0, None) == SHAPE       # byte size overflows
+    assert add(None, None, None, None, None, 1e-6, 0, 16, 0, None) == OK  # M == 0
+    if not _gpu():
+        assert add(f, f, g, f, f, 1e-6, 4, 16, 0, None) == DEVICE
 
 
 def test_gemm_validation(L):

@@ -211,6 +211,48 @@ def test_rmsnorm_quant_group128_full_workload_sampled():
     _eq_rms(h, gamma, 128, rows=sample_rows(4096, 128, seed=2))
 
 
+def _eq_add_rms(x, r, gamma, group_size, eps=1e-6, rows=None):
+    rd = r.to(dev())
+    q, s = fp8.add_rmsnorm_quant(x.to(dev()), rd, gamma.to(dev()), eps, group_size)
+    if rows is None:
+        xh, rh = x, r
+    else:
+        idx = torch.as_tensor(rows)
+        xh, rh = x[idx], r[idx]
+    oq, os_, oh = oracle.add_rmsnorm_quant(xh, rh, gamma, eps, group_size)
+    gq, gs, gh = host(q), host(s), synth.bf16_bits(rd)
+    if rows is not None:
+        gq, gs, gh = gq[rows], gs[rows], gh[rows]
+    assert np.array_equal(gh, oh), f"residual differs at {np.argwhere(gh != oh)[:5]}"
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("M,K,gs", [(3, 8, 0), (7, 200, 0), (5, 4096, 0), (9, 12288, 0),
+                                    (4, 40000, 0), (6, 256, 128), (33, 5120, 128),
+                                    (3, 40064, 128)])
+def test_add_rmsnorm_quant_shapes(M, K, gs):
+    say(f"add_rmsnorm_quant [{M}, {K}] group_size {gs}")
+    x, gamma = synth.rms_inputs(M=M, K=K, seed=M * K + 1)
+    r = synth.normal_bf16((M, K), seed=M + 2 * K, std=3.0)
+    _eq_add_rms(x, r, gamma, gs)
+
+
+@pytest.mark.parametrize("gs", [0, 128])
+def test_add_rmsnorm_quant_full_workload(gs):
+    say(f"add_rmsnorm_quant full [4096, 5120], group_size {gs}")
+    x, gamma = synth.rms_inputs(seed=5)
+    r = synth.normal_bf16((4096, 5120), seed=6, std=3.0)
+    _eq_add_rms(x, r, gamma, gs, rows=None if gs == 0 else sample_rows(4096, 256, seed=7))
+
+
+def test_add_rmsnorm_quant_cancelling_residual():
+    """r = -x: the new residual is all +0, so every row is the zero row."""
+    say("add_rmsnorm_quant with residual -x")
+    x, gamma = synth.rms_inputs(M=8, K=4096, seed=9)
+    _eq_add_rms(x, -x, gamma, 0)
+
+
 def _eq_req(ws, fmt, out=None, block_rows=None):
     res = fp8.requantize_weights([w.to(dev()) if not w.is_cuda else w for w in ws], fmt)
     for i, (w, (q, s)) in enumerate(zip(ws, res)):
