@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/fp8w8a8.h"
 #include "launch.hpp"
@@ -48,6 +49,55 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Stream-K workspace of the small-M GEMM, one per (device, stream): allocated
+// on the first GEMM call that needs it and held until the process ends.  The
+// arrival counters are cleared once, by an ordinary memset on that stream
+// (ordered before the first kernel); every launch leaves them zero.  No
+// allocation is attempted while the stream is being captured into a graph:
+// then the GEMM runs without stream-K.  Calls on one stream are ordered, so
+// they may share the workspace; calls on different streams get their own.
+struct WsEntry {
+    int dev;
+    hipStream_t stream;
+    fp8k::GemmWorkspace ws;
+};
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+
+bool gemm_workspace(hipStream_t st, fp8k::GemmWorkspace* out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    for (const WsEntry& e : g_ws)
+        if (e.dev == dev && e.stream == st) {
+            *out = e.ws;
+            return true;
+        }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return false;
+    }
+    void* part = nullptr;
+    void* cnt = nullptr;
+    const size_t cnt_bytes = size_t(fp8k::kGemmWsMaxTiles) * sizeof(int32_t);
+    if (hipMalloc(&part, size_t(fp8k::kGemmWsPartBytes)) != hipSuccess ||
+        hipMalloc(&cnt, cnt_bytes) != hipSuccess ||
+        hipMemsetAsync(cnt, 0, cnt_bytes, st) != hipSuccess) {
+        (void)hipGetLastError();
+        if (part) (void)hipFree(part);
+        if (cnt) (void)hipFree(cnt);
+        return false;
+    }
+    WsEntry e{dev, st, {part, static_cast<int32_t*>(cnt)}};
+    g_ws.push_back(e);
+    *out = e.ws;
+    return true;
+}
 
 }  // namespace
 
@@ -231,7 +281,11 @@ int fp8_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s, const f
         !aligned(w_s, 4))
         return FP8_ERR_ALIGN;
     if (int st = device_check()) return st;
-    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, as_stream(stream)));
+    fp8k::GemmWorkspace ws{};
+    const bool have_ws =
+        fp8k::gemm_small_path(M, N, K) && gemm_workspace(as_stream(stream), &ws);
+    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, have_ws ? &ws : nullptr,
+                                      as_stream(stream)));
 }
 
 int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,

@@ -716,6 +716,90 @@ __device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
     return t;
 }
 
+// One K step of a 128 x 128 tile from LDS stage `la`: BLOCK promotes each
+// 16 x 16 product by its row scale x the weight block scale into acc (the FMA
+// of a product trails its MFMA by one); ROW accumulates in the MFMA.
+template <int GRAN>
+__device__ __forceinline__ void pipe_mma(const uint8_t* la, const float* sW, int kb,
+                                         v4f (&acc)[4][2], int wm, int wn, int lr, int lk) {
+    const uint8_t* lb = la + BMP * BK;
+    v8i x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
+    if constexpr (GRAN == GRAN_BLOCK) {
+        const float sw = uniform_load(sW, kb);
+        const float* lsa = reinterpret_cast<const float*>(la + kStageTileP);
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * sw;
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        v8i wcur = frag(lb, wn * 32 + lr, lk);
+        v4f prev;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            v8i wnext = wcur;
+            if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v4f pk = mfma_f8(wcur, x[i], zero);
+                if (i > 0 || jj > 0) {
+                    const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? jj : jj - 1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
+                }
+                prev = pk;
+            }
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[3][1][e] = __builtin_fmaf(prev[e], sc[3], acc[3][1][e]);
+    } else {
+        v8i wcur = frag(lb, wn * 32 + lr, lk);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            v8i wnext = wcur;
+            if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][jj] = mfma_f8(wcur, x[i], acc[i][jj]);
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// bf16 stores of a finished 128 x 128 tile (ROW: scaled by the row and column
+// scales first); acc is left zeroed for the next tile.
+template <int GRAN>
+__device__ __forceinline__ void pipe_store(const Tile& ct, v4f (&acc)[4][2], int64_t N, int wm,
+                                           int wn, int lr, int lk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + lr;
+        float sa = 1.0f;
+        if constexpr (GRAN == GRAN_ROW) sa = ct.sA[r < ct.rows ? r : ct.rows - 1];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            v4f v = acc[i][jj];
+            acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (GRAN == GRAN_ROW) {
+                const v4f s4 =
+                    *reinterpret_cast<const v4f*>(ct.sW + wn * 32 + jj * 16 + 4 * lk);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+            }
+            if (r < ct.rows) {
+                uint2 o;
+                o.x = bf16x2_rne(v[0], v[1]);
+                o.y = bf16x2_rne(v[2], v[3]);
+                *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * N + wn * 32 + jj * 16 +
+                                          4 * lk) = o;
+            }
+        }
+    }
+}
+
 // Persistent small-M / grouped kernel.  The grid holds one workgroup per CU
 // (at most); XCD x = blockIdx % 8 owns the x-th eighth of the tile order and
 // its workgroups take every nx-th tile of it, so the workgroups of one XCD
@@ -826,79 +910,8 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
             }
         }
 
-        const uint8_t* la = lds + (g % NSTP) * kStageP;
-        const uint8_t* lb = la + BMP * BK;
-        v8i x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
-        if constexpr (GRAN == GRAN_BLOCK) {
-            const float sw = uniform_load(ct.sW, kb);
-            const float* lsa = reinterpret_cast<const float*>(la + kStageTileP);
-            float sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * sw;
-            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            v8i wcur = frag(lb, wn * 32 + lr, lk);
-            v4f prev;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                v8i wnext = wcur;
-                if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4f pk = mfma_f8(wcur, x[i], zero);
-                    if (i > 0 || jj > 0) {
-                        const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? jj : jj - 1;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
-                    }
-                    prev = pk;
-                }
-                wcur = wnext;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[3][1][e] = __builtin_fmaf(prev[e], sc[3], acc[3][1][e]);
-        } else {
-            v8i wcur = frag(lb, wn * 32 + lr, lk);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                v8i wnext = wcur;
-                if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][jj] = mfma_f8(wcur, x[i], acc[i][jj]);
-                wcur = wnext;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        if (kb == kbn - 1) {  // tile done: bf16 stores, fresh accumulators
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + i * 16 + lr;
-                float sa = 1.0f;
-                if constexpr (GRAN == GRAN_ROW) sa = ct.sA[r < ct.rows ? r : ct.rows - 1];
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    v4f v = acc[i][jj];
-                    acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (GRAN == GRAN_ROW) {
-                        const v4f s4 =
-                            *reinterpret_cast<const v4f*>(ct.sW + wn * 32 + jj * 16 + 4 * lk);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
-                    }
-                    if (r < ct.rows) {
-                        uint2 o;
-                        o.x = bf16x2_rne(v[0], v[1]);
-                        o.y = bf16x2_rne(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + wn * 32 + jj * 16 +
-                                                  4 * lk) = o;
-                    }
-                }
-            }
-        }
+        pipe_mma<GRAN>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
+        if (kb == kbn - 1) pipe_store<GRAN>(ct, acc, S.N, wm, wn, lr, lk);  // tile done
         if (++kb == kbn) {
             kb = 0;
             ++c_ti;
@@ -907,19 +920,234 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K small-M kernel (dense only).  The tiles' K steps, tile after tile
+// (u = tile * KB + kb, tiles in the k_gemm_pipe order), are cut into G equal
+// contiguous ranges, one per workgroup, so every CU gets the same number of
+// steps whatever the tile count (at decode M a linear has fewer 128 x 128
+// tiles than there are CUs, and a long K would leave most CUs idle).  A
+// workgroup whose range covers a whole tile stores it directly.  A tile cut
+// between workgroups is finished by the contributor that arrives last: each
+// contributor writes its fp32 accumulators to its partial slot, releases
+// them, and bumps the tile's arrival counter; the one that brings the count
+// to the number of contributors sums the partials in contributor order (so
+// the result does not depend on arrival order), resets the counter to zero
+// for the next launch and stores the tile.  Nobody waits for another
+// workgroup, so the scheme needs no co-residency.
+//   Coherence across XCDs (each has its own L2) is per access, not per cache:
+// partials are written and read as relaxed agent-scope atomics (64-bit
+// stores that write through the L2 and loads that read past it), and every
+// thread waits for its stores to complete before the workgroup barrier that
+// precedes the counter update.  Agent-scope fences would do the same by
+// writing back and invalidating the whole L2 of the XCD, which costs the
+// other workgroups there their cached operand tiles.
+//   Workspace: part = G x 2 slots of 128 x 128 fp32 (slot 0: the first tile
+//   of a workgroup's range, slot 1: its last), in register order (v4f index
+//   (slot * 8 + i * 2 + jj) * 512 + tid); cnt = one int per tile, zero
+//   between launches.
+// ---------------------------------------------------------------------------
+static_assert(kGemmWsPartBytes == kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
+
+struct SkWork {
+    v4f* part;
+    int32_t* cnt;
+};
+
+// one v4f of a partial tile as two relaxed agent-scope 64-bit atomics
+__device__ __forceinline__ void sk_put(v4f* p, const v4f& v) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    const uint64_t lo = (uint64_t)__float_as_uint(v[1]) << 32 | __float_as_uint(v[0]);
+    const uint64_t hi = (uint64_t)__float_as_uint(v[3]) << 32 | __float_as_uint(v[2]);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ v4f sk_get(const v4f* p) {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v4f{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+               __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+}
+
+// A thread's 4 x 2 accumulator fragments (rows wm * 64 + i * 16 + lr of its
+// wave) to / from a partial slot; CHECK skips rows at or past `wrows` (rows
+// of the wave that exist), which only the wave holding row M - 1 needs.
+template <bool CHECK>
+__device__ __forceinline__ void sk_write(v4f* mine, const v4f (&acc)[4][2], int wrows, int lr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (!CHECK || i * 16 + lr < wrows)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) sk_put(mine + (i * 2 + jj) * kThreadsP, acc[i][jj]);
+}
+__device__ __forceinline__ void sk_add(v4f (&sum)[4][2], const v4f (&p)[4][2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[i][jj][e] = sum[i][jj][e] + p[i][jj][e];
+}
+template <bool CHECK>
+__device__ __forceinline__ void sk_read_add(v4f (&sum)[4][2], const v4f* pp, int wrows, int lr) {
+    v4f p[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            p[i][jj] = (!CHECK || i * 16 + lr < wrows) ? sk_get(pp + (i * 2 + jj) * kThreadsP)
+                                                        : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    sk_add(sum, p);
+}
+
+// first K step of rank c's range, and the rank owning step u
+__device__ __forceinline__ int64_t sk_start(int64_t c, int64_t Wt, int64_t G) {
+    return c * Wt / G;
+}
+__device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t Wt, int64_t G) {
+    return ((u + 1) * G + Wt - 1) / Wt - 1;
+}
+
+template <int GRAN>
+__global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tiles, SkWork ws) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP + 16];
+    int32_t* s_last = reinterpret_cast<int32_t*>(lds + kLdsP);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int64_t KB = S.K / BK, Wt = tiles * KB, G = gridDim.x;
+    // XCD-contiguous rank: the workgroups of XCD x (blockIdx % 8 == x) hold
+    // consecutive ranks, so one XCD's ranges are adjacent steps and tiles
+    const int64_t bid = blockIdx.x, xcd = bid & 7;
+    const int64_t q8 = G >> 3, r8 = G & 7;
+    const int64_t c = xcd * q8 + (xcd < r8 ? xcd : r8) + (bid >> 3);
+    const int64_t u0 = sk_start(c, Wt, G), u1 = sk_start(c + 1, Wt, G);
+    const int ng = (int)(u1 - u0);
+    if (ng <= 0) return;  // whole workgroup leaves together
+    const int64_t t_first = u0 / KB;
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int kbn = (int)KB;
+    int64_t l_t = t_first;  // tile and k block of the next stage to load
+    int l_kb = (int)(u0 - t_first * KB);
+    Tile lt = tile_at<GRAN, false>(S, l_t);
+#pragma unroll
+    for (int st = 0; st < NSTP - 1; ++st) {
+        if (st < ng) {
+            stage_pipe<GRAN>(lds, st, lt, S.K, KB, l_kb, wave, lane);
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_t;
+                if (l_t < tiles) lt = tile_at<GRAN, false>(S, l_t);
+            }
+        }
+    }
+    int64_t c_t = t_first;  // tile being multiplied, its k block, where this range entered it
+    int kb = (int)(u0 - t_first * KB);
+    int kb_in = kb;
+    Tile ct = tile_at<GRAN, false>(S, c_t);
+
+    for (int g = 0; g < ng; ++g) {
+        asm volatile("" ::: "memory");
+        wait_stage<GRAN>(g, ng);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (g + NSTP - 1 < ng) {
+            stage_pipe<GRAN>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_t;
+                if (l_t < tiles) lt = tile_at<GRAN, false>(S, l_t);
+            }
+        }
+        pipe_mma<GRAN>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
+
+        if (kb == kbn - 1 || g == ng - 1) {  // this range's part of tile c_t is done
+            if (kb_in == 0 && kb == kbn - 1) {
+                pipe_store<GRAN>(ct, acc, S.N, wm, wn, lr, lk);
+            } else {
+                const int64_t c_lo = sk_owner(c_t * KB, Wt, G);
+                const int64_t c_hi = sk_owner(c_t * KB + KB - 1, Wt, G);
+                const int slot = (c_t == t_first) ? 0 : 1;
+                // rows past M carry nothing: a wave whose 64 rows are all
+                // valid (the common case) moves its partial without checks
+                const int wrows = ct.rows - wm * 64;
+                v4f* mine = ws.part + (c * 2 + slot) * 8 * kThreadsP + tid;
+                if (wrows >= 64)
+                    sk_write<false>(mine, acc, wrows, lr);
+                else if (wrows > 0)
+                    sk_write<true>(mine, acc, wrows, lr);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this thread's partial is out
+                __syncthreads();
+                if (tid == 0) {
+                    const int32_t before = __hip_atomic_fetch_add(
+                        ws.cnt + c_t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    *s_last = (before == (int32_t)(c_hi - c_lo)) ? 1 : 0;
+                }
+                __syncthreads();
+                if (*s_last) {
+                    v4f sum[4][2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) sum[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+                        if (cc == c) {
+                            sk_add(sum, acc);
+                            continue;
+                        }
+                        const int sl = (sk_start(cc, Wt, G) / KB == c_t) ? 0 : 1;
+                        const v4f* pp = ws.part + (cc * 2 + sl) * 8 * kThreadsP + tid;
+                        if (wrows >= 64)
+                            sk_read_add<false>(sum, pp, wrows, lr);
+                        else if (wrows > 0)
+                            sk_read_add<true>(sum, pp, wrows, lr);
+                    }
+                    if (tid == 0)
+                        __hip_atomic_store(ws.cnt + c_t, 0, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    pipe_store<GRAN>(ct, sum, S.N, wm, wn, lr, lk);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        if (++kb == kbn) {
+            kb = 0;
+            kb_in = 0;
+            ++c_t;
+            if (c_t < tiles) ct = tile_at<GRAN, false>(S, c_t);
+        }
+    }
+}
+
 }  // namespace
 
+// The large-M kernel addresses a tile with 32-bit buffer offsets (256 rows x
+// K bytes, so K <= 2^22) and counts tiles and steps in int.
+bool gemm_small_path(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
+    return !(M >= 1024 && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
+             (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31));
+}
+
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
-                       void* y, int64_t M, int64_t N, int64_t K, int gran, hipStream_t st) {
+                       void* y, int64_t M, int64_t N, int64_t K, int gran,
+                       const GemmWorkspace* ws, hipStream_t st) {
     if (M == 0) return hipSuccess;
     const auto* A = static_cast<const uint8_t*>(a);
     const auto* Wp = static_cast<const uint8_t*>(w);
     auto* Yp = static_cast<uint16_t*>(y);
-    // The large-M kernel addresses a tile with 32-bit buffer offsets
-    // (256 rows x K bytes, so K <= 2^22) and counts tiles and steps in int.
-    const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
-    if (M >= 1024 && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
-        (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
+    if (!gemm_small_path(M, N, K)) {
+        const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
         const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
         const BigGeom G{M, N, K, 1};
         if (gran == GRAN_BLOCK)
@@ -937,6 +1165,19 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     S.M = M; S.N = N; S.K = K; S.E = 0;
     S.tm_count = (M + BMP - 1) / BMP;
     const int64_t tiles = S.tm_count * (N / BNP);
+    const int64_t steps = tiles * (K / BK);
+    if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
+        // stream-K: every workgroup gets at least one K step (grid <= steps)
+        const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
+        const SkWork sk{static_cast<v4f*>(ws->part), ws->cnt};
+        if (gran == GRAN_BLOCK)
+            hipLaunchKernelGGL(k_gemm_sk<GRAN_BLOCK>, dim3((unsigned)grid), dim3(kThreadsP), 0, st,
+                               S, tiles, sk);
+        else
+            hipLaunchKernelGGL(k_gemm_sk<GRAN_ROW>, dim3((unsigned)grid), dim3(kThreadsP), 0, st,
+                               S, tiles, sk);
+        return hipGetLastError();
+    }
     const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
     if (gran == GRAN_BLOCK)
         hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, false>), dim3((unsigned)grid), dim3(kThreadsP),

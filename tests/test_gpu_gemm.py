@@ -93,6 +93,78 @@ def test_dense_linears_full_size_sampled(name, M):
     assert_rows_close(y, ref, rows=rows, what=f"{name} M={M}")
 
 
+# Small-M shapes run stream-K: the tiles' K steps are split evenly over the
+# workgroups and a tile cut between workgroups is summed by its last arriver.
+@pytest.mark.parametrize("M,N,K", [(200, 8960, 640),    # 140 tiles, ranges of 2-3 steps
+                                   (1000, 5120, 384),   # 320 tiles (> one per CU)
+                                   (3, 1024, 12288),    # 8 tiles, 96 steps each
+                                   (129, 128, 128)])    # 2 tiles, 1 step each
+def test_block_stream_k_shapes(M, N, K):
+    say(f"block GEMM stream-K {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + 2 * N + K)
+    W = synth.weight(N, K, seed=N + 2 * K)
+    y, ref = _block_pipeline(X, W)
+    assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
+
+
+def test_stream_k_repeatable_across_interleaved_shapes():
+    """Outputs do not depend on arrival order, and every launch leaves the
+    arrival counters zero: A, B, A give bit-identical A outputs, all within
+    tolerance of the oracle."""
+    say("stream-K repeatability: shapes A, B, A on one stream")
+    shapes = [(256, 4096, 12288), (96, 6144, 4096)]
+    ops = []
+    for i, (M, N, K) in enumerate(shapes):
+        X = synth.act_col_outliers(M, K, seed=40 + i)
+        W = synth.weight(N, K, seed=50 + i)
+        qa, sa = fp8.quantize_block(X.to(dev()))
+        (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_F32)
+        ops.append(((qa, sa), (qw, sw), X, W))
+    outs = []
+    for idx in (0, 1, 0, 0):
+        a, w, _, _ = ops[idx]
+        outs.append(fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK))
+    torch.cuda.synchronize()
+    for o in outs[2:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    for idx, o in ((0, outs[0]), (1, outs[1])):
+        _, _, X, W = ops[idx]
+        oqa, osa = oracle.quantize_block(X)
+        oqw, osw = oracle.quantize_weight_block(W, 0)
+        ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_BLOCK)
+        assert_rows_close(o, ref, what=f"shape {shapes[idx]}")
+
+
+def test_small_m_gemm_in_graph_capture():
+    """Under graph capture no workspace is allocated for the capturing stream,
+    so the small-M GEMM runs the plain persistent kernel; every replay (with
+    eager work and synchronizations between them) matches the eager stream-K
+    result within tolerance of the oracle."""
+    say("small-M GEMM captured in a HIP graph, 3 replays")
+    M, N, K = 256, 4096, 4096
+    X = synth.act_col_outliers(M, K, seed=61)
+    W = synth.weight(N, K, seed=62)
+    qa, sa = fp8.quantize_block(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_F32)
+    eager = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK, out=y)
+    oqa, osa = oracle.quantize_block(X)
+    oqw, osw = oracle.quantize_weight_block(W, 0)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_BLOCK)
+    for rep in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_rows_close(y, ref, what=f"replay {rep}")
+        diff = (y.float() - eager.float()).abs().max().item()
+        assert diff <= 1e-2 * eager.float().abs().max().item()
+        _ = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)  # eager work between
+
+
 def test_ragged_m_full_k():
     M, N, K = 8192 + 37, 512, 12288
     say(f"block GEMM ragged {M}x{N}x{K}, sampled rows incl. the last tile")
