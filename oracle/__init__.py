@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.orc_bf16_rne_array.restype = None
         L.orc_add_bf16.argtypes = [u16p, u16p, i64, u16p]
         L.orc_add_bf16.restype = None
+        L.orc_silu_array.argtypes = [u16p, i64, f32p]
+        L.orc_silu_array.restype = None
+        L.orc_swiglu_bf16.argtypes = [u16p, i64, i64, u16p]
+        L.orc_swiglu_bf16.restype = None
         L.orc_scale_f32.argtypes = [ctypes.c_float]
         L.orc_scale_f32.restype = ctypes.c_float
         L.orc_e8m0_exponent.argtypes = [ctypes.c_float]
@@ -299,6 +303,32 @@ def add_rmsnorm_quant(x, r, gamma, eps: float, group_size: int = 0):
     else:
         q, s = quantize_block(rmsnorm_bf16(h, gamma, eps))
     return q, s, h
+
+
+def silu_f32(g) -> np.ndarray:
+    """SiLU of bf16 values (bits or tensor), correctly rounded to fp32."""
+    gb = _bits16(g)
+    out = np.empty(gb.shape, np.float32)
+    lib().orc_silu_array(_p(gb, ctypes.c_uint16), gb.size, _p(out, ctypes.c_float))
+    return out
+
+
+def swiglu_bf16(gu) -> np.ndarray:
+    """bf16 bits [T, I] of bf16_rne(silu(gate) * up), gate = columns [0, I) and
+    up = [I, 2I) of the gate_up output gu [T, 2I]."""
+    b = _bits16(gu)
+    T, I2 = b.shape
+    assert I2 % 2 == 0
+    y = np.empty((T, I2 // 2), np.uint16)
+    lib().orc_swiglu_bf16(_p(b, ctypes.c_uint16), T, I2 // 2, _p(y, ctypes.c_uint16))
+    return y
+
+
+def swiglu_quant(gu):
+    """SwiGLU then 1x128 quantization of its bf16 output: (q, s, y)."""
+    y = swiglu_bf16(gu)
+    q, s = quantize_block(y)
+    return q, s, y
 
 
 # ----------------------------------------------------------------- GEMM --

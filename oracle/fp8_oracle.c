@@ -197,6 +197,42 @@ void orc_add_bf16(const uint16_t* x, const uint16_t* r, int64_t n, uint16_t* h) 
         h[i] = f64_to_bf16_rne((double)orc_bf16_to_f32(x[i]) + (double)orc_bf16_to_f32(r[i]));
 }
 
+/* SiLU of a bf16 value, correctly rounded to fp32: the nearest fp32 to
+ * g * sigmoid(g) = g / (1 + e^-g) (ties cannot occur: the value is
+ * transcendental for g != 0).  Evaluated in fp64 and rounded once; the fp64
+ * error (a few 2^-53 relative) decides the rounding only within that distance
+ * of an fp32 midpoint, and an exhaustive test over every bf16 input against
+ * high-precision decimal arithmetic shows no such case.  Large |g|: e^-g
+ * overflows to +inf for g < -709 and the quotient is -0; for g > 745 it is 0
+ * and the quotient is g. */
+float orc_silu_f32(uint16_t gb) {
+    double g = (double)orc_bf16_to_f32(gb);
+    return (float)(g / (1.0 + exp(-g)));
+}
+
+void orc_silu_array(const uint16_t* g, int64_t n, float* out) {
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) out[i] = orc_silu_f32(g[i]);
+}
+
+/* SwiGLU of the gate_up projection's bf16 output (the MoE chain between the
+ * gate_up and down grouped GEMMs): gu [T, 2I], gate = columns [0, I), up =
+ * columns [I, 2I); y[t][i] = bf16_rne(silu(gate) * up), one fp32 multiply of
+ * the correctly rounded silu and the up value. */
+void orc_swiglu_bf16(const uint16_t* gu, int64_t T, int64_t I, uint16_t* y) {
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        int64_t i;
+        for (i = 0; i < I; ++i) {
+            float sg = orc_silu_f32(gu[t * 2 * I + i]);
+            float u = orc_bf16_to_f32(gu[t * 2 * I + I + i]);
+            y[t * I + i] = orc_f32_to_bf16_rne(sg * u);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scales                                                                   */
 /* ------------------------------------------------------------------------ */

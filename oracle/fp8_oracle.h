@@ -68,6 +68,15 @@ void     orc_bf16_rne_array(const float* v, int64_t n, uint16_t* out);
  * x + r, elementwise over n values. */
 void     orc_add_bf16(const uint16_t* x, const uint16_t* r, int64_t n, uint16_t* h);
 
+/* SiLU of a bf16 value, correctly rounded to fp32 (nearest fp32 to
+ * g / (1 + e^-g)); the array form is for pinning. */
+float    orc_silu_f32(uint16_t g);
+void     orc_silu_array(const uint16_t* g, int64_t n, float* out);
+
+/* SwiGLU between the MoE gate_up and down GEMMs: gu bf16 [T, 2I], gate =
+ * columns [0, I), up = [I, 2I); y bf16 [T, I] = bf16_rne(silu(gate) * up). */
+void     orc_swiglu_bf16(const uint16_t* gu, int64_t T, int64_t I, uint16_t* y);
+
 /* ---- scales ---- */
 
 /* fp32 scale of a group whose largest magnitude is amax: amax / 448 as one
