@@ -293,11 +293,20 @@ def main():
                        vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, sptr)))
     calls.append(("quant_kv_tensor", L.fp8_quantize_tensors, (kvdescs, len(kv_x), sptr)))
     calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
+    # the expert chain: 1x128 quant of the routed rows, gate_up GEMM, SwiGLU +
+    # 1x128 quant of its output, down GEMM
+    mg, md = moe["gate_up"], moe["down"]
+    assert mg["N"] == 2 * md["K"] and mg["T"] == md["T"]
     for which in ("gate_up", "down"):
         m = moe[which]
-        calls.append(("quant_moe", L.fp8_quantize_block,
-                      (vp(m["A"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
-                       vp(m["As"].data_ptr()), sptr)))
+        if which == "gate_up":
+            calls.append(("quant_moe", L.fp8_quantize_block,
+                          (vp(m["A"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
+                           vp(m["As"].data_ptr()), sptr)))
+        else:
+            calls.append(("swiglu_quant_moe", L.fp8_swiglu_quant,
+                          (vp(mg["Y"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
+                           vp(m["As"].data_ptr()), sptr)))
         calls.append(("gemm_moe", L.fp8_grouped_gemm_a8w8_scaled,
                       (vp(m["Aq"].data_ptr()), vp(m["Wq"].data_ptr()), vp(m["As"].data_ptr()),
                        vp(m["Ws"].data_ptr()), vp(m["off"].data_ptr()), vp(m["Y"].data_ptr()),
@@ -335,17 +344,22 @@ def main():
     work["quant_kv_tensor"] = {"bytes": float(sum(3 * t.numel() + 4 for t in kv_x))}
     work["requant_moe"] = {"bytes": 0.0}
     work["quant_moe"] = {"bytes": 0.0}
+    work["swiglu_quant_moe"] = {"bytes": 0.0}
     work["gemm_moe"] = {"flops": 0.0, "bytes": 0.0}
     for m in moe.values():
         E, N, K, T = m["E"], m["N"], m["K"], m["T"]
         work["requant_moe"]["bytes"] += 3 * E * N * K + 4 * (E * N // 128) * (K // 128)
-        work["quant_moe"]["bytes"] += 3 * T * K + 4 * T * (K // 128)
+        if m is moe["gate_up"]:
+            work["quant_moe"]["bytes"] += 3 * T * K + 4 * T * (K // 128)
+        else:  # SwiGLU: reads gate and up (2 x 2 B), writes 1 B per output element
+            work["swiglu_quant_moe"]["bytes"] += 5 * T * K + 4 * T * (K // 128)
         work["gemm_moe"]["flops"] += 2.0 * T * N * K
         work["gemm_moe"]["bytes"] += T * K + E * N * K + 4 * (T * (K // 128) + (E * N // 128)
                                                              * (K // 128)) + 2 * T * N
     launches = {"requant": 1, "rmsnorm_quant": 1, "add_rmsnorm_quant": 1, "quant_token_w": 1,
                 "gemm_row": 1,
-                "requant_moe": 1, "quant_moe": 2, "gemm_moe": 2, "requant_e8m0": 1,
+                "requant_moe": 1, "quant_moe": 1, "swiglu_quant_moe": 1, "gemm_moe": 2,
+                "requant_e8m0": 1,
                 "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes),
                 "quant_kv_tensor": 1}
     for M in Ms:
@@ -419,7 +433,8 @@ def main():
                          "per-token quant of [4096,5120], its residual-add form, per-row weight quant of "
                          "[12288,5120], row-scaled GEMM) and the qwen3-30b-a3b-shaped MoE "
                          "path (expert re-quant, 1x128 quant of 32768 routed rows, grouped "
-                         "GEMMs gate_up 2048->1536 and down 768->2048 over 128 experts), "
+                         "GEMM gate_up 2048->1536, SwiGLU + 1x128 quant, grouped GEMM down "
+                         "768->2048, over 128 experts), "
                          "and the E8M0 variant (the policy re-quantized with E8M0 scales, one "
                          "layer's four linears at M=8192 through E8M0 activation quant and "
                          "the MX-scaled GEMM), and the K/V cache recalibration (per-tensor "

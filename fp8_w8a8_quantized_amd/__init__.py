@@ -22,7 +22,7 @@ __all__ = [
     "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
     "quantize_tensors", "quantize_tensor", "quantize_block_e8m0", "batched_gemm_a8w8_mxscale",
     "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
-    "add_rmsnorm_quant", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
+    "add_rmsnorm_quant", "swiglu_quant", "silu_f32_of_bf16", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
     "status_string", "abi_version",
 ]
 
@@ -82,6 +82,8 @@ def load_library() -> ctypes.CDLL:
         "fp8_batched_gemm_a8w8_mxscale": ([vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
         "fp8_rmsnorm_quant": ([vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_add_rmsnorm_quant": ([vp, vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
+        "fp8_swiglu_quant": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_silu_f32_of_bf16": ([ctypes.c_uint32, i64, vp, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
         "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
@@ -230,6 +232,34 @@ def add_rmsnorm_quant(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tens
            L.fp8_add_rmsnorm_quant(_ptr(q), _ptr(x), _ptr(residual), _ptr(s), _ptr(gamma),
                                    float(eps), M, K, group_size, _stream(x)))
     return q, s
+
+
+def swiglu_quant(gu: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """SwiGLU of the gate_up output gu bf16 [T, 2I] (gate first), then 1x128
+    quantization: codes [T, I] and scales [T, I/128]."""
+    _need(gu, torch.bfloat16, 2, "gu")
+    T, I2 = gu.shape
+    if I2 % 2:
+        raise ValueError("gu must have an even number of columns")
+    I = I2 // 2
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((T, I), dtype=torch.uint8, device=gu.device)
+        s = torch.empty((T, I // 128 if I % 128 == 0 else 0), dtype=torch.float32,
+                        device=gu.device)
+    L = load_library()
+    _check("fp8_swiglu_quant", L.fp8_swiglu_quant(_ptr(gu), T, I, _ptr(q), _ptr(s), _stream(gu)))
+    return q, s
+
+
+def silu_f32_of_bf16(first_bits: int, n: int, device="cuda") -> torch.Tensor:
+    """Diagnostic: the device silu of bf16 bit patterns first_bits .. + n - 1."""
+    out = torch.empty((n,), dtype=torch.float32, device=device)
+    L = load_library()
+    _check("fp8_silu_f32_of_bf16",
+           L.fp8_silu_f32_of_bf16(first_bits, n, _ptr(out), _stream(out)))
+    return out
 
 
 def requantize_weights(weights: Sequence[torch.Tensor], scale_fmt: int = SCALE_F32,

@@ -341,4 +341,23 @@ int fp8_bf16_round_f32_bits(uint64_t first_bits, int64_t n, void* out, void* str
     return launched(fp8k::launch_bf16_bits(first_bits, n, out, as_stream(stream)));
 }
 
+int fp8_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s, void* stream) {
+    if (T < 0) return FP8_ERR_ARG;
+    if (I <= 0 || I % 128 != 0) return FP8_ERR_SHAPE;
+    if (T == 0) return FP8_OK;
+    if (!gu || !q || !s) return FP8_ERR_ARG;
+    if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_swiglu_quant(gu, T, I, q, s, as_stream(stream)));
+}
+
+int fp8_silu_f32_of_bf16(uint32_t first_bits, int64_t n, float* out, void* stream) {
+    if (n < 0 || first_bits > 0xFFFFu || (uint64_t)n > 0x10000u - first_bits) return FP8_ERR_ARG;
+    if (n == 0) return FP8_OK;
+    if (!out) return FP8_ERR_ARG;
+    if (!aligned(out, 4)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_silu_bits(first_bits, n, out, as_stream(stream)));
+}
+
 }  // extern "C"

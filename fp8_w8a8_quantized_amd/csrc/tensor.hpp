@@ -1,8 +1,8 @@
-// Per-tensor dynamic quantization: launch interface between the C-ABI layer
-// and the kernels.  One fp32 scale per tensor (amax / 448); up to
-// kTensMaxDescs tensors per launch sequence, with descriptors passed in kernel
-// arguments.  A tensor of nvec 16-byte vectors covers ceil(nvec / kTensChunk)
-// workgroup chunks.
+// Launch interface of the per-tensor quantizer and of the SwiGLU quantizer.
+// Per-tensor dynamic quantization: one fp32 scale per tensor (amax / 448); up
+// to kTensMaxDescs tensors per launch sequence, with descriptors passed in
+// kernel arguments.  A tensor of nvec 16-byte vectors covers
+// ceil(nvec / kTensChunk) workgroup chunks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,5 +24,11 @@ struct TensBatch {
     int n;
 };
 hipError_t launch_tensor_batch(const TensBatch& batch, int64_t chunks, hipStream_t st);
+
+// SwiGLU + 1x128 quantization of gu bf16 [T, 2I] (I % 128 == 0, T > 0), and
+// the diagnostic silu of bf16 bit patterns.
+hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s,
+                               hipStream_t st);
+hipError_t launch_silu_bits(uint32_t first, int64_t n, float* out, hipStream_t st);
 
 }  // namespace fp8k

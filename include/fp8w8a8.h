@@ -151,6 +151,30 @@ int fp8_add_rmsnorm_quant(void* q_e4m3, const void* x_bf16, void* residual_bf16,
                           const void* gamma_bf16, float eps, int64_t M, int64_t K,
                           int group_size, void* stream);
 
+/*
+ * Fused SwiGLU + 1x128 FP8 quantization: the MoE chain between the gate_up
+ * and down grouped GEMMs (the "FP8-RL" abstract (i): W8A8 linears of MoE
+ * models, whose down projection consumes this activation; the 1x128 groups of
+ * the vLLM DeepSeek V4 page §3).  The pages show no SwiGLU, so it is read as
+ * the usual silu_and_mul:
+ *   gu : bf16 [T, 2I], the gate_up GEMM output; gate = columns [0, I),
+ *        up = columns [I, 2I).
+ *   y  = bf16_rne(silu(gate) * up): silu(g) is the fp32 value nearest to
+ *        g / (1 + e^-g) (correctly rounded), times up in one fp32 multiply.
+ *   q  : E4M3 [T, I] (out)       s : fp32 [T, I/128] (out), y's 1x128 groups
+ *        quantized exactly as fp8_quantize_block would quantize y.
+ *   T < 0 -> FP8_ERR_ARG; I <= 0 or I % 128 != 0 -> FP8_ERR_SHAPE.
+ */
+int fp8_swiglu_quant(const void* gu_bf16, int64_t T, int64_t I, void* q_e4m3, float* s,
+                     void* stream);
+
+/*
+ * Diagnostic (test support): out[i] = silu of the bf16 bit pattern
+ * first_bits + i, as computed inside fp8_swiglu_quant (fp32).  The patterns
+ * must lie in [0, 0x10000); out holds n floats (device, 4-byte aligned).
+ */
+int fp8_silu_f32_of_bf16(uint32_t first_bits, int64_t n, float* out, void* stream);
+
 /* One weight of a re-quantization batch (all pointers device memory). */
 typedef struct {
     const void* w_bf16; /* [N, K] bf16                                          */

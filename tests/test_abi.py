@@ -40,7 +40,8 @@ def test_header_declares_the_calls():
                      "fp8_grouped_gemm_a8w8_scaled", "fp8_abi_version", "fp8_status_string",
                      "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
                      "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
-                     "fp8_quantize_tensors", "fp8_add_rmsnorm_quant"):
+                     "fp8_quantize_tensors", "fp8_add_rmsnorm_quant", "fp8_swiglu_quant",
+                     "fp8_silu_f32_of_bf16"):
         assert required in names
 
 
@@ -115,6 +116,22 @@ def test_add_rmsnorm_quant_validation(L):
     assert add(None, None, None, None, None, 1e-6, 0, 16, 0, None) == OK  # M == 0
     if not _gpu():
         assert add(f, f, g, f, f, 1e-6, 4, 16, 0, None) == DEVICE
+
+
+def test_swiglu_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert L.fp8_swiglu_quant(f, -1, 128, f, f, None) == ARG
+    assert L.fp8_swiglu_quant(f, 4, 100, f, f, None) == SHAPE
+    assert L.fp8_swiglu_quant(f, 4, 0, f, f, None) == SHAPE
+    assert L.fp8_swiglu_quant(f, 4, 128, None, f, None) == ARG
+    assert L.fp8_swiglu_quant(vp(FAKE + 8), 4, 128, f, f, None) == ALIGN
+    assert L.fp8_swiglu_quant(None, 0, 128, None, None, None) == OK
+    assert L.fp8_silu_f32_of_bf16(0xFFFF, 2, f, None) == ARG
+    assert L.fp8_silu_f32_of_bf16(0x10000, 0, f, None) == ARG
+    assert L.fp8_silu_f32_of_bf16(0, 16, vp(FAKE + 2), None) == ALIGN
+    if not _gpu():
+        assert L.fp8_swiglu_quant(f, 4, 128, f, f, None) == DEVICE
 
 
 def test_gemm_validation(L):

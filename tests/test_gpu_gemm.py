@@ -16,7 +16,8 @@ import torch
 import fp8_w8a8_quantized_amd as fp8
 import oracle
 import synth
-from tests.gpu_util import assert_rows_close, dev, ensure_library, host, sample_rows, say
+from tests.gpu_util import (GEMM_ROW_TOL, assert_rows_close, dev, ensure_library, host,
+                            sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -251,6 +252,50 @@ def test_grouped_moe_full_size_sampled(which):
     rows = np.unique(np.array(rows))
     y, ref, rows = _grouped_pipeline(A, W, offsets, rows=rows)
     assert_rows_close(y, ref, rows=rows, what=f"moe {which}")
+
+
+def test_moe_chain_gate_up_swiglu_down_sampled():
+    """The MoE expert chain on the GPU: 1x128 quant of the routed rows ->
+    grouped gate_up GEMM -> SwiGLU + 1x128 quant -> grouped down GEMM.  The
+    oracle runs the same chain from the same bf16 inputs (its gate_up output
+    rounded to bf16).  Tolerance: the sum of the two stages' bounds, 2e-2 of
+    the row max.  Where the two sides' gate_up outputs differ by a bf16 ulp,
+    a SwiGLU code can land one E4M3 step apart, so the second GEMM sees
+    slightly different inputs on top of its own error."""
+    say("MoE chain gate_up -> swiglu_quant -> down, full size, sampled rows")
+    A, Wg, offsets = synth.moe_inputs("gate_up", seed=0)
+    _, Wd, _ = synth.moe_inputs("down", seed=0)
+    E, N1, K1 = Wg.shape
+    _, N2, K2 = Wd.shape
+    assert N1 == 2 * K2
+    off = torch.as_tensor(offsets, dtype=torch.int32, device=dev())
+    qa, sa = fp8.quantize_block(A.to(dev()))
+    (qg, sg), (qd, sd) = fp8.requantize_weights(
+        [Wg.to(dev()).reshape(E * N1, K1), Wd.to(dev()).reshape(E * N2, K2)], fp8.SCALE_F32)
+    y1 = fp8.grouped_gemm_a8w8_scaled((qa, sa), (qg.view(E, N1, K1), sg.view(E, N1 // 128, -1)),
+                                      off)
+    q2, s2 = fp8.swiglu_quant(y1)
+    y2 = fp8.grouped_gemm_a8w8_scaled((q2, s2), (qd.view(E, N2, K2), sd.view(E, N2 // 128, -1)),
+                                      off)
+    rng = np.random.default_rng(14)
+    rows = []
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            rows += [a, int(rng.integers(a, b))]
+    rows = np.unique(np.array(rows))
+    oqa, osa = oracle.quantize_block(A[torch.as_tensor(rows)])
+    expert_of = np.searchsorted(np.asarray(offsets), rows, side="right") - 1
+    ref = np.zeros((rows.size, N2))
+    for e in np.unique(expert_of):
+        sel = np.nonzero(expert_of == e)[0]
+        oqg, osg = oracle.quantize_weight_block(Wg[int(e)], 0)
+        h = oracle.gemm(oqa[sel], oqg, osa[sel], osg, oracle.GRAN_BLOCK)
+        hb = torch.from_numpy(h).float().to(torch.bfloat16)
+        oq2, os2, _ = oracle.swiglu_quant(hb)
+        oqd, osd = oracle.quantize_weight_block(Wd[int(e)], 0)
+        ref[sel] = oracle.gemm(oq2, oqd, os2, osd, oracle.GRAN_BLOCK)
+    assert_rows_close(y2, ref, rows=rows, what="moe chain", tol=2 * GEMM_ROW_TOL)
 
 
 # --------------------------------------------------- E8M0 (MX) scaled GEMM --

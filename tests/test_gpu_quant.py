@@ -253,6 +253,57 @@ def test_add_rmsnorm_quant_cancelling_residual():
     _eq_add_rms(x, -x, gamma, 0)
 
 
+# ------------------------------------------------------- SwiGLU + 1x128 quant --
+def test_silu_all_bf16_patterns():
+    """The device silu equals the oracle's correctly rounded silu on every
+    bf16 input that is not NaN (bit for bit, signed zeros included)."""
+    say("silu of all 65536 bf16 patterns")
+    got = host(fp8.silu_f32_of_bf16(0, 1 << 16, device=dev())).view(np.uint32)
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    keep = ~(((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0))
+    ref = oracle.silu_f32(bits.astype(np.uint16)).view(np.uint32)
+    bad = np.nonzero(keep & (got != ref))[0]
+    assert bad.size == 0, f"{bad.size} patterns differ, first {bad[:8]}"
+
+
+def _eq_swiglu(gu, rows=None):
+    q, s = fp8.swiglu_quant(gu.to(dev()))
+    gh = gu if rows is None else gu[torch.as_tensor(rows)]
+    oq, os_, _ = oracle.swiglu_quant(gh)
+    gq, gs = host(q), host(s)
+    if rows is not None:
+        gq, gs = gq[rows], gs[rows]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("T,I", [(1, 128), (3, 256), (17, 768), (100, 1536), (5, 6144),
+                                 (33, 384)])
+def test_swiglu_quant_shapes(T, I):
+    say(f"swiglu_quant [{T}, 2 x {I}]")
+    gu = synth.normal_bf16((T, 2 * I), seed=T * 7 + I, std=3.0)
+    _eq_swiglu(gu)
+
+
+def test_swiglu_quant_extremes():
+    """Gates far in both tails (silu = g, silu = -0), zero groups and
+    outlier up values in one tensor."""
+    say("swiglu_quant extremes")
+    gu = synth.normal_bf16((8, 2 * 256), seed=77, std=2.0)
+    gu[0, :256] = 300.0      # silu(g) = g
+    gu[1, :256] = -300.0     # silu(g) = -0: a group of signed zeros
+    gu[2, 256:] = 0.0        # up = 0
+    gu[3, 256 + 5] = 4000.0  # one outlier sets its group's scale
+    gu[4, :128] = -80.0      # subnormal silu values
+    _eq_swiglu(gu)
+
+
+def test_swiglu_quant_moe_full_size_sampled():
+    say("swiglu_quant [32768, 2 x 768], sampled rows")
+    gu = synth.normal_bf16((32768, 2 * 768), seed=12, std=2.0)
+    _eq_swiglu(gu, rows=sample_rows(32768, 256, seed=13))
+
+
 def _eq_req(ws, fmt, out=None, block_rows=None):
     res = fp8.requantize_weights([w.to(dev()) if not w.is_cuda else w for w in ws], fmt)
     for i, (w, (q, s)) in enumerate(zip(ws, res)):
