@@ -305,6 +305,22 @@ def add_rmsnorm_quant(x, r, gamma, eps: float, group_size: int = 0):
     return q, s, h
 
 
+def quantize_block_gather(x, row_token):
+    """Token gather + 1x128 quantization (the MoE dispatch before the gate_up
+    GEMM): row t quantizes x[row_token[t]]; an index outside [0, n_src)
+    gives a zero row with zero scales."""
+    xb = _bits16(x)
+    n_src, K = xb.shape
+    idx = np.asarray(row_token, dtype=np.int64)
+    valid = (idx >= 0) & (idx < n_src)
+    q = np.zeros((idx.size, K), np.uint8)
+    s = np.zeros((idx.size, K // 128), np.float32)
+    if valid.any():
+        qv, sv = quantize_block(np.ascontiguousarray(xb[idx[valid]]))
+        q[valid], s[valid] = qv, sv
+    return q, s
+
+
 def silu_f32(g) -> np.ndarray:
     """SiLU of bf16 values (bits or tensor), correctly rounded to fp32."""
     gb = _bits16(g)

@@ -297,3 +297,21 @@ def test_tensor_codes_match_exact_arithmetic_and_zero_tensor():
     z[1, 3] = -0.0
     qz, sz = oracle.quantize_tensor(_bits(z))
     assert float(sz) == 0.0 and qz[1, 3] == 0x80 and np.count_nonzero(qz) == 1
+
+
+def test_gather_quant_indexing():
+    """Token gather + 1x128 quantization: identity index is the plain block
+    quantizer, a permutation permutes its rows, repeated tokens give equal
+    rows, and out-of-range indices give zero rows with zero scales."""
+    x = synth.act_col_outliers(12, 384, seed=31)
+    q0, s0 = oracle.quantize_block(x)
+    q, s = oracle.quantize_block_gather(x, np.arange(12))
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    perm = np.random.default_rng(32).permutation(12)
+    q, s = oracle.quantize_block_gather(x, perm)
+    assert np.array_equal(q, q0[perm]) and np.array_equal(s, s0[perm])
+    idx = np.array([3, 3, -1, 12, 0, 11, 3])
+    q, s = oracle.quantize_block_gather(x, idx)
+    assert np.array_equal(q[0], q0[3]) and np.array_equal(q[1], q0[3]) and np.array_equal(q[6], q0[3])
+    assert np.all(q[2:4] == 0) and np.all(s[2:4] == 0)
+    assert np.array_equal(q[4], q0[0]) and np.array_equal(s[5], s0[11])
