@@ -209,7 +209,10 @@ def main():
     Wrs = torch.empty((RN,), dtype=torch.float32, device=dev)
     Yr = torch.empty((RM, RN), dtype=torch.bfloat16, device=dev)
 
-    # MoE path: routed rows, stacked expert weights, grouped GEMMs
+    # MoE path: token rows + routing, stacked expert weights, grouped GEMMs
+    token_of_row, _ = synth.moe_routing()
+    moe_tok = torch.as_tensor(token_of_row, dtype=torch.int32, device=dev)
+    moe_x = synth.normal_bf16((synth.MOE_TOKENS, synth.MOE_HIDDEN), seed=11, device=dev)
     moe = {}
     for which in ("gate_up", "down"):
         A, Wm, offsets = synth.moe_inputs(which, seed=0, device=dev)
@@ -299,10 +302,10 @@ def main():
     assert mg["N"] == 2 * md["K"] and mg["T"] == md["T"]
     for which in ("gate_up", "down"):
         m = moe[which]
-        if which == "gate_up":
-            calls.append(("quant_moe", L.fp8_quantize_block,
-                          (vp(m["A"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
-                           vp(m["As"].data_ptr()), sptr)))
+        if which == "gate_up":  # dispatch: gather each routed row's token, quantize 1x128
+            calls.append(("quant_gather_moe", L.fp8_quantize_block_gather,
+                          (vp(moe_x.data_ptr()), moe_x.shape[0], m["K"], vp(moe_tok.data_ptr()),
+                           m["T"], vp(m["Aq"].data_ptr()), vp(m["As"].data_ptr()), sptr)))
         else:
             calls.append(("swiglu_quant_moe", L.fp8_swiglu_quant,
                           (vp(mg["Y"].data_ptr()), m["T"], m["K"], vp(m["Aq"].data_ptr()),
@@ -343,14 +346,15 @@ def main():
                                            + (N // 128) * (K // 128) + 2 * MXM * N)
     work["quant_kv_tensor"] = {"bytes": float(sum(3 * t.numel() + 4 for t in kv_x))}
     work["requant_moe"] = {"bytes": 0.0}
-    work["quant_moe"] = {"bytes": 0.0}
+    work["quant_gather_moe"] = {"bytes": 0.0}
     work["swiglu_quant_moe"] = {"bytes": 0.0}
     work["gemm_moe"] = {"flops": 0.0, "bytes": 0.0}
     for m in moe.values():
         E, N, K, T = m["E"], m["N"], m["K"], m["T"]
         work["requant_moe"]["bytes"] += 3 * E * N * K + 4 * (E * N // 128) * (K // 128)
-        if m is moe["gate_up"]:
-            work["quant_moe"]["bytes"] += 3 * T * K + 4 * T * (K // 128)
+        if m is moe["gate_up"]:  # token rows read once, routed codes written
+            work["quant_gather_moe"]["bytes"] += (2 * moe_x.numel() + 4 * T + T * K
+                                                  + 4 * T * (K // 128))
         else:  # SwiGLU: reads gate and up (2 x 2 B), writes 1 B per output element
             work["swiglu_quant_moe"]["bytes"] += 5 * T * K + 4 * T * (K // 128)
         work["gemm_moe"]["flops"] += 2.0 * T * N * K
@@ -358,7 +362,7 @@ def main():
                                                              * (K // 128)) + 2 * T * N
     launches = {"requant": 1, "rmsnorm_quant": 1, "add_rmsnorm_quant": 1, "quant_token_w": 1,
                 "gemm_row": 1,
-                "requant_moe": 1, "quant_moe": 1, "swiglu_quant_moe": 1, "gemm_moe": 2,
+                "requant_moe": 1, "quant_gather_moe": 1, "swiglu_quant_moe": 1, "gemm_moe": 2,
                 "requant_e8m0": 1,
                 "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes),
                 "quant_kv_tensor": 1}
@@ -432,7 +436,7 @@ def main():
                          "and M=256; plus once per step the per-token path (RMSNorm + "
                          "per-token quant of [4096,5120], its residual-add form, per-row weight quant of "
                          "[12288,5120], row-scaled GEMM) and the qwen3-30b-a3b-shaped MoE "
-                         "path (expert re-quant, 1x128 quant of 32768 routed rows, grouped "
+                         "path (expert re-quant, token gather + 1x128 quant of 32768 routed rows, grouped "
                          "GEMM gate_up 2048->1536, SwiGLU + 1x128 quant, grouped GEMM down "
                          "768->2048, over 128 experts), "
                          "and the E8M0 variant (the policy re-quantized with E8M0 scales, one "

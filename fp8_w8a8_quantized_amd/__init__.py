@@ -22,7 +22,7 @@ __all__ = [
     "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
     "quantize_tensors", "quantize_tensor", "quantize_block_e8m0", "batched_gemm_a8w8_mxscale",
     "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
-    "add_rmsnorm_quant", "swiglu_quant", "silu_f32_of_bf16", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
+    "add_rmsnorm_quant", "swiglu_quant", "quantize_block_gather", "silu_f32_of_bf16", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
     "status_string", "abi_version",
 ]
 
@@ -83,6 +83,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_rmsnorm_quant": ([vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_add_rmsnorm_quant": ([vp, vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_swiglu_quant": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_quantize_block_gather": ([vp, i64, i64, vp, i64, vp, vp, vp], i32),
         "fp8_silu_f32_of_bf16": ([ctypes.c_uint32, i64, vp, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
@@ -250,6 +251,27 @@ def swiglu_quant(gu: torch.Tensor, out=None) -> Tuple[torch.Tensor, torch.Tensor
                         device=gu.device)
     L = load_library()
     _check("fp8_swiglu_quant", L.fp8_swiglu_quant(_ptr(gu), T, I, _ptr(q), _ptr(s), _stream(gu)))
+    return q, s
+
+
+def quantize_block_gather(x: torch.Tensor, row_token: torch.Tensor, out=None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token gather + 1x128 quantization: row t of the result quantizes
+    x[row_token[t]] (x bf16 [n_src, K], row_token int32 [T] on the device)."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(row_token, torch.int32, 1, "row_token")
+    n_src, K = x.shape
+    T = row_token.shape[0]
+    if out is not None:
+        q, s = _as_u8(out[0]), out[1]
+    else:
+        q = torch.empty((T, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((T, K // 128 if K % 128 == 0 else 0), dtype=torch.float32,
+                        device=x.device)
+    L = load_library()
+    _check("fp8_quantize_block_gather",
+           L.fp8_quantize_block_gather(_ptr(x), n_src, K, _ptr(row_token), T, _ptr(q), _ptr(s),
+                                       _stream(x)))
     return q, s
 
 

@@ -351,6 +351,19 @@ int fp8_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s, vo
     return launched(fp8k::launch_swiglu_quant(gu, T, I, q, s, as_stream(stream)));
 }
 
+int fp8_quantize_block_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,
+                              int64_t T, void* q, float* s, void* stream) {
+    if (T < 0 || n_src < 0 || n_src > INT32_MAX) return FP8_ERR_ARG;
+    if (K <= 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (T == 0) return FP8_OK;
+    if (!row_token || !q || !s || (n_src > 0 && !x)) return FP8_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(row_token, 4) || !aligned(q, 16) || !aligned(s, 4))
+        return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(
+        fp8k::launch_quant_gather(x, n_src, K, row_token, T, q, s, as_stream(stream)));
+}
+
 int fp8_silu_f32_of_bf16(uint32_t first_bits, int64_t n, float* out, void* stream) {
     if (n < 0 || first_bits > 0xFFFFu || (uint64_t)n > 0x10000u - first_bits) return FP8_ERR_ARG;
     if (n == 0) return FP8_OK;

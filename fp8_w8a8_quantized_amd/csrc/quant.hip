@@ -532,6 +532,46 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Token gather + 1x128 quantization (the MoE dispatch before the gate_up
+// GEMM): output row t is the 1x128 quantization of x[row_token[t]].  The
+// layout is k_quant_block's (16 lanes x 8 elements per group, 4 groups per
+// wave step); each group looks up its source row first.  An index outside
+// [0, n_src) yields a zero row (codes 0, scale 0) and reads nothing.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void k_quant_gather(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ row_token,
+                                                      uint2* __restrict__ q,
+                                                      float* __restrict__ s, int64_t G,
+                                                      int64_t GK, int64_t n_src) {
+    const int lane = threadIdx.x & 63, li = lane & 15;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t chunk0 = wave * U;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+        v[u] = uint4{0u, 0u, 0u, 0u};
+        if (gid < G) {
+            const int64_t t = gid / GK, j = gid - t * GK;
+            const int64_t src = row_token[t];
+            if (src >= 0 && src < n_src) v[u] = x[src * GK * 16 + j * 16 + li];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+        float f[8];
+        unpack8(v[u], f);
+        const GroupDiv g = group_div(max_16lanes(amax8(f)));
+        if (gid < G) {
+            q[gid * 16 + li] = encode8(f, g);
+            if (li == 0) s[gid] = g.s;
+        }
+    }
+}
+
 // Diagnostic: silu of the bf16 bit patterns first .. first + n - 1, as fp32.
 __global__ __launch_bounds__(256) void k_silu_bits(uint32_t first, int64_t n,
                                                    float* __restrict__ out) {
@@ -633,6 +673,15 @@ hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, fl
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
     return launch(k_swiglu_quant<U>, (waves + 3) / 4, st, static_cast<const uint4*>(gu),
                   static_cast<uint2*>(q), s, G, GI);
+}
+
+hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,
+                               int64_t T, void* q, float* s, hipStream_t st) {
+    constexpr int U = 4;
+    const int64_t GK = K / 128, G = T * GK;
+    const int64_t waves = (G + 4 * U - 1) / (4 * U);
+    return launch(k_quant_gather<U>, (waves + 3) / 4, st, static_cast<const uint4*>(x), row_token,
+                  static_cast<uint2*>(q), s, G, GK, n_src);
 }
 
 hipError_t launch_silu_bits(uint32_t first, int64_t n, float* out, hipStream_t st) {

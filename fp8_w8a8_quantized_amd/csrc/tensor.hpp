@@ -1,4 +1,4 @@
-// Launch interface of the per-tensor quantizer and of the SwiGLU quantizer.
+// Launch interface of the per-tensor, SwiGLU and token-gather quantizers.
 // Per-tensor dynamic quantization: one fp32 scale per tensor (amax / 448); up
 // to kTensMaxDescs tensors per launch sequence, with descriptors passed in
 // kernel arguments.  A tensor of nvec 16-byte vectors covers
@@ -30,5 +30,10 @@ hipError_t launch_tensor_batch(const TensBatch& batch, int64_t chunks, hipStream
 hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s,
                                hipStream_t st);
 hipError_t launch_silu_bits(uint32_t first, int64_t n, float* out, hipStream_t st);
+
+// Token gather + 1x128 quantization: q[t] = quant(x[row_token[t]]), x bf16
+// [n_src, K] (K % 128 == 0, T > 0).
+hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,
+                               int64_t T, void* q, float* s, hipStream_t st);
 
 }  // namespace fp8k

@@ -169,6 +169,22 @@ int fp8_swiglu_quant(const void* gu_bf16, int64_t T, int64_t I, void* q_e4m3, fl
                      void* stream);
 
 /*
+ * Token gather + 1x128 FP8 quantization: the MoE dispatch that lays the
+ * routed copies of each token out in expert order before the grouped gate_up
+ * GEMM ("FP8-RL" abstract (i): W8A8 linears of MoE models; 1x128 groups as in
+ * fp8_quantize_block).
+ *   x         : bf16 [n_src, K], one row per token   (K % 128 == 0)
+ *   row_token : int32 [T], device; output row t takes token row_token[t]
+ *   q         : E4M3 [T, K] (out)     s : fp32 [T, K/128] (out)
+ *   q[t], s[t] are exactly fp8_quantize_block of the row x[row_token[t]].
+ *   An index outside [0, n_src) gives a zero row (codes 0, scales 0) and reads
+ *   nothing.  T < 0, n_src < 0 or n_src > INT32_MAX -> FP8_ERR_ARG.
+ */
+int fp8_quantize_block_gather(const void* x_bf16, int64_t n_src, int64_t K,
+                              const int32_t* row_token, int64_t T, void* q_e4m3, float* s,
+                              void* stream);
+
+/*
  * Diagnostic (test support): out[i] = silu of the bf16 bit pattern
  * first_bits + i, as computed inside fp8_swiglu_quant (fp32).  The patterns
  * must lie in [0, 0x10000); out holds n floats (device, 4-byte aligned).

@@ -41,7 +41,7 @@ def test_header_declares_the_calls():
                      "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
                      "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
                      "fp8_quantize_tensors", "fp8_add_rmsnorm_quant", "fp8_swiglu_quant",
-                     "fp8_silu_f32_of_bf16"):
+                     "fp8_silu_f32_of_bf16", "fp8_quantize_block_gather"):
         assert required in names
 
 
@@ -132,6 +132,22 @@ def test_swiglu_validation(L):
     assert L.fp8_silu_f32_of_bf16(0, 16, vp(FAKE + 2), None) == ALIGN
     if not _gpu():
         assert L.fp8_swiglu_quant(f, 4, 128, f, f, None) == DEVICE
+
+
+def test_gather_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    g = L.fp8_quantize_block_gather
+    assert g(f, 4, 128, f, -1, f, f, None) == ARG
+    assert g(f, -1, 128, f, 4, f, f, None) == ARG
+    assert g(f, 2 ** 31, 128, f, 4, f, f, None) == ARG
+    assert g(f, 4, 100, f, 4, f, f, None) == SHAPE
+    assert g(f, 4, 128, None, 4, f, f, None) == ARG
+    assert g(None, 4, 128, f, 4, f, f, None) == ARG
+    assert g(f, 4, 128, vp(FAKE + 2), 4, f, f, None) == ALIGN
+    assert g(None, 0, 128, None, 0, None, None, None) == OK
+    if not _gpu():
+        assert g(f, 4, 128, f, 4, f, f, None) == DEVICE
 
 
 def test_gemm_validation(L):

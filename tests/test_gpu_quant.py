@@ -304,6 +304,39 @@ def test_swiglu_quant_moe_full_size_sampled():
     _eq_swiglu(gu, rows=sample_rows(32768, 256, seed=13))
 
 
+# ------------------------------------------------- token gather + 1x128 quant --
+def _eq_gather(x, idx, rows=None):
+    q, s = fp8.quantize_block_gather(x.to(dev()), torch.as_tensor(idx, dtype=torch.int32,
+                                                                   device=dev()))
+    sel = np.arange(len(idx)) if rows is None else rows
+    oq, os_ = oracle.quantize_block_gather(x, np.asarray(idx)[sel])
+    gq, gs = host(q)[sel], host(s)[sel]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("n_src,K,T", [(1, 128, 1), (7, 256, 30), (100, 2048, 333),
+                                       (64, 5120, 17)])
+def test_gather_quant_shapes(n_src, K, T):
+    say(f"quantize_block_gather x [{n_src}, {K}] -> {T} rows")
+    x = synth.act_col_outliers(n_src, K, seed=n_src + K + T)
+    idx = np.random.default_rng(T).integers(0, n_src, T)
+    _eq_gather(x, idx)
+
+
+def test_gather_quant_out_of_range_rows_are_zero():
+    say("quantize_block_gather with indices outside the token range")
+    x = synth.act_col_outliers(10, 256, seed=90)
+    _eq_gather(x, np.array([0, -1, 9, 10, 2 ** 31 - 1, -2 ** 31, 5, 5]))
+
+
+def test_gather_quant_moe_dispatch_sampled():
+    say("quantize_block_gather: 4096 tokens x 2048 -> 32768 routed rows, sampled")
+    token_of_row, _ = synth.moe_routing()
+    x = synth.normal_bf16((synth.MOE_TOKENS, synth.MOE_HIDDEN), seed=11)
+    _eq_gather(x, token_of_row, rows=sample_rows(token_of_row.size, 256, seed=15))
+
+
 def _eq_req(ws, fmt, out=None, block_rows=None):
     res = fp8.requantize_weights([w.to(dev()) if not w.is_cuda else w for w in ws], fmt)
     for i, (w, (q, s)) in enumerate(zip(ws, res)):
