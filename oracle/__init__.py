@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.orc_silu_array.restype = None
         L.orc_swiglu_bf16.argtypes = [u16p, i64, i64, u16p]
         L.orc_swiglu_bf16.restype = None
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.orc_inverse_rope_bf16.argtypes = [u16p, i64p, f32p, f32p, i64, i64, i64, i64, i64,
+                                            u16p]
+        L.orc_inverse_rope_bf16.restype = None
         L.orc_scale_f32.argtypes = [ctypes.c_float]
         L.orc_scale_f32.restype = ctypes.c_float
         L.orc_e8m0_exponent.argtypes = [ctypes.c_float]
@@ -319,6 +323,33 @@ def quantize_block_gather(x, row_token):
         qv, sv = quantize_block(np.ascontiguousarray(xb[idx[valid]]))
         q[valid], s[valid] = qv, sv
     return q, s
+
+
+def inverse_rope_bf16(o, positions, cos_cache, sin_cache, rope_dim: int) -> np.ndarray:
+    """bf16 bits [T, H, D] of the inverse RoPE of o (bf16 [T, H, D]) with the
+    rotary part in the last rope_dim dims of each head (interleaved pairs)."""
+    ob = _bits16(o)
+    T, H, D = ob.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    c = np.ascontiguousarray(cos_cache, dtype=np.float32)
+    s = np.ascontiguousarray(sin_cache, dtype=np.float32)
+    P, half = c.shape
+    assert half * 2 == rope_dim and s.shape == c.shape and pos.shape == (T,)
+    z = np.empty((T, H, D), np.uint16)
+    lib().orc_inverse_rope_bf16(_p(ob, ctypes.c_uint16), _p(pos, ctypes.c_int64),
+                                _p(c, ctypes.c_float), _p(s, ctypes.c_float), T, H, D,
+                                rope_dim, P, _p(z, ctypes.c_uint16))
+    return z
+
+
+def inverse_rope_group_quant(o, positions, cos_cache, sin_cache, rope_dim: int):
+    """Inverse RoPE, then 1x128 E8M0 quantization of each token's flattened
+    [H * D] row (feeding the batched MX GEMM): (q [T, H*D], s bytes
+    [T, H*D/128], z bits [T, H, D])."""
+    z = inverse_rope_bf16(o, positions, cos_cache, sin_cache, rope_dim)
+    T = z.shape[0]
+    q, s = quantize_block_e8m0(np.ascontiguousarray(z.reshape(T, -1)))
+    return q, s, z
 
 
 def silu_f32(g) -> np.ndarray:

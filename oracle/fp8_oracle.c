@@ -233,6 +233,50 @@ void orc_swiglu_bf16(const uint16_t* gu, int64_t T, int64_t I, uint16_t* y) {
     }
 }
 
+/* Inverse RoPE ahead of the output projection (the vLLM DeepSeek V4 page,
+ * section 3: inverse_rope_group_quant(o, positions, cos, sin, ...)).  o is
+ * bf16 [T][H][D]; the last R dims of each head carry the rotary part, as
+ * interleaved pairs (y0, y1) = dims (D-R+2i, D-R+2i+1) with angle index i;
+ * cos/sin are fp32 [P][R/2] rows indexed by the token's position.  The
+ * inverse rotation by that angle is
+ *     x0 = y0*c + y1*s,   x1 = y1*c - y0*s,
+ * each product and the sum one fp32 operation, then rounded to bf16.  Other
+ * dims pass through.  A position outside [0, P) gives a zero row. */
+void orc_inverse_rope_bf16(const uint16_t* o, const int64_t* pos, const float* cosc,
+                           const float* sinc, int64_t T, int64_t H, int64_t D, int64_t R,
+                           int64_t P, uint16_t* z) {
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        int64_t h, d, p = pos[t];
+        for (h = 0; h < H; ++h) {
+            const uint16_t* yr = o + (t * H + h) * D;
+            uint16_t* zr = z + (t * H + h) * D;
+            for (d = 0; d < D; ++d) {
+                if (p < 0 || p >= P) {
+                    zr[d] = 0;
+                } else if (d < D - R) {
+                    zr[d] = yr[d];
+                } else {
+                    int64_t r = d - (D - R), i = r / 2;
+                    float c = cosc[p * (R / 2) + i], s = sinc[p * (R / 2) + i];
+                    float v;
+                    if (r % 2 == 0) {
+                        float y0 = orc_bf16_to_f32(yr[d]), y1 = orc_bf16_to_f32(yr[d + 1]);
+                        float a = y0 * c, b = y1 * s;
+                        v = a + b;
+                    } else {
+                        float y0 = orc_bf16_to_f32(yr[d - 1]), y1 = orc_bf16_to_f32(yr[d]);
+                        float a = y1 * c, b = y0 * s;
+                        v = a - b;
+                    }
+                    zr[d] = orc_f32_to_bf16_rne(v);
+                }
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scales                                                                   */
 /* ------------------------------------------------------------------------ */

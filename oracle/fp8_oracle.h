@@ -77,6 +77,14 @@ void     orc_silu_array(const uint16_t* g, int64_t n, float* out);
  * columns [0, I), up = [I, 2I); y bf16 [T, I] = bf16_rne(silu(gate) * up). */
 void     orc_swiglu_bf16(const uint16_t* gu, int64_t T, int64_t I, uint16_t* y);
 
+/* Inverse RoPE (vLLM DeepSeek V4 page §3): o bf16 [T][H][D], rotary part =
+ * last R dims of each head as interleaved pairs; cos/sin fp32 [P][R/2];
+ * x0 = y0*c + y1*s, x1 = y1*c - y0*s in fp32, rounded to bf16; a position
+ * outside [0, P) gives a zero row. */
+void     orc_inverse_rope_bf16(const uint16_t* o, const int64_t* pos, const float* cosc,
+                               const float* sinc, int64_t T, int64_t H, int64_t D, int64_t R,
+                               int64_t P, uint16_t* z);
+
 /* ---- scales ---- */
 
 /* fp32 scale of a group whose largest magnitude is amax: amax / 448 as one

@@ -29,6 +29,11 @@ Workload recipes (sizes and distributions of the pages' configurations):
                   (expert, token); X [4096, 2048] ~ N(0, 1) gathered to
                   [32768, 2048]; down-projection input [32768, 768] ~ N(0, 1);
                   W gate_up [128, 1536, 2048], down [128, 2048, 768] ~ N(0, 0.02).
+  inverse RoPE:   o [T, 64 heads, 128] ~ N(0, 1) bf16 with the rotary part in
+                  the last 64 dims of each head; positions = token index within
+                  sequences of 2048; cos/sin fp32 [8192, 32] of angle
+                  p * 10000^(-2i/64), computed in fp64 and rounded once
+                  (shapes are synthetic: the pages give none).
   KV cache:       per layer K and V [8192 tokens, 8 KV heads x 128] (the
                   Qwen3-8B-shaped attention of the dense linears); K ~ N(0, 1)
                   with one whole column x50 (an outlier channel), V ~ N(0, 1);
@@ -54,6 +59,8 @@ MOE_TOKENS, MOE_EXPERTS, MOE_TOPK = 4096, 128, 8
 MOE_HIDDEN, MOE_INTER = 2048, 768
 
 KV_TOKENS, KV_HEADS, KV_HEAD_DIM = 8192, 8, 128
+
+ROPE_HEADS, ROPE_HEAD_DIM, ROPE_DIM, ROPE_GROUPS, ROPE_MAX_POS, ROPE_SEQ = 64, 128, 64, 8, 8192, 2048
 
 
 def _is_dev(device) -> bool:
@@ -185,3 +192,19 @@ def kv_cache(layer: int, seed: int = 0, tokens: int = KV_TOKENS, device="cpu"):
     k = act_col_outliers(tokens, width, seed + 2 * layer, device=device)
     v = normal_bf16((tokens, width), seed + 2 * layer + 1, 1.0, device)
     return k, v
+
+
+def rope_cache(max_pos: int = ROPE_MAX_POS, rope_dim: int = ROPE_DIM, base: float = 10000.0):
+    """cos and sin fp32 [max_pos, rope_dim / 2] of angle p * base^(-2i/rope_dim)."""
+    inv = base ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def rope_inputs(tokens: int, seed: int = 0, heads: int = ROPE_HEADS, head_dim: int = ROPE_HEAD_DIM,
+                seq: int = ROPE_SEQ, device="cpu"):
+    """o bf16 [tokens, heads, head_dim] ~ N(0, 1) and int64 positions (token
+    index within consecutive sequences of `seq`)."""
+    o = normal_bf16((tokens, heads, head_dim), seed, 1.0, device)
+    pos = np.arange(tokens, dtype=np.int64) % seq
+    return o, pos
