@@ -252,6 +252,22 @@ def main():
         kvdescs[i] = fp8._TensorDesc(t.data_ptr(), kv_q[i].data_ptr(), kv_s[i].data_ptr(),
                                      t.numel())
 
+    # output projection of the DeepSeek-V4-style attention: inverse RoPE + E8M0
+    # group quant of o, batched MX GEMM over 8 head groups
+    OT, OG, ON = synth.ROPE_TOKENS, synth.ROPE_GROUPS, synth.ROPE_OUT
+    OKG = synth.ROPE_HEADS * synth.ROPE_HEAD_DIM // OG
+    ro, rpos = synth.rope_inputs(OT, seed=7, device=dev)
+    rpos = torch.as_tensor(rpos, device=dev)
+    rcos, rsin = (torch.as_tensor(a, device=dev) for a in synth.rope_cache())
+    rW = synth.normal_bf16((OG * ON, OKG), seed=8, std=0.02, device=dev)
+    rWq = torch.empty_like(rW, dtype=torch.uint8)
+    rWs = torch.empty((OG * ON // 128, OKG // 128), dtype=torch.uint8, device=dev)
+    rdesc = (fp8._WeightDesc * 1)()
+    rdesc[0] = fp8._WeightDesc(rW.data_ptr(), rWq.data_ptr(), rWs.data_ptr(), OG * ON, OKG)
+    rq = torch.empty((OT, OG * OKG), dtype=torch.uint8, device=dev)
+    rs = torch.empty((OT, OG * OKG // 128), dtype=torch.uint8, device=dev)
+    rY = torch.empty((OT, OG, ON), dtype=torch.bfloat16, device=dev)
+
     mdescs = (fp8._WeightDesc * 2)()
     for i, which in enumerate(("gate_up", "down")):
         m = moe[which]
@@ -295,6 +311,15 @@ def main():
                       (vp(Xq8[j].data_ptr()), vp(Wq8[j].data_ptr()), vp(Xs8[j].data_ptr()),
                        vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, sptr)))
     calls.append(("quant_kv_tensor", L.fp8_quantize_tensors, (kvdescs, len(kv_x), sptr)))
+    calls.append(("requant_e8m0_wo", L.fp8_requantize_weights, (rdesc, 1, fp8.SCALE_E8M0, sptr)))
+    calls.append(("rope_quant_m8192", L.fp8_inverse_rope_group_quant,
+                  (vp(ro.data_ptr()), vp(rpos.data_ptr()), vp(rcos.data_ptr()),
+                   vp(rsin.data_ptr()), OT, synth.ROPE_HEADS, synth.ROPE_HEAD_DIM,
+                   synth.ROPE_DIM, rcos.shape[0], OG, vp(rq.data_ptr()), vp(rs.data_ptr()),
+                   sptr)))
+    calls.append(("gemm_mx_wo_m8192", L.fp8_batched_gemm_a8w8_mxscale,
+                  (vp(rq.data_ptr()), vp(rWq.data_ptr()), vp(rs.data_ptr()), vp(rWs.data_ptr()),
+                   vp(rY.data_ptr()), OG, OT, ON, OKG, sptr)))
     calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
     # the expert chain: 1x128 quant of the routed rows, gate_up GEMM, SwiGLU +
     # 1x128 quant of its output, down GEMM
@@ -345,6 +370,15 @@ def main():
         work["gemm_mx_m8192"]["bytes"] += (MXM * K + N * K + MXM * (K // 128)
                                            + (N // 128) * (K // 128) + 2 * MXM * N)
     work["quant_kv_tensor"] = {"bytes": float(sum(3 * t.numel() + 4 for t in kv_x))}
+    work["requant_e8m0_wo"] = {"bytes": float(3 * OG * ON * OKG
+                                              + (OG * ON // 128) * (OKG // 128))}
+    rope_elems = OT * OG * OKG
+    work["rope_quant_m8192"] = {"bytes": float(3 * rope_elems + rope_elems // 128 + 8 * OT
+                                               + OT * synth.ROPE_DIM * 4)}
+    work["gemm_mx_wo_m8192"] = {"flops": 2.0 * OT * OG * ON * OKG,
+                                "bytes": float(rope_elems + OG * ON * OKG + rope_elems // 128
+                                               + (OG * ON // 128) * (OKG // 128)
+                                               + 2 * OT * OG * ON)}
     work["requant_moe"] = {"bytes": 0.0}
     work["quant_gather_moe"] = {"bytes": 0.0}
     work["swiglu_quant_moe"] = {"bytes": 0.0}
@@ -365,7 +399,8 @@ def main():
                 "requant_moe": 1, "quant_gather_moe": 1, "swiglu_quant_moe": 1, "gemm_moe": 2,
                 "requant_e8m0": 1,
                 "quant_e8m0_m8192": len(shapes), "gemm_mx_m8192": len(shapes),
-                "quant_kv_tensor": 1}
+                "quant_kv_tensor": 1, "requant_e8m0_wo": 1, "rope_quant_m8192": 1,
+                "gemm_mx_wo_m8192": 1}
     for M in Ms:
         launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
 
@@ -441,12 +476,18 @@ def main():
                          "768->2048, over 128 experts), "
                          "and the E8M0 variant (the policy re-quantized with E8M0 scales, one "
                          "layer's four linears at M=8192 through E8M0 activation quant and "
-                         "the MX-scaled GEMM), and the K/V cache recalibration (per-tensor "
-                         "quant of every layer's K and V, [8192, 1024] each)"),
+                         "the MX-scaled GEMM), the K/V cache recalibration (per-tensor "
+                         "quant of every layer's K and V, [8192, 1024] each), and an "
+                         "attention output projection (inverse RoPE + E8M0 group quant of "
+                         "o [8192, 64 heads, 128], batched MX GEMM over 8 head groups "
+                         "1024->1024, its weight re-quantized with E8M0 scales)"),
             "layers": layers, "M": list(Ms),
             "linears": {name: {"N": N, "K": K} for name, (N, K) in shapes},
             "per_token": {"M": RM, "K": RK, "N": RN},
             "kv_cache": {"tensors": len(kv_x), "shape": list(kv_x[0].shape)},
+            "out_proj_rope": {"tokens": OT, "heads": synth.ROPE_HEADS,
+                              "head_dim": synth.ROPE_HEAD_DIM, "rope_dim": synth.ROPE_DIM,
+                              "groups": OG, "N_per_group": ON, "K_per_group": OKG},
             "moe": {"experts": moe["gate_up"]["E"], "rows": moe["gate_up"]["T"],
                     "gate_up": {"N": moe["gate_up"]["N"], "K": moe["gate_up"]["K"]},
                     "down": {"N": moe["down"]["N"], "K": moe["down"]["K"]}},

@@ -22,7 +22,8 @@ __all__ = [
     "Fp8Error", "Fp8LibraryMissing", "GRAN_BLOCK", "GRAN_ROW", "SCALE_F32", "SCALE_E8M0",
     "quantize_tensors", "quantize_tensor", "quantize_block_e8m0", "batched_gemm_a8w8_mxscale",
     "library_path", "load_library", "quantize_block", "quantize_token", "rmsnorm_quant",
-    "add_rmsnorm_quant", "swiglu_quant", "quantize_block_gather", "silu_f32_of_bf16", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
+    "add_rmsnorm_quant", "swiglu_quant", "quantize_block_gather", "inverse_rope_group_quant",
+    "silu_f32_of_bf16", "requantize_weights", "gemm_a8w8_scaled", "grouped_gemm_a8w8_scaled", "encode_f32_bits",
     "status_string", "abi_version",
 ]
 
@@ -84,6 +85,8 @@ def load_library() -> ctypes.CDLL:
         "fp8_add_rmsnorm_quant": ([vp, vp, vp, vp, vp, f32, i64, i64, i32, vp], i32),
         "fp8_swiglu_quant": ([vp, i64, i64, vp, vp, vp], i32),
         "fp8_quantize_block_gather": ([vp, i64, i64, vp, i64, vp, vp, vp], i32),
+        "fp8_inverse_rope_group_quant": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                          vp], i32),
         "fp8_silu_f32_of_bf16": ([ctypes.c_uint32, i64, vp, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
@@ -272,6 +275,36 @@ def quantize_block_gather(x: torch.Tensor, row_token: torch.Tensor, out=None
     _check("fp8_quantize_block_gather",
            L.fp8_quantize_block_gather(_ptr(x), n_src, K, _ptr(row_token), T, _ptr(q), _ptr(s),
                                        _stream(x)))
+    return q, s
+
+
+def inverse_rope_group_quant(o: torch.Tensor, positions: torch.Tensor, cos_cache: torch.Tensor,
+                             sin_cache: torch.Tensor, num_groups: int, out=None
+                             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Inverse RoPE of o bf16 [T, H, D] (rotary part: the last 2 * cos_cache.shape[1]
+    dims of each head, interleaved pairs), then 1x128 E8M0 quantization.
+    Returns (codes [T, G, H*D/G], E8M0 bytes [T, G, H*D/(128 G)]) with G =
+    num_groups, the token-major layout batched_gemm_a8w8_mxscale takes."""
+    _need(o, torch.bfloat16, 3, "o")
+    _need(positions, torch.int64, 1, "positions")
+    _need(cos_cache, torch.float32, 2, "cos_cache")
+    _need(sin_cache, torch.float32, 2, "sin_cache")
+    T, H, D = o.shape
+    P, half = cos_cache.shape
+    if tuple(sin_cache.shape) != (P, half) or positions.shape[0] != T:
+        raise ValueError("positions / cos / sin shapes disagree with o")
+    G = int(num_groups)
+    Kg = H * D // G if G > 0 and (H * D) % G == 0 else 0
+    if out is not None:
+        q, s = _as_u8(out[0]), _as_u8(out[1])
+    else:
+        q = torch.empty((T, G, Kg), dtype=torch.uint8, device=o.device)
+        s = torch.empty((T, G, Kg // 128), dtype=torch.uint8, device=o.device)
+    L = load_library()
+    _check("fp8_inverse_rope_group_quant",
+           L.fp8_inverse_rope_group_quant(_ptr(o), _ptr(positions), _ptr(cos_cache),
+                                          _ptr(sin_cache), T, H, D, 2 * half, P, G, _ptr(q),
+                                          _ptr(s), _stream(o)))
     return q, s
 
 

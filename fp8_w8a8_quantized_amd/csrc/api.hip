@@ -364,6 +364,29 @@ int fp8_quantize_block_gather(const void* x, int64_t n_src, int64_t K, const int
         fp8k::launch_quant_gather(x, n_src, K, row_token, T, q, s, as_stream(stream)));
 }
 
+int fp8_inverse_rope_group_quant(const void* o, const int64_t* positions, const float* cos_cache,
+                                 const float* sin_cache, int64_t T, int64_t H, int64_t D,
+                                 int64_t rope_dim, int64_t max_pos, int64_t num_groups, void* q,
+                                 uint8_t* s, void* stream) {
+    if (T < 0 || rope_dim < 0 || rope_dim % 2 != 0 || max_pos < 0 || num_groups <= 0)
+        return FP8_ERR_ARG;
+    if (H <= 0 || D <= 0 || D % 8 != 0 || rope_dim > D || H % num_groups != 0 ||
+        D > INT32_MAX || H > (INT32_MAX - 1) / D)  // a row's offsets fit in int
+        return FP8_ERR_SHAPE;
+    if ((H / num_groups) * D % 128 != 0) return FP8_ERR_SHAPE;
+    if (rope_dim > 0 && max_pos == 0) return FP8_ERR_ARG;
+    if (max_pos > INT64_MAX / (rope_dim / 2 + 1)) return FP8_ERR_ARG;
+    if (T == 0) return FP8_OK;
+    if (!o || !positions || !q || !s || (rope_dim > 0 && (!cos_cache || !sin_cache)))
+        return FP8_ERR_ARG;
+    if (!aligned(o, 16) || !aligned(q, 16) || !aligned(positions, 8) || !aligned(cos_cache, 4) ||
+        !aligned(sin_cache, 4))
+        return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_inv_rope_quant(o, positions, cos_cache, sin_cache, T, H, D,
+                                                rope_dim, max_pos, q, s, as_stream(stream)));
+}
+
 int fp8_silu_f32_of_bf16(uint32_t first_bits, int64_t n, float* out, void* stream) {
     if (n < 0 || first_bits > 0xFFFFu || (uint64_t)n > 0x10000u - first_bits) return FP8_ERR_ARG;
     if (n == 0) return FP8_OK;

@@ -572,6 +572,115 @@ __global__ __launch_bounds__(256) void k_quant_gather(const uint4* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Inverse RoPE + 1x128 E8M0 quantization (the DeepSeek V4 output projection's
+// pre-op, feeding the batched MX GEMM).  o bf16 [T][H][D] (D % 8 == 0): the
+// last R dims of each head are interleaved pairs (y0, y1) with angle index i;
+// cos/sin fp32 [P][R/2].  x0 = y0*c + y1*s and x1 = y1*c - y0*s as single
+// fp32 operations (the library is built without FMA contraction), rounded to
+// bf16; other dims pass through.  Each token's flattened [H*D] row is then
+// quantized in 1x128 groups with E8M0 scales, as k_quant_block<U, 1> does.
+// A lane's 8 elements lie in one head; a position outside [0, P) gives a
+// zero row and reads nothing from the caches.
+// ---------------------------------------------------------------------------
+// IDX: the index type of groups (32-bit when the group count fits).  VEC:
+// R % 8 == 0 and (D - R) % 8 == 0, so a lane's 8 elements are either all
+// rotary (4 consecutive angles, one 16-byte cos and sin load each) or all
+// pass-through.
+template <int U, typename IDX, bool VEC>
+__global__ __launch_bounds__(256) void k_inv_rope_quant(
+    const uint4* __restrict__ o, const int64_t* __restrict__ pos, const float* __restrict__ cosc,
+    const float* __restrict__ sinc, uint2* __restrict__ q, uint8_t* __restrict__ s, int64_t G64,
+    int64_t GK64, int D, int R, int64_t P) {
+    const int lane = threadIdx.x & 63, li = lane & 15;
+    const IDX G = (IDX)G64, GK = (IDX)GK64;
+    const IDX wave = (IDX)blockIdx.x * 4 + (IDX)(threadIdx.x >> 6);
+    const IDX chunk0 = wave * U;
+    const int half = R >> 1, rope0 = D - R;
+    uint4 v[U];
+    int64_t p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const IDX gid = (chunk0 + u) * 4 + (IDX)(lane >> 4);
+        v[u] = uint4{0u, 0u, 0u, 0u};
+        p[u] = -1;
+        if (gid < G) {  // both loads in bounds; an invalid position zeroes the row after
+            p[u] = pos[gid / GK];
+            v[u] = o[(int64_t)gid * 16 + li];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const IDX gid = (chunk0 + u) * 4 + (IDX)(lane >> 4);
+        if (p[u] < 0 || p[u] >= P) {
+            p[u] = -1;
+            v[u] = uint4{0u, 0u, 0u, 0u};
+        }
+        float f[8];
+        unpack8(v[u], f);
+        if (p[u] >= 0) {
+            const IDX j = gid - (gid / GK) * GK;
+            const int e0 = (int)(j * 128) + li * 8;    // element offset in the row
+            const int d0 = e0 - (e0 / D) * D;          // its dim within the head
+            const float* cr = cosc + p[u] * half;
+            const float* sr = sinc + p[u] * half;
+            float x[8];
+            if constexpr (VEC) {
+                if (d0 >= rope0) {
+                    const int i0 = (d0 - rope0) >> 1;  // a multiple of 4
+                    const float4 c4 = *reinterpret_cast<const float4*>(cr + i0);
+                    const float4 s4 = *reinterpret_cast<const float4*>(sr + i0);
+                    const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+                    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                    for (int k = 0; k < 8; k += 2) {
+                        const float c = cv[k >> 1], sn = sv[k >> 1];
+                        const float a = f[k] * c, b = f[k + 1] * sn;
+                        const float a1 = f[k + 1] * c, b1 = f[k] * sn;
+                        x[k] = a + b;
+                        x[k + 1] = a1 - b1;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) x[k] = f[k];
+                }
+            } else {
+#pragma unroll
+            for (int k = 0; k < 8; k += 2) {
+                const int d = d0 + k;
+                if (d >= rope0) {
+                    const int i = (d - rope0) >> 1;
+                    const float c = cr[i], sn = sr[i];
+                    const float a = f[k] * c, b = f[k + 1] * sn;
+                    const float a1 = f[k + 1] * c, b1 = f[k] * sn;
+                    x[k] = a + b;
+                    x[k + 1] = a1 - b1;
+                } else {
+                    x[k] = f[k];
+                    x[k + 1] = f[k + 1];
+                }
+            }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; k += 2) {
+                const uint32_t pr = bf16x2_rne(x[k], x[k + 1]);
+                f[k] = bf16_lo(pr);
+                f[k + 1] = bf16_hi(pr);
+            }
+        }
+        const float amax = max_16lanes(amax8(f));
+        const int e = e8m0_exponent(amax / 448.0f);
+        const float inv = e8m0_inv(e);
+        float t8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t8[k] = f[k] * inv;
+        if (gid < G) {
+            q[(int64_t)gid * 16 + li] = e4m3x8(t8);
+            if (li == 0) s[gid] = (uint8_t)(e + 127);
+        }
+    }
+}
+
 // Diagnostic: silu of the bf16 bit patterns first .. first + n - 1, as fp32.
 __global__ __launch_bounds__(256) void k_silu_bits(uint32_t first, int64_t n,
                                                    float* __restrict__ out) {
@@ -682,6 +791,27 @@ hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const in
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
     return launch(k_quant_gather<U>, (waves + 3) / 4, st, static_cast<const uint4*>(x), row_token,
                   static_cast<uint2*>(q), s, G, GK, n_src);
+}
+
+hipError_t launch_inv_rope_quant(const void* o, const int64_t* pos, const float* cosc,
+                                 const float* sinc, int64_t T, int64_t H, int64_t D, int64_t R,
+                                 int64_t P, void* q, uint8_t* s, hipStream_t st) {
+    constexpr int U = 4;
+    const int64_t GK = H * D / 128, G = T * GK;
+    const int64_t waves = (G + 4 * U - 1) / (4 * U);
+    const int64_t blocks = (waves + 3) / 4;
+    const bool small = blocks * 16 * U < (int64_t(1) << 31);  // every gid fits in int32
+    const bool vec = R % 8 == 0 && (D - R) % 8 == 0 &&
+                     reinterpret_cast<uintptr_t>(cosc) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(sinc) % 16 == 0;
+    const auto* ov = static_cast<const uint4*>(o);
+    auto* qv = static_cast<uint2*>(q);
+#define FP8_ROPE(IDX, VEC) \
+    launch(k_inv_rope_quant<U, IDX, VEC>, blocks, st, ov, pos, cosc, sinc, qv, s, G, GK, (int)D, \
+           (int)R, P)
+    if (small) return vec ? FP8_ROPE(int32_t, true) : FP8_ROPE(int32_t, false);
+    return vec ? FP8_ROPE(int64_t, true) : FP8_ROPE(int64_t, false);
+#undef FP8_ROPE
 }
 
 hipError_t launch_silu_bits(uint32_t first, int64_t n, float* out, hipStream_t st) {

@@ -1,4 +1,5 @@
-// Launch interface of the per-tensor, SwiGLU and token-gather quantizers.
+// Launch interface of the per-tensor, SwiGLU, token-gather and inverse-RoPE
+// quantizers.
 // Per-tensor dynamic quantization: one fp32 scale per tensor (amax / 448); up
 // to kTensMaxDescs tensors per launch sequence, with descriptors passed in
 // kernel arguments.  A tensor of nvec 16-byte vectors covers
@@ -33,6 +34,12 @@ hipError_t launch_silu_bits(uint32_t first, int64_t n, float* out, hipStream_t s
 
 // Token gather + 1x128 quantization: q[t] = quant(x[row_token[t]]), x bf16
 // [n_src, K] (K % 128 == 0, T > 0).
+// Inverse RoPE + 1x128 E8M0 quantization of o bf16 [T][H][D] (D % 8 == 0,
+// even R <= D, H * D % 128 == 0, T > 0; P >= 1 when R > 0).
+hipError_t launch_inv_rope_quant(const void* o, const int64_t* pos, const float* cosc,
+                                 const float* sinc, int64_t T, int64_t H, int64_t D, int64_t R,
+                                 int64_t P, void* q, uint8_t* s, hipStream_t st);
+
 hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,
                                int64_t T, void* q, float* s, hipStream_t st);
 

@@ -185,6 +185,31 @@ int fp8_quantize_block_gather(const void* x_bf16, int64_t n_src, int64_t K,
                               void* stream);
 
 /*
+ * Inverse RoPE + 1x128 E8M0 quantization: the pre-op of the DeepSeek V4
+ * output projection in the vLLM page §3 (inverse_rope_group_quant(o,
+ * positions, cos, sin, num_groups, quant_group_size=128) feeding
+ * batched_gemm_a8w8_mxscale).  The page shows only the call; the readings:
+ *   o          : bf16 [T, H, D] (D % 8 == 0); the last rope_dim dims of each
+ *                head are the rotary part, as interleaved pairs (y0, y1) =
+ *                dims (D - rope_dim + 2i, D - rope_dim + 2i + 1), angle index i
+ *   positions  : int64 [T]; cos_cache, sin_cache : fp32 [max_pos, rope_dim/2]
+ *   x0 = y0*c + y1*s, x1 = y1*c - y0*s (fp32, each operation rounded, no
+ *   fused multiply-add), rounded to bf16; other dims pass through.
+ *   q : E4M3 [T, H*D] (out), read as [T, num_groups, H*D/num_groups] by
+ *   fp8_batched_gemm_a8w8_mxscale;  s : E8M0 bytes [T, H*D/128] (out), each
+ *   1x128 group of the flattened row quantized as fp8_quantize_block_e8m0.
+ *   A position outside [0, max_pos) gives a zero row (codes 0, bytes 0).
+ *   Errors: T < 0, odd or negative rope_dim, rope_dim > 0 with max_pos 0,
+ *   num_groups <= 0 -> FP8_ERR_ARG; H or D <= 0, D % 8, rope_dim > D,
+ *   H % num_groups, (H/num_groups)*D % 128, H*D >= 2^31 -> FP8_ERR_SHAPE.
+ */
+int fp8_inverse_rope_group_quant(const void* o_bf16, const int64_t* positions,
+                                 const float* cos_cache, const float* sin_cache, int64_t T,
+                                 int64_t H, int64_t D, int64_t rope_dim, int64_t max_pos,
+                                 int64_t num_groups, void* q_e4m3, uint8_t* s_e8m0,
+                                 void* stream);
+
+/*
  * Diagnostic (test support): out[i] = silu of the bf16 bit pattern
  * first_bits + i, as computed inside fp8_swiglu_quant (fp32).  The patterns
  * must lie in [0, 0x10000); out holds n floats (device, 4-byte aligned).

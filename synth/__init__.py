@@ -33,7 +33,8 @@ Workload recipes (sizes and distributions of the pages' configurations):
                   the last 64 dims of each head; positions = token index within
                   sequences of 2048; cos/sin fp32 [8192, 32] of angle
                   p * 10000^(-2i/64), computed in fp64 and rounded once
-                  (shapes are synthetic: the pages give none).
+                  8192 tokens; the projection's weights [8 groups, 1024, 1024]
+                  ~ N(0, 0.02) (shapes are synthetic: the pages give none).
   KV cache:       per layer K and V [8192 tokens, 8 KV heads x 128] (the
                   Qwen3-8B-shaped attention of the dense linears); K ~ N(0, 1)
                   with one whole column x50 (an outlier channel), V ~ N(0, 1);
@@ -61,6 +62,7 @@ MOE_HIDDEN, MOE_INTER = 2048, 768
 KV_TOKENS, KV_HEADS, KV_HEAD_DIM = 8192, 8, 128
 
 ROPE_HEADS, ROPE_HEAD_DIM, ROPE_DIM, ROPE_GROUPS, ROPE_MAX_POS, ROPE_SEQ = 64, 128, 64, 8, 8192, 2048
+ROPE_TOKENS, ROPE_OUT = 8192, 1024  # tokens per step; per-group output width of the projection
 
 
 def _is_dev(device) -> bool:

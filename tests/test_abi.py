@@ -41,7 +41,8 @@ def test_header_declares_the_calls():
                      "fp8_encode_f32_bits", "fp8_bf16_round_f32_bits",
                      "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
                      "fp8_quantize_tensors", "fp8_add_rmsnorm_quant", "fp8_swiglu_quant",
-                     "fp8_silu_f32_of_bf16", "fp8_quantize_block_gather"):
+                     "fp8_silu_f32_of_bf16", "fp8_quantize_block_gather",
+                     "fp8_inverse_rope_group_quant"):
         assert required in names
 
 
@@ -148,6 +149,26 @@ def test_gather_validation(L):
     assert g(None, 0, 128, None, 0, None, None, None) == OK
     if not _gpu():
         assert g(f, 4, 128, f, 4, f, f, None) == DEVICE
+
+
+def test_inverse_rope_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    r = L.fp8_inverse_rope_group_quant
+    assert r(f, f, f, f, -1, 4, 128, 64, 16, 1, f, f, None) == ARG    # T
+    assert r(f, f, f, f, 4, 4, 128, 63, 16, 1, f, f, None) == ARG     # odd rope dim
+    assert r(f, f, f, f, 4, 4, 128, 64, 0, 1, f, f, None) == ARG      # no cache rows
+    assert r(f, f, f, f, 4, 4, 128, 64, 16, 0, f, f, None) == ARG     # groups
+    assert r(f, f, f, f, 4, 4, 100, 64, 16, 1, f, f, None) == SHAPE   # D % 8
+    assert r(f, f, f, f, 4, 4, 64, 128, 16, 1, f, f, None) == SHAPE   # rope dim > D
+    assert r(f, f, f, f, 4, 4, 128, 64, 16, 3, f, f, None) == SHAPE   # H % groups
+    assert r(f, f, f, f, 4, 2, 96, 64, 16, 2, f, f, None) == SHAPE    # group width % 128
+    assert r(f, None, f, f, 4, 4, 128, 64, 16, 1, f, f, None) == ARG
+    assert r(f, f, None, f, 4, 4, 128, 64, 16, 1, f, f, None) == ARG
+    assert r(f, vp(FAKE + 4), f, f, 4, 4, 128, 64, 16, 1, f, f, None) == ALIGN
+    assert r(None, None, None, None, 0, 4, 128, 64, 16, 1, None, None, None) == OK
+    if not _gpu():
+        assert r(f, f, f, f, 4, 4, 128, 64, 16, 1, f, f, None) == DEVICE
 
 
 def test_gemm_validation(L):

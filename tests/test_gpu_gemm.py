@@ -340,6 +340,32 @@ def test_mx_batched_groups():
     assert_rows_close(y.view(M * B, N), ref.reshape(M * B, N), what="batched mx")
 
 
+def test_inverse_rope_quant_into_batched_mx_gemm():
+    """The DeepSeek V4 output-projection path: inverse RoPE + E8M0 group quant
+    of o [T, 64, 128] viewed as 8 groups of 1024, then the batched MX GEMM
+    against per-group weights [8, 512, 1024].  The codes are bit-exact (the
+    quantizer's own test), so the GEMM tolerance applies."""
+    T, G, N = 512, synth.ROPE_GROUPS, 512
+    say(f"inverse RoPE quant -> batched MX GEMM, T={T} groups={G} N={N}")
+    o, pos = synth.rope_inputs(T, seed=44)
+    cos, sin = synth.rope_cache()
+    K = synth.ROPE_HEADS * synth.ROPE_HEAD_DIM // G
+    W = synth.normal_bf16((G, N, K), seed=45, std=0.02)
+    qa, sa = fp8.inverse_rope_group_quant(o.to(dev()), torch.as_tensor(pos, device=dev()),
+                                          torch.as_tensor(cos, device=dev()),
+                                          torch.as_tensor(sin, device=dev()), G)
+    (qw, sw), = fp8.requantize_weights([W.to(dev()).reshape(G * N, K)], fp8.SCALE_E8M0)
+    y = fp8.batched_gemm_a8w8_mxscale((qa, sa), (qw.view(G, N, K), sw.view(G, N // 128, -1)))
+    rows = sample_rows(T, 48, seed=46)
+    oq, os_, _ = oracle.inverse_rope_group_quant(o[torch.as_tensor(rows)], pos[rows], cos, sin,
+                                                 synth.ROPE_DIM)
+    oqw, osw = oracle.quantize_weight_block(W.reshape(G * N, K), 1)
+    ref = oracle.batched_mx_gemm(oq.reshape(-1, G, K), oqw.reshape(G, N, K),
+                                 os_.reshape(-1, G, K // 128), osw.reshape(G, N // 128, -1))
+    got = y[torch.as_tensor(rows, device=dev())].reshape(rows.size * G, N)
+    assert_rows_close(got, ref.reshape(rows.size * G, N), what="rope -> mx gemm")
+
+
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_mx_dense_full_size_sampled(name):
     N, K = synth.DENSE_SHAPES[name]

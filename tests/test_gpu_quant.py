@@ -337,6 +337,65 @@ def test_gather_quant_moe_dispatch_sampled():
     _eq_gather(x, token_of_row, rows=sample_rows(token_of_row.size, 256, seed=15))
 
 
+# ---------------------------------------- inverse RoPE + 1x128 E8M0 quant --
+def _eq_rope(o, pos, cos, sin, groups, rows=None):
+    q, s = fp8.inverse_rope_group_quant(o.to(dev()), torch.as_tensor(pos, device=dev()),
+                                        torch.as_tensor(cos, device=dev()),
+                                        torch.as_tensor(sin, device=dev()), groups)
+    T = o.shape[0]
+    sel = np.arange(T) if rows is None else rows
+    oq, os_, _ = oracle.inverse_rope_group_quant(o[torch.as_tensor(sel)], np.asarray(pos)[sel],
+                                                 cos, sin, 2 * cos.shape[1])
+    gq = host(q).reshape(T, -1)[sel]
+    gs = host(s).reshape(T, -1)[sel]
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs, os_), "E8M0 bytes differ"
+
+
+@pytest.mark.parametrize("T,H,D,R,G", [(1, 1, 128, 64, 1), (7, 4, 128, 64, 2),
+                                       (5, 2, 192, 64, 1),    # groups straddle heads
+                                       (9, 8, 64, 64, 4),     # all dims rotary
+                                       (3, 4, 128, 0, 1),     # no rotary part
+                                       (33, 16, 128, 32, 8)])
+def test_inverse_rope_quant_shapes(T, H, D, R, G):
+    say(f"inverse_rope_group_quant T={T} H={H} D={D} R={R} groups={G}")
+    o, pos = synth.rope_inputs(T, seed=T + H + D + R, heads=H, head_dim=D, seq=11)
+    cos, sin = synth.rope_cache(16, R)
+    _eq_rope(o, pos, cos, sin, G)
+
+
+def test_inverse_rope_quant_unaligned_caches_take_scalar_path():
+    """cos/sin starting 4 bytes into an allocation cannot take 16-byte loads;
+    the result is the same."""
+    say("inverse_rope_group_quant with 4-byte aligned cos/sin")
+    o, pos = synth.rope_inputs(5, seed=47, heads=4, head_dim=128, seq=9)
+    cos, sin = synth.rope_cache(16, 64)
+    cb = torch.zeros(cos.size + 1, dtype=torch.float32, device=dev())
+    sb = torch.zeros(sin.size + 1, dtype=torch.float32, device=dev())
+    cb[1:] = torch.as_tensor(cos.reshape(-1), device=dev())
+    sb[1:] = torch.as_tensor(sin.reshape(-1), device=dev())
+    cv, sv = cb[1:].view(16, 32), sb[1:].view(16, 32)
+    q, s = fp8.inverse_rope_group_quant(o.to(dev()), torch.as_tensor(pos, device=dev()), cv, sv, 2)
+    oq, os_, _ = oracle.inverse_rope_group_quant(o, pos, cos, sin, 64)
+    assert np.array_equal(host(q).reshape(5, -1), oq)
+    assert np.array_equal(host(s).reshape(5, -1), os_)
+
+
+def test_inverse_rope_quant_out_of_range_positions():
+    say("inverse_rope_group_quant with positions outside the cache")
+    o, _ = synth.rope_inputs(6, seed=41, heads=4, head_dim=128)
+    cos, sin = synth.rope_cache(16, 64)
+    _eq_rope(o, np.array([0, 16, -1, 15, 2 ** 40, 3], np.int64), cos, sin, 2)
+
+
+def test_inverse_rope_quant_full_workload_sampled():
+    T = 8192
+    say(f"inverse_rope_group_quant [{T}, 64, 128], R = 64, 8 groups, sampled rows")
+    o, pos = synth.rope_inputs(T, seed=42)
+    cos, sin = synth.rope_cache()
+    _eq_rope(o, pos, cos, sin, synth.ROPE_GROUPS, rows=sample_rows(T, 128, seed=43))
+
+
 def _eq_req(ws, fmt, out=None, block_rows=None):
     res = fp8.requantize_weights([w.to(dev()) if not w.is_cuda else w for w in ws], fmt)
     for i, (w, (q, s)) in enumerate(zip(ws, res)):
