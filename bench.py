@@ -31,6 +31,8 @@ there.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the work.
 
 ``--calibrate-copy`` instead runs a plain device copy of 1 GiB a few times,
 the reference kernel whose counter reading scales FETCH_SIZE / WRITE_SIZE.
+``--one-gemm M N K`` instead runs one block-scaled GEMM shape (seeded dense
+inputs, quantized by the library) ``--reps`` times, for counter runs.
 """
 from __future__ import annotations
 
@@ -94,6 +96,31 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
+def one_gemm(M: int, N: int, K: int, reps: int):
+    """One block-scaled GEMM shape, reps launches (for counter runs)."""
+    import torch
+
+    import fp8_w8a8_quantized_amd as fp8
+    import synth
+
+    dev = torch.device("cuda:0")
+    X = synth.act_col_outliers(M, K, seed=1, device=dev)
+    W = synth.weight(N, K, seed=2, device=dev)
+    a = fp8.quantize_block(X)
+    (w,) = fp8.requantize_weights([W], fp8.SCALE_F32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK, out=y)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    print(json.dumps({"gemm": [M, N, K], "reps": reps, "avg_us": round(us, 2),
+                      "tflops": round(2.0 * M * N * K / us / 1e6, 1)}))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +131,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=8192)
     ap.add_argument("--cpu-sample-layers", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--one-gemm", type=int, nargs=3, metavar=("M", "N", "K"))
+    ap.add_argument("--reps", type=int, default=3)
     return ap.parse_args()
 
 
@@ -155,9 +184,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.one_gemm:
+        one_gemm(*args.one_gemm, args.reps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the sharded path is described in DESIGN.md, not built)"}))
+                          "(the sharded path is not built)"}))
         sys.exit(2)
 
     import torch

@@ -8,7 +8,7 @@
  * (no FMA contraction and no fast-math, so every float operation below is one
  * IEEE binary32 operation with round-to-nearest-even, subnormals kept).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   rounding to E4M3 is round-to-nearest-even; overflow saturates to +-448;
  *   the element quotient is one correctly rounded fp32 division x / s by the
  *   stored scale; an all-zero group has scale 0 and signed-zero codes; the
