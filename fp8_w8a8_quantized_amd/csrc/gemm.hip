@@ -157,6 +157,8 @@ struct BigSrc {
 // columns (N % 256 == 128).
 struct BigTile {
     int b, tm, tn, rows, cols;
+    int64_t row0;  // first row of A and Y (per batch)
+    int e;         // weight batch: the batch b, or the expert of a grouped tile
 };
 
 __device__ __forceinline__ BigTile big_tile(int logical, int tm_count, int tn_count,
@@ -175,21 +177,59 @@ __device__ __forceinline__ BigTile big_tile(int logical, int tm_count, int tn_co
     const int64_t left = G.M - (int64_t)t.tm * BM2, cleft = G.N - (int64_t)t.tn * BN2;
     t.rows = left < BM2 ? (int)left : BM2;
     t.cols = cleft < BN2 ? (int)cleft : BN2;
+    t.row0 = 0;  // read only for grouped tiles
+    t.e = 0;
+    return t;
+}
+
+// Grouped (MoE) tiles: expert by expert, then column tile by column tile with
+// the expert's row tiles adjacent (they share the W tile).  pre[e] (LDS) is
+// the prefix over experts of ceil(rows_e / 256) * tn_count; expert e's rows
+// are [rlo[e], rhi[e]) of A and Y.
+struct BigGroups {
+    const int32_t* pre;
+    const int32_t* rlo;
+    const int32_t* rhi;
+    int E;
+};
+
+__device__ __forceinline__ BigTile big_tile_grouped(int logical, int tn_count, const BigGeom& G,
+                                                    const BigGroups& g) {
+    int lo = 0, hi = g.E - 1;  // last expert whose prefix start <= logical
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.pre[mid] <= logical) lo = mid; else hi = mid - 1;
+    }
+    BigTile t;
+    const int r_lo = g.rlo[lo], r_hi = g.rhi[lo];
+    const int mt = (r_hi - r_lo + BM2 - 1) / BM2;
+    const int lt = logical - g.pre[lo];
+    t.b = 0;
+    t.e = lo;
+    t.tn = lt / mt;
+    t.tm = lt - t.tn * mt;
+    t.row0 = (int64_t)r_lo + (int64_t)t.tm * BM2;
+    const int64_t left = r_hi - t.row0, cleft = G.N - (int64_t)t.tn * BN2;
+    t.rows = left < BM2 ? (int)left : BM2;
+    t.cols = cleft < BN2 ? (int)cleft : BN2;
     return t;
 }
 
 // Load sources of tile t.  Rows past M (and columns past N) read the last
 // valid row (column): their results are never stored.
-template <int GRAN>
+template <int GRAN, bool GROUPED>
 __device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* A, const uint8_t* W,
                                                const void* sA, const void* sW, const BigGeom& G,
                                                int wave, int lane) {
     const int K = (int)G.K, KB = K / BK, B = G.B;
-    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    // grouped tiles carry their first row and expert; dense and batched ones
+    // are at row tm * 256 of batch b
+    const int64_t row0 = GROUPED ? t.row0 : (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const int64_t wb = GROUPED ? t.e : t.b;
     const int lda = B * K;  // bytes between consecutive rows of one batch of A
     BigSrc S;
     S.a = buffer_rsrc(A + (row0 * B + t.b) * (int64_t)K, (t.rows - 1) * lda + K);
-    S.w = buffer_rsrc(W + ((int64_t)t.b * G.N + n0) * K, t.cols * K);
+    S.w = buffer_rsrc(W + (wb * G.N + n0) * K, t.cols * K);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = (i * 8 + wave) * 64 + lane;  // LDS chunk this lane fills
@@ -206,7 +246,7 @@ __device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* 
     const int wbl = (lane & 1) < nb ? (lane & 1) : nb - 1;  // lane l: weight block l & 1
     if constexpr (GRAN == GRAN_BLOCK) {  // fp32 scales (B == 1)
         const float* sa = static_cast<const float*>(sA) + row0 * KB;
-        const float* sw = static_cast<const float*>(sW) + (n0 / BK) * KB;
+        const float* sw = static_cast<const float*>(sW) + (wb * (G.N / BK) + n0 / BK) * KB;
         S.sa = buffer_rsrc(sa, t.rows * KB * 4);
         S.sw = buffer_rsrc(sw, nb * KB * 4);
         S.offsa = rr * KB * 4;
@@ -214,7 +254,7 @@ __device__ __forceinline__ BigSrc big_tile_src(const BigTile& t, const uint8_t* 
     } else if constexpr (GRAN == GRAN_MX) {  // E8M0 bytes [M, B, KB] and [B, N/128, KB]
         const uint8_t* sa = static_cast<const uint8_t*>(sA) + (row0 * B + t.b) * KB;
         const uint8_t* sw =
-            static_cast<const uint8_t*>(sW) + ((int64_t)t.b * (G.N / BK) + n0 / BK) * KB;
+            static_cast<const uint8_t*>(sW) + (wb * (G.N / BK) + n0 / BK) * KB;
         S.sa = buffer_rsrc(sa, (t.rows - 1) * B * KB + KB);
         S.sw = buffer_rsrc(sw, nb * KB);
         S.offsa = rr * B * KB;
@@ -456,11 +496,11 @@ __device__ __forceinline__ void big_tail(v4f (&acc)[4][8], const v8i (&x)[4], Bi
 // Store a wave's 64 x 128 block of tile t (bf16, 8 bytes per lane and column
 // tile) and clear the accumulators for the next tile.  ROW applies the per-row
 // and per-column fp32 scales here (B == 1).
-template <int GRAN>
+template <int GRAN, bool GROUPED>
 __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
                                           const void* sA, const void* sW, const BigGeom& G,
                                           int wm, int wn, int lr, int lk) {
-    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const int64_t row0 = GROUPED ? t.row0 : (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
     const int64_t ldy = (int64_t)G.B * G.N;
     if (wn * 128 < t.cols) {  // the wave's 128 columns exist
 #pragma unroll
@@ -493,20 +533,68 @@ __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, ui
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+constexpr int kMaxExpertsBig = 1024;  // expert table size of the grouped form
+
 // Persistent: workgroup b runs on XCD b % 8; the XCD's workgroups share a
 // contiguous range of logical tiles and take them round-robin.  The steps
 // (tile, K block) of one workgroup form one stream through the two LDS
 // stages, so the first K block of the next tile loads while the last K block
 // of the current one is multiplied and its output stored.
-template <int GRAN>
+template <int GRAN, bool GROUPED>
 __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restrict__ A,
                                                         const uint8_t* __restrict__ W,
                                                         const void* __restrict__ sA,
                                                         const void* __restrict__ sW,
-                                                        uint16_t* __restrict__ Y, BigGeom G) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
+                                                        uint16_t* __restrict__ Y, BigGeom G,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int E) {
+    // one LDS object for the stage ring and (grouped) the expert tables, so the
+    // compiler keeps telling the direct-to-LDS stage writes from operand reads
+    constexpr int kTab = GROUPED ? (3 * kMaxExpertsBig + 1) * 4 : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2 + kTab];
     const int tm_count = (int)((G.M + BM2 - 1) / BM2), tn_count = (int)((G.N + BN2 - 1) / BN2);
-    const int T = G.B * tm_count * tn_count;
+    int T = G.B * tm_count * tn_count;
+    BigGroups grp{};
+    if constexpr (GROUPED) {
+        // prefix over experts of their tile counts, and their row ranges (wave 0)
+        int32_t* s_pre = reinterpret_cast<int32_t*>(lds + kLds2);
+        int32_t* s_rlo = s_pre + kMaxExpertsBig + 1;
+        int32_t* s_rhi = s_rlo + kMaxExpertsBig;
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            int base = 0;
+            for (int e0 = 0; e0 < E; e0 += 64) {
+                const int e = e0 + lane;
+                int cnt = 0;
+                if (e < E) {
+                    int64_t lo = offsets[e], hi = offsets[e + 1];
+                    lo = lo < 0 ? 0 : (lo > G.M ? G.M : lo);
+                    hi = hi < lo ? lo : (hi > G.M ? G.M : hi);
+                    cnt = (int)((hi - lo + BM2 - 1) / BM2) * tn_count;
+                    s_rlo[e] = (int32_t)lo;
+                    s_rhi[e] = (int32_t)hi;
+                }
+                int incl = cnt;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int up = __shfl_up(incl, o);
+                    if (lane >= o) incl += up;
+                }
+                if (e < E) s_pre[e] = base + incl - cnt;
+                base += __shfl(incl, 63);
+            }
+            if (lane == 0) s_pre[E] = base;
+        }
+        __syncthreads();
+        grp = BigGroups{s_pre, s_rlo, s_rhi, E};
+        T = s_pre[E];
+    }
+    auto tile_of = [&](int logical) {
+        if constexpr (GROUPED)
+            return big_tile_grouped(logical, tn_count, G, grp);
+        else
+            return big_tile(logical, tm_count, tn_count, G);
+    };
     const int KB = (int)(G.K / BK);
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int nwg = ((int)gridDim.x - xcd + 7) >> 3;  // workgroups on this XCD
@@ -544,8 +632,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
     c.psc = 0.0f;
 
     int lt = 0, lkb = 0;  // load cursor: tile, K block
-    BigSrc S = big_tile_src<GRAN>(big_tile(first, tm_count, tn_count, G), A, W, sA, sW, G, wave,
-                                  lane);
+    BigSrc S = big_tile_src<GRAN, GROUPED>(tile_of(first), A, W, sA, sW, G, wave, lane);
     stage_big<GRAN>(lds, 0, S, 0, wave);
     // Materialize the output pointer now: a scalar load still in flight
     // during the loop would turn every LDS wait into lgkmcnt(0).
@@ -561,8 +648,8 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
             if (++lkb == KB) {
                 lkb = 0;
                 ++lt;
-                S = big_tile_src<GRAN>(big_tile(first + lt * nwg, tm_count, tn_count, G), A, W,
-                                       sA, sW, G, wave, lane);
+                S = big_tile_src<GRAN, GROUPED>(tile_of(first + lt * nwg), A, W, sA, sW, G, wave,
+                                                lane);
             }
             stage_big<GRAN>(lds, cur ^ 1, S, lkb, wave);
         }
@@ -575,8 +662,8 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
                 promote(acc[3][7], c.p, c.psc);
                 c.p = v4f{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, G), Y, sA,
-                            sW, G, wm, wn, lr, lk);
+            big_store<GRAN, GROUPED>(acc, tile_of(first + (ct - 1) * nwg), Y, sA, sW, G, wm, wn,
+                                     lr, lk);
         }
         big_body<GRAN>(lds, cur, acc, x, w0, bs, c, wn, lr, lk);
         if (++ckb == KB) {
@@ -585,8 +672,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
         }
     }
     big_tail<GRAN>(acc, x, c);
-    big_store<GRAN>(acc, big_tile(first + (ct - 1) * nwg, tm_count, tn_count, G), Y, sA, sW, G,
-                    wm, wn, lr, lk);
+    big_store<GRAN, GROUPED>(acc, tile_of(first + (ct - 1) * nwg), Y, sA, sW, G, wm, wn, lr, lk);
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,13 +1237,13 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
         const BigGeom G{M, N, K, 1};
         if (gran == GRAN_BLOCK)
-            hipLaunchKernelGGL(k_gemm_big<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
-                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
-                               G);
+            hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
+                               st, A, Wp, static_cast<const void*>(a_s),
+                               static_cast<const void*>(w_s), Yp, G, nullptr, 0);
         else
-            hipLaunchKernelGGL(k_gemm_big<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
-                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
-                               G);
+            hipLaunchKernelGGL((k_gemm_big<GRAN_ROW, false>), dim3(grid), dim3(kThreads2), 0,
+                               st, A, Wp, static_cast<const void*>(a_s),
+                               static_cast<const void*>(w_s), Yp, G, nullptr, 0);
         return hipGetLastError();
     }
     TileSpace S{};
@@ -1199,6 +1285,19 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
     S.Y = static_cast<uint16_t*>(y);
     S.offsets = offsets;
     S.M = T; S.N = N; S.K = K; S.E = E;
+    // Experts with a few hundred rows each fill 256-row tiles: the large-M
+    // kernel then reads each operand byte from LDS half as often as the
+    // 128 x 128 tiles do.  Its buffer offsets need K <= 2^22, and the tile and
+    // step counts (at most ceil(T/256) + E row tiles) must fit in int.
+    const int64_t max_tiles = (T / BM2 + E) * ((N + BN2 - 1) / BN2);
+    if (T >= 192 * E && K <= (int64_t(1) << 22) && max_tiles < (int64_t(1) << 31) &&
+        (max_tiles / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
+        const BigGeom G{T, N, K, 1};
+        hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
+                           dim3(kThreads2), 0, st, S.A, S.W, static_cast<const void*>(a_s),
+                           static_cast<const void*>(w_s), S.Y, G, offsets, (int)E);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
                        dim3(kThreadsP), 0, st, S, (int64_t)0);
     return hipGetLastError();
@@ -1211,10 +1310,10 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
     const int64_t tiles = B * ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
     const unsigned grid = (unsigned)(tiles < 256 ? tiles : 256);  // one per CU
     const BigGeom G{M, N, K, (int)B};
-    hipLaunchKernelGGL(k_gemm_big<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
+    hipLaunchKernelGGL((k_gemm_big<GRAN_MX, false>), dim3(grid), dim3(kThreads2), 0, st,
                        static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                        static_cast<const void*>(a_s), static_cast<const void*>(w_s),
-                       static_cast<uint16_t*>(y), G);
+                       static_cast<uint16_t*>(y), G, nullptr, 0);
     return hipGetLastError();
 }
 

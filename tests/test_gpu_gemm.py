@@ -239,6 +239,39 @@ def test_grouped_rows_outside_offsets_untouched():
     assert not torch.all(y[:40] == 7.0)
 
 
+def test_grouped_big_tiles_ragged_experts():
+    """Experts averaging >= 192 rows take 256-row tiles: row counts around
+    the tile size (0, 1, 255, 256, 257, ...) and a 128-column tail."""
+    say("grouped GEMM, 256-row tiles, ragged experts, N % 256 == 128")
+    counts = [0, 1, 255, 256, 257, 600, 900, 130]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T, N, K = int(offsets[-1]), 384, 384
+    A = synth.act_col_outliers(T, K, seed=18)
+    W = synth.normal_bf16((len(counts), N, K), seed=19, std=0.02)
+    y, ref, rows = _grouped_pipeline(A, W, offsets)
+    assert_rows_close(y, ref, what="grouped big tiles")
+
+
+def test_grouped_big_tiles_rows_outside_offsets_untouched():
+    say("grouped GEMM, 256-row tiles, rows outside [offsets[0], offsets[E]) untouched")
+    offsets = np.array([10, 300, 300, 1700], np.int32)
+    T, N, K = 2000, 256, 256
+    A = synth.act_col_outliers(T, K, seed=21)
+    W = synth.normal_bf16((3, N, K), seed=22, std=0.02)
+    qa, sa = fp8.quantize_block(A.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.reshape(3 * N, K).to(dev())], fp8.SCALE_F32)
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device=dev())
+    off = torch.as_tensor(offsets, device=dev())
+    fp8.grouped_gemm_a8w8_scaled((qa, sa), (qw.view(3, N, K), sw.view(3, 2, 2)), off, out=y)
+    assert torch.all(y[:10] == 7.0) and torch.all(y[1700:] == 7.0)
+    oqa, osa = oracle.quantize_block(A)
+    for e in (0, 2):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        oqw, osw = oracle.quantize_weight_block(W[e], 0)
+        ref = oracle.gemm(oqa[a:b], oqw, osa[a:b], osw, oracle.GRAN_BLOCK)
+        assert_rows_close(y[a:b], ref, what=f"expert {e}")
+
+
 @pytest.mark.parametrize("which", ["gate_up", "down"])
 def test_grouped_moe_full_size_sampled(which):
     say(f"grouped GEMM MoE {which} full size, sampled rows (>= 1 per expert)")
