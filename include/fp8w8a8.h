@@ -38,9 +38,11 @@
  *     memory on the current HIP device.
  *   * `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     on it; the call returns before the kernels finish.
- *   * The caller owns and allocates every buffer; the library allocates no
- *     device memory and keeps no pointer after the call returns (the kernels
- *     use the buffers until the stream reaches them).
+ *   * The caller owns and allocates every input and output buffer, and the
+ *     library keeps no pointer to them after the call returns (the kernels
+ *     use the buffers until the stream reaches them).  The one allocation of
+ *     the library is the workspace of fp8_gemm_a8w8_scaled at small M (see
+ *     there).
  *   * Errors: argument, shape and device checks run on the host before any
  *     launch; on error nothing is written and a negative fp8_status returns.
  *     Launch failures return FP8_ERR_LAUNCH.  Faults inside kernels surface
@@ -271,6 +273,16 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   scaled and added in fp32), output rounded to bf16 (nearest even).
  *   bias must be NULL (FP8_ERR_ARG otherwise).  K % 128 != 0 or
  *   N % 128 != 0 -> FP8_ERR_SHAPE.  M is any value >= 0.
+ *   Small M (below 1024, or an N that is not a multiple of 256) splits the K
+ *   steps of all tiles evenly over the CUs (stream-K) and sums split tiles in
+ *   a fixed order, so repeated calls give identical bytes.  That needs a
+ *   workspace of 32 MiB + 256 KiB, which the library allocates on the first
+ *   such call on each (device, stream) and keeps until the process ends.
+ *   Calls on one stream share it (they are ordered); calls on different
+ *   streams use different workspaces.  While the stream is being captured
+ *   into a graph and has no workspace yet, no allocation is made and a
+ *   kernel without the split runs instead (same results within the GEMM
+ *   tolerance, not the same bytes).
  */
 int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
                          const float* w_s, const void* bias, void* y_bf16, int64_t M,
@@ -287,6 +299,8 @@ int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_
  *             offsets[E] = T (empty experts allowed).  The kernel reads and
  *             writes only rows in [0, T) whatever the offsets hold.
  *   y   : bf16 [T, N] (out); rows covered by no expert are left untouched.
+ *   When the experts average at least 192 rows the work runs on 256 x 256
+ *   tiles, otherwise on 128 x 128 tiles (results within the GEMM tolerance).
  *   K % 128 != 0 or N % 128 != 0 -> FP8_ERR_SHAPE; E < 1, E > 1024 or
  *   T > 2^31 - 1 -> FP8_ERR_ARG.
  */
