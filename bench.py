@@ -488,7 +488,8 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
         "traffic": recorded_traffic(),
-        "kernel": "block-scaled FP8 GEMM k_gemm_big<0>, the 144 M=8192 launches of a step",
+        "kernel": "block-scaled FP8 GEMM k_gemm_big<0, false>, the 144 M=8192 launches of a "
+                  "step",
     }
 
     out = {
