@@ -694,38 +694,99 @@ constexpr int BMP = 128, BNP = 128, kThreadsP = 512, NSTP = 4;
 constexpr int64_t kPersistentGrid = 256;  // one workgroup per CU (LDS bound)
 constexpr int64_t kMaxExperts = 1024;     // prefix array size of the grouped kernel
 constexpr int kStageTileP = (BMP + BNP) * BK;            // 32 KiB of operands
-constexpr int kStageP = kStageTileP + 4 * BMP * 4;        // + four copies of sA
+constexpr int kSwP = kStageTileP + 4 * BMP * 4;           // after four copies of sA:
+constexpr int kStageP = kSwP + 8 * 256;                   // each wave's copy of sW (BUF)
 constexpr int kLdsP = NSTP * kStageP;
-static_assert(kLdsP <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+static_assert(kLdsP + (3 * 1024 + 1) * 4 <= 160 * 1024,
+              "gfx950 has 160 KiB of LDS per workgroup (stage ring + expert tables)");
 
 // s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left unconstrained (gfx9)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-template <int GRAN>
-__device__ __forceinline__ void stage_pipe(uint8_t* lds, int st, const Tile& t, int64_t K,
-                                           int64_t KB, int kb, int wave, int lane) {
+// Where a stage's loads come from.  BUF (K <= 2^22): buffer resources over
+// the tile's rows and scales, with each lane's 32-bit offsets computed once
+// per tile; the loads are buffer_load ... lds, which keep the compiler's LDS
+// waits counted, and each wave also stages its own copy of the weight-block
+// scale.  Otherwise (longer K): the global form from the tile's pointers, and
+// the weight-block scale read with a scalar load.
+struct PipeSrc {
+    __amdgpu_buffer_rsrc_t a, w, sa, sw;
+    int offa[2], offw[2], offsa;
+};
+
+template <int GRAN, bool BUF>
+struct PipeLoad {
+    Tile t;
+    PipeSrc s;
+    __device__ __forceinline__ void set(const Tile& tile, int64_t K, int64_t KB, int wave,
+                                        int lane) {
+        t = tile;
+        if constexpr (BUF) {
+            const int k = (int)K, kbn = (int)KB;
+            s.a = buffer_rsrc(t.A, t.rows * k);
+            s.w = buffer_rsrc(t.W, BNP * k);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = (i * 8 + wave) * 64 + lane;
+                const int r = p >> 3;
+                const int c = swz_pos(r, p & 7);
+                const int ra = r < t.rows ? r : t.rows - 1;
+                s.offa[i] = ra * k + c * 16;
+                s.offw[i] = r * k + c * 16;
+            }
+            if constexpr (GRAN == GRAN_BLOCK) {
+                const int r = (wave & 1) * 64 + lane;
+                const int rr = r < t.rows ? r : t.rows - 1;
+                s.sa = buffer_rsrc(t.sA, t.rows * kbn * 4);
+                s.sw = buffer_rsrc(t.sW, kbn * 4);
+                s.offsa = rr * kbn * 4;
+            }
+        }
+    }
+};
+
+template <int GRAN, bool BUF>
+__device__ __forceinline__ void stage_pipe(uint8_t* lds, int st, const PipeLoad<GRAN, BUF>& L,
+                                           int64_t K, int64_t KB, int kb, int wave, int lane) {
     uint8_t* la = lds + st * kStageP;
     uint8_t* lb = la + BMP * BK;
+    if constexpr (BUF) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pbase = (i * 8 + wave) * 64;  // LDS chunk of lane 0 (8 rows per wave load)
-        const int p = pbase + lane;
-        const int r = p >> 3;
-        const int c = swz_pos(r, p & 7);
-        const int ra = r < t.rows ? r : t.rows - 1;
-        g2l_16(t.A + ra * K + kb * BK + c * 16, la + pbase * 16);
-        g2l_16(t.W + r * K + kb * BK + c * 16, lb + pbase * 16);
-    }
-    if constexpr (GRAN == GRAN_BLOCK) {
-        const int r = (wave & 1) * 64 + lane;
-        const int rr = r < t.rows ? r : t.rows - 1;
-        g2l_4(t.sA + rr * KB + kb, la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256);
+        for (int i = 0; i < 2; ++i) {
+            const int pbase = (i * 8 + wave) * 64;  // LDS chunk of lane 0 (8 rows per wave load)
+            b2l(L.s.a, la + pbase * 16, 16, L.s.offa[i], kb * BK);
+            b2l(L.s.w, lb + pbase * 16, 16, L.s.offw[i], kb * BK);
+        }
+        if constexpr (GRAN == GRAN_BLOCK) {
+            b2l(L.s.sa, la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256, 4,
+                L.s.offsa, kb * 4);
+            b2l(L.s.sw, la + kSwP + wave * 256, 4, 0, kb * 4);  // every lane the same word
+        }
+    } else {
+        const Tile& t = L.t;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pbase = (i * 8 + wave) * 64;
+            const int p = pbase + lane;
+            const int r = p >> 3;
+            const int c = swz_pos(r, p & 7);
+            const int ra = r < t.rows ? r : t.rows - 1;
+            g2l_16(t.A + ra * K + kb * BK + c * 16, la + pbase * 16);
+            g2l_16(t.W + r * K + kb * BK + c * 16, lb + pbase * 16);
+        }
+        if constexpr (GRAN == GRAN_BLOCK) {
+            const int r = (wave & 1) * 64 + lane;
+            const int rr = r < t.rows ? r : t.rows - 1;
+            g2l_4(t.sA + rr * KB + kb,
+                  la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256);
+        }
     }
 }
 
-template <int GRAN>
+template <int GRAN, bool BUF>
 __device__ __forceinline__ void wait_stage(int kb, int KB) {
-    constexpr int per = GRAN == GRAN_BLOCK ? 5 : 4;  // loads per stage per thread
+    // loads per stage per thread
+    constexpr int per = GRAN == GRAN_BLOCK ? (BUF ? 6 : 5) : 4;
     if (kb + 2 < KB)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
     else if (kb + 1 < KB)
@@ -805,7 +866,7 @@ __device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
 // One K step of a 128 x 128 tile from LDS stage `la`: BLOCK promotes each
 // 16 x 16 product by its row scale x the weight block scale into acc (the FMA
 // of a product trails its MFMA by one); ROW accumulates in the MFMA.
-template <int GRAN>
+template <int GRAN, bool BUF>
 __device__ __forceinline__ void pipe_mma(const uint8_t* la, const float* sW, int kb,
                                          v4f (&acc)[4][2], int wm, int wn, int lr, int lk) {
     const uint8_t* lb = la + BMP * BK;
@@ -813,7 +874,11 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* la, const float* sW, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
     if constexpr (GRAN == GRAN_BLOCK) {
-        const float sw = uniform_load(sW, kb);
+        float sw;
+        if constexpr (BUF)
+            sw = *reinterpret_cast<const float*>(la + kSwP + (wm | (wn << 1)) * 256);
+        else
+            sw = uniform_load(sW, kb);
         const float* lsa = reinterpret_cast<const float*>(la + kStageTileP);
         float sc[4];
 #pragma unroll
@@ -893,7 +958,7 @@ __device__ __forceinline__ void pipe_store(const Tile& ct, v4f (&acc)[4][2], int
 // tiles form one sequence g = (tile i, k block) that the 4-stage ring walks
 // without a break: the next tile's first stages load while the current tile
 // finishes.
-template <int GRAN, bool GROUPED>
+template <int GRAN, bool GROUPED, bool BUF>
 __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t dense_tiles) {
     // one LDS object for the stage ring and (grouped) the expert tables: with
     // separate __shared__ arrays the compiler can no longer tell the
@@ -966,16 +1031,18 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
     // built from it) lands in VGPRs, and a weight-scale read then becomes a
     // vector load whose wait drains the whole stage ring.
     const int kbn = (int)KB, ng = (int)NG;
-    Tile lt = tile_at<GRAN, GROUPED>(S, first);  // tile being loaded
+    PipeLoad<GRAN, BUF> lt;  // tile being loaded
+    lt.set(tile_at<GRAN, GROUPED>(S, first), S.K, KB, wave, lane);
     int l_ti = 0, l_kb = 0;                      // (tile, k block) of the next stage to load
 #pragma unroll
     for (int st = 0; st < NSTP - 1; ++st) {
         if (st < ng) {
-            stage_pipe<GRAN>(lds, st, lt, S.K, KB, l_kb, wave, lane);
+            stage_pipe<GRAN, BUF>(lds, st, lt, S.K, KB, l_kb, wave, lane);
             if (++l_kb == kbn) {
                 l_kb = 0;
                 ++l_ti;
-                if (l_ti < ntiles) lt = tile_at<GRAN, GROUPED>(S, first + l_ti * nx);
+                if (l_ti < ntiles)
+                    lt.set(tile_at<GRAN, GROUPED>(S, first + l_ti * nx), S.K, KB, wave, lane);
             }
         }
     }
@@ -984,19 +1051,20 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
 
     for (int g = 0; g < ng; ++g) {
         asm volatile("" ::: "memory");
-        wait_stage<GRAN>(g, ng);
+        wait_stage<GRAN, BUF>(g, ng);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (g + NSTP - 1 < ng) {  // refill the stage consumed at g - 1
-            stage_pipe<GRAN>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
+            stage_pipe<GRAN, BUF>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
             if (++l_kb == kbn) {
                 l_kb = 0;
                 ++l_ti;
-                if (l_ti < ntiles) lt = tile_at<GRAN, GROUPED>(S, first + l_ti * nx);
+                if (l_ti < ntiles)
+                    lt.set(tile_at<GRAN, GROUPED>(S, first + l_ti * nx), S.K, KB, wave, lane);
             }
         }
 
-        pipe_mma<GRAN>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
+        pipe_mma<GRAN, BUF>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
         if (kb == kbn - 1) pipe_store<GRAN>(ct, acc, S.N, wm, wn, lr, lk);  // tile done
         if (++kb == kbn) {
             kb = 0;
@@ -1094,7 +1162,7 @@ __device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t Wt, int64_t G) {
     return ((u + 1) * G + Wt - 1) / Wt - 1;
 }
 
-template <int GRAN>
+template <int GRAN, bool BUF>
 __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tiles, SkWork ws) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP + 16];
     int32_t* s_last = reinterpret_cast<int32_t*>(lds + kLdsP);
@@ -1122,15 +1190,16 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
     const int kbn = (int)KB;
     int64_t l_t = t_first;  // tile and k block of the next stage to load
     int l_kb = (int)(u0 - t_first * KB);
-    Tile lt = tile_at<GRAN, false>(S, l_t);
+    PipeLoad<GRAN, BUF> lt;
+    lt.set(tile_at<GRAN, false>(S, l_t), S.K, KB, wave, lane);
 #pragma unroll
     for (int st = 0; st < NSTP - 1; ++st) {
         if (st < ng) {
-            stage_pipe<GRAN>(lds, st, lt, S.K, KB, l_kb, wave, lane);
+            stage_pipe<GRAN, BUF>(lds, st, lt, S.K, KB, l_kb, wave, lane);
             if (++l_kb == kbn) {
                 l_kb = 0;
                 ++l_t;
-                if (l_t < tiles) lt = tile_at<GRAN, false>(S, l_t);
+                if (l_t < tiles) lt.set(tile_at<GRAN, false>(S, l_t), S.K, KB, wave, lane);
             }
         }
     }
@@ -1141,18 +1210,18 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
 
     for (int g = 0; g < ng; ++g) {
         asm volatile("" ::: "memory");
-        wait_stage<GRAN>(g, ng);
+        wait_stage<GRAN, BUF>(g, ng);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (g + NSTP - 1 < ng) {
-            stage_pipe<GRAN>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
+            stage_pipe<GRAN, BUF>(lds, (g + NSTP - 1) % NSTP, lt, S.K, KB, l_kb, wave, lane);
             if (++l_kb == kbn) {
                 l_kb = 0;
                 ++l_t;
-                if (l_t < tiles) lt = tile_at<GRAN, false>(S, l_t);
+                if (l_t < tiles) lt.set(tile_at<GRAN, false>(S, l_t), S.K, KB, wave, lane);
             }
         }
-        pipe_mma<GRAN>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
+        pipe_mma<GRAN, BUF>(lds + (g % NSTP) * kStageP, ct.sW, kb, acc, wm, wn, lr, lk);
 
         if (kb == kbn - 1 || g == ng - 1) {  // this range's part of tile c_t is done
             if (kb_in == 0 && kb == kbn - 1) {
@@ -1252,25 +1321,31 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     S.tm_count = (M + BMP - 1) / BMP;
     const int64_t tiles = S.tm_count * (N / BNP);
     const int64_t steps = tiles * (K / BK);
+    const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
     if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
         // stream-K: every workgroup gets at least one K step (grid <= steps)
         const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
         const SkWork sk{static_cast<v4f*>(ws->part), ws->cnt};
-        if (gran == GRAN_BLOCK)
-            hipLaunchKernelGGL(k_gemm_sk<GRAN_BLOCK>, dim3((unsigned)grid), dim3(kThreadsP), 0, st,
-                               S, tiles, sk);
-        else
-            hipLaunchKernelGGL(k_gemm_sk<GRAN_ROW>, dim3((unsigned)grid), dim3(kThreadsP), 0, st,
-                               S, tiles, sk);
+#define FP8_SK(G, B) \
+    hipLaunchKernelGGL((k_gemm_sk<G, B>), dim3((unsigned)grid), dim3(kThreadsP), 0, st, S, tiles, sk)
+        if (gran == GRAN_BLOCK) {
+            if (buf) FP8_SK(GRAN_BLOCK, true); else FP8_SK(GRAN_BLOCK, false);
+        } else {
+            if (buf) FP8_SK(GRAN_ROW, true); else FP8_SK(GRAN_ROW, false);
+        }
+#undef FP8_SK
         return hipGetLastError();
     }
     const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
-    if (gran == GRAN_BLOCK)
-        hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, false>), dim3((unsigned)grid), dim3(kThreadsP),
-                           0, st, S, tiles);
-    else
-        hipLaunchKernelGGL((k_gemm_pipe<GRAN_ROW, false>), dim3((unsigned)grid), dim3(kThreadsP), 0,
-                           st, S, tiles);
+#define FP8_PIPE(G, B) \
+    hipLaunchKernelGGL((k_gemm_pipe<G, false, B>), dim3((unsigned)grid), dim3(kThreadsP), 0, st, S, \
+                       tiles)
+    if (gran == GRAN_BLOCK) {
+        if (buf) FP8_PIPE(GRAN_BLOCK, true); else FP8_PIPE(GRAN_BLOCK, false);
+    } else {
+        if (buf) FP8_PIPE(GRAN_ROW, true); else FP8_PIPE(GRAN_ROW, false);
+    }
+#undef FP8_PIPE
     return hipGetLastError();
 }
 
@@ -1298,8 +1373,12 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
                            static_cast<const void*>(w_s), S.Y, G, offsets, (int)E);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
-                       dim3(kThreadsP), 0, st, S, (int64_t)0);
+    if (K <= (int64_t(1) << 22))
+        hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true, true>), dim3((unsigned)kPersistentGrid),
+                           dim3(kThreadsP), 0, st, S, (int64_t)0);
+    else
+        hipLaunchKernelGGL((k_gemm_pipe<GRAN_BLOCK, true, false>), dim3((unsigned)kPersistentGrid),
+                           dim3(kThreadsP), 0, st, S, (int64_t)0);
     return hipGetLastError();
 }
 
