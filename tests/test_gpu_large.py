@@ -7,7 +7,8 @@ sampled rows, blocks and elements (first, last and random ones).
   - per-tensor quantization of a 2.4e9-element tensor whose maximum is planted
     (1000.0 at a known index, N(0, 1) elsewhere), so its scale is fixed by
     construction and sampled codes can be checked;
-  - the block-scaled GEMM with an output of 131136 x 16384 > 2^31 elements.
+  - the block-scaled GEMM with an output of 131136 x 16384 > 2^31 elements;
+  - a small-M GEMM with K past the 32-bit buffer offsets of its loads.
 """
 import numpy as np
 import pytest
@@ -113,4 +114,22 @@ def test_gemm_output_past_2e31_elements():
     ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_BLOCK)
     assert_rows_close(y, ref, rows=rows, what="large output")
     del X, W, qa, sa, qw, sw, y
+    torch.cuda.empty_cache()
+
+
+def test_small_m_gemm_k_past_buffer_offsets():
+    """K = 2^22 + 128: 128 rows of K bytes no longer fit 32-bit buffer
+    offsets, so the small-M kernels load with the global form."""
+    M, N, K = 3, 128, (1 << 22) + 128
+    say(f"block GEMM {M}x{N}x{K} (global-form loads)")
+    X = synth.act_col_outliers(M, K, seed=75)
+    W = synth.weight(N, K, seed=76, device=dev())
+    qa, sa = fp8.quantize_block(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W], fp8.SCALE_F32)
+    y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)
+    oqa, osa = oracle.quantize_block(X)
+    oqw, osw = oracle.quantize_weight_block(W.cpu(), 0)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_BLOCK)
+    assert_rows_close(y, ref, what="long K")
+    del W, qw, sw
     torch.cuda.empty_cache()
