@@ -50,13 +50,12 @@ int launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// Stream-K workspace of the small-M GEMM, one per (device, stream): allocated
-// on the first GEMM call that needs it and held until the process ends.  The
-// arrival counters are cleared once, by an ordinary memset on that stream
-// (ordered before the first kernel); every launch leaves them zero.  No
-// allocation is attempted while the stream is being captured into a graph:
-// then the GEMM runs without stream-K.  Calls on one stream are ordered, so
-// they may share the workspace; calls on different streams get their own.
+// Stream-K workspace of the small-M GEMM (partial tiles), one per (device,
+// stream): allocated on the first GEMM call that needs it and held until the
+// process ends.  No allocation is attempted while the stream is being
+// captured into a graph: then the GEMM runs without stream-K.  Calls on one
+// stream are ordered, so they may share the workspace; calls on different
+// streams get their own.
 struct WsEntry {
     int dev;
     hipStream_t stream;
@@ -83,17 +82,11 @@ bool gemm_workspace(hipStream_t st, fp8k::GemmWorkspace* out) {
         return false;
     }
     void* part = nullptr;
-    void* cnt = nullptr;
-    const size_t cnt_bytes = size_t(fp8k::kGemmWsMaxTiles) * sizeof(int32_t);
-    if (hipMalloc(&part, size_t(fp8k::kGemmWsPartBytes)) != hipSuccess ||
-        hipMalloc(&cnt, cnt_bytes) != hipSuccess ||
-        hipMemsetAsync(cnt, 0, cnt_bytes, st) != hipSuccess) {
+    if (hipMalloc(&part, size_t(fp8k::kGemmWsPartBytes)) != hipSuccess) {
         (void)hipGetLastError();
-        if (part) (void)hipFree(part);
-        if (cnt) (void)hipFree(cnt);
         return false;
     }
-    WsEntry e{dev, st, {part, static_cast<int32_t*>(cnt)}};
+    WsEntry e{dev, st, {part}};
     g_ws.push_back(e);
     *out = e.ws;
     return true;

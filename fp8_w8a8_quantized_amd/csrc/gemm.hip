@@ -1080,48 +1080,27 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
 // contiguous ranges, one per workgroup, so every CU gets the same number of
 // steps whatever the tile count (at decode M a linear has fewer 128 x 128
 // tiles than there are CUs, and a long K would leave most CUs idle).  A
-// workgroup whose range covers a whole tile stores it directly.  A tile cut
-// between workgroups is finished by the contributor that arrives last: each
-// contributor writes its fp32 accumulators to its partial slot, releases
-// them, and bumps the tile's arrival counter; the one that brings the count
-// to the number of contributors sums the partials in contributor order (so
-// the result does not depend on arrival order), resets the counter to zero
-// for the next launch and stores the tile.  Nobody waits for another
-// workgroup, so the scheme needs no co-residency.
-//   Coherence across XCDs (each has its own L2) is per access, not per cache:
-// partials are written and read as relaxed agent-scope atomics (64-bit
-// stores that write through the L2 and loads that read past it), and every
-// thread waits for its stores to complete before the workgroup barrier that
-// precedes the counter update.  Agent-scope fences would do the same by
-// writing back and invalidating the whole L2 of the XCD, which costs the
-// other workgroups there their cached operand tiles.
+// workgroup whose range covers a whole tile stores it directly.  For a tile
+// cut between workgroups each contributor stores its fp32 accumulators in its
+// partial slot and moves on; k_sk_reduce, launched next on the same stream,
+// sums each such tile's partials in contributor order (so the bytes do not
+// depend on timing) and stores it.  The kernel boundary orders the partial
+// stores before the reads on every XCD, so neither kernel waits on another
+// workgroup or needs a counter.
 //   Workspace: part = G x 2 slots of 128 x 128 fp32 (slot 0: the first tile
 //   of a workgroup's range, slot 1: its last), in register order (v4f index
-//   (slot * 8 + i * 2 + jj) * 512 + tid); cnt = one int per tile, zero
-//   between launches.
+//   (slot * 8 + i * 2 + jj) * 512 + tid).
 // ---------------------------------------------------------------------------
 static_assert(kGemmWsPartBytes == kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
 
 struct SkWork {
     v4f* part;
-    int32_t* cnt;
 };
 
-// one v4f of a partial tile as two relaxed agent-scope 64-bit atomics
-__device__ __forceinline__ void sk_put(v4f* p, const v4f& v) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(p);
-    const uint64_t lo = (uint64_t)__float_as_uint(v[1]) << 32 | __float_as_uint(v[0]);
-    const uint64_t hi = (uint64_t)__float_as_uint(v[3]) << 32 | __float_as_uint(v[2]);
-    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ v4f sk_get(const v4f* p) {
-    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return v4f{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-               __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
-}
+// one v4f of a partial tile (plain 16-byte accesses: the kernel boundary
+// between the stream-K kernel and the reduce orders them)
+__device__ __forceinline__ void sk_put(v4f* p, const v4f& v) { *p = v; }
+__device__ __forceinline__ v4f sk_get(const v4f* p) { return *p; }
 
 // A thread's 4 x 2 accumulator fragments (rows wm * 64 + i * 16 + lr of its
 // wave) to / from a partial slot; CHECK skips rows at or past `wrows` (rows
@@ -1164,8 +1143,7 @@ __device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t Wt, int64_t G) {
 
 template <int GRAN, bool BUF>
 __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tiles, SkWork ws) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP + 16];
-    int32_t* s_last = reinterpret_cast<int32_t*>(lds + kLdsP);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -1227,8 +1205,6 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
             if (kb_in == 0 && kb == kbn - 1) {
                 pipe_store<GRAN>(ct, acc, S.N, wm, wn, lr, lk);
             } else {
-                const int64_t c_lo = sk_owner(c_t * KB, Wt, G);
-                const int64_t c_hi = sk_owner(c_t * KB + KB - 1, Wt, G);
                 const int slot = (c_t == t_first) ? 0 : 1;
                 // rows past M carry nothing: a wave whose 64 rows are all
                 // valid (the common case) moves its partial without checks
@@ -1238,37 +1214,6 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
                     sk_write<false>(mine, acc, wrows, lr);
                 else if (wrows > 0)
                     sk_write<true>(mine, acc, wrows, lr);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this thread's partial is out
-                __syncthreads();
-                if (tid == 0) {
-                    const int32_t before = __hip_atomic_fetch_add(
-                        ws.cnt + c_t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    *s_last = (before == (int32_t)(c_hi - c_lo)) ? 1 : 0;
-                }
-                __syncthreads();
-                if (*s_last) {
-                    v4f sum[4][2];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) sum[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
-                        if (cc == c) {
-                            sk_add(sum, acc);
-                            continue;
-                        }
-                        const int sl = (sk_start(cc, Wt, G) / KB == c_t) ? 0 : 1;
-                        const v4f* pp = ws.part + (cc * 2 + sl) * 8 * kThreadsP + tid;
-                        if (wrows >= 64)
-                            sk_read_add<false>(sum, pp, wrows, lr);
-                        else if (wrows > 0)
-                            sk_read_add<true>(sum, pp, wrows, lr);
-                    }
-                    if (tid == 0)
-                        __hip_atomic_store(ws.cnt + c_t, 0, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    pipe_store<GRAN>(ct, sum, S.N, wm, wn, lr, lk);
-                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1282,6 +1227,37 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
             if (c_t < tiles) ct = tile_at<GRAN, false>(S, c_t);
         }
     }
+}
+
+// Sum of the partials of each tile that the stream-K kernel split (one
+// workgroup per tile; a tile one workgroup covered whole exits at once), in
+// contributor order, then the tile's bf16 store.  Threads map to accumulator
+// fragments exactly as in the stream-K kernel.
+template <int GRAN>
+__global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t tiles, int64_t G,
+                                                        const v4f* __restrict__ part) {
+    const int64_t t = blockIdx.x, KB = S.K / BK, Wt = tiles * KB;
+    const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
+    if (c_lo == c_hi) return;  // stored whole by its workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1, lr = lane & 15, lk = lane >> 4;
+    const Tile ct = tile_at<GRAN, false>(S, t);
+    const int wrows = ct.rows - wm * 64;
+    v4f sum[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) sum[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+        const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
+        const v4f* pp = part + (cc * 2 + sl) * 8 * kThreadsP + tid;
+        if (wrows >= 64)
+            sk_read_add<false>(sum, pp, wrows, lr);
+        else if (wrows > 0)
+            sk_read_add<true>(sum, pp, wrows, lr);
+    }
+    pipe_store<GRAN>(ct, sum, S.N, wm, wn, lr, lk);
 }
 
 }  // namespace
@@ -1325,7 +1301,7 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
         // stream-K: every workgroup gets at least one K step (grid <= steps)
         const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
-        const SkWork sk{static_cast<v4f*>(ws->part), ws->cnt};
+        const SkWork sk{static_cast<v4f*>(ws->part)};
 #define FP8_SK(G, B) \
     hipLaunchKernelGGL((k_gemm_sk<G, B>), dim3((unsigned)grid), dim3(kThreadsP), 0, st, S, tiles, sk)
         if (gran == GRAN_BLOCK) {
@@ -1334,6 +1310,16 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
             if (buf) FP8_SK(GRAN_ROW, true); else FP8_SK(GRAN_ROW, false);
         }
 #undef FP8_SK
+        if (hipError_t e = hipGetLastError()) return e;
+        if (steps % grid != 0 || (steps / grid) % (K / BK) != 0) {  // some tile is split
+            if (gran == GRAN_BLOCK)
+                hipLaunchKernelGGL(k_sk_reduce<GRAN_BLOCK>, dim3((unsigned)tiles),
+                                   dim3(kThreadsP), 0, st, S, tiles, grid,
+                                   static_cast<const v4f*>(sk.part));
+            else
+                hipLaunchKernelGGL(k_sk_reduce<GRAN_ROW>, dim3((unsigned)tiles), dim3(kThreadsP),
+                                   0, st, S, tiles, grid, static_cast<const v4f*>(sk.part));
+        }
         return hipGetLastError();
     }
     const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;

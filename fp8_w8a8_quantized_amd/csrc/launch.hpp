@@ -43,13 +43,12 @@ hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 
 // Workspace of the stream-K small-M GEMM (device memory, one per stream):
-// part holds 256 workgroups x 2 partial 128 x 128 fp32 tiles, cnt one arrival
-// counter per tile (zero before the first launch; every launch leaves it zero).
+// 256 workgroups x 2 partial 128 x 128 fp32 tiles.  Tile counts above
+// kGemmWsMaxTiles (one reduce workgroup per tile) run without stream-K.
 constexpr int64_t kGemmWsPartBytes = int64_t(256) * 2 * 128 * 128 * 4;
 constexpr int64_t kGemmWsMaxTiles = int64_t(1) << 16;
 struct GemmWorkspace {
     void* part;
-    int32_t* cnt;
 };
 // true when launch_gemm takes the small-M (128 x 128 tile) path for this shape
 bool gemm_small_path(int64_t M, int64_t N, int64_t K);

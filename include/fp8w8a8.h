@@ -275,9 +275,10 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   N % 128 != 0 -> FP8_ERR_SHAPE.  M is any value >= 0.
  *   Small M (below 1024; also N % 256 != 0 or K > 2^22) splits the K
  *   steps of all tiles evenly over the CUs (stream-K) and sums split tiles in
- *   a fixed order, so repeated calls give identical bytes.  That needs a
- *   workspace of 32 MiB + 256 KiB, which the library allocates on the first
- *   such call on each (device, stream) and keeps until the process ends.
+ *   a fixed order in a second kernel, so repeated calls give identical bytes.
+ *   That needs a workspace of 32 MiB for the partial tiles, which the library
+ *   allocates on the first such call on each (device, stream) and keeps until
+ *   the process ends.
  *   Calls on one stream share it (they are ordered); calls on different
  *   streams use different workspaces.  While the stream is being captured
  *   into a graph and has no workspace yet, no allocation is made and a
