@@ -283,7 +283,9 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   streams use different workspaces.  While the stream is being captured
  *   into a graph and has no workspace yet, no allocation is made and a
  *   kernel without the split runs instead (same results within the GEMM
- *   tolerance, not the same bytes).
+ *   tolerance, not the same bytes).  A graph captured on a stream that
+ *   already had a workspace records that workspace: replays of it must not
+ *   overlap other small-M GEMMs issued on that stream, or each other.
  */
 int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
                          const float* w_s, const void* bias, void* y_bf16, int64_t M,
