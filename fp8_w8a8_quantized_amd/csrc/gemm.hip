@@ -31,8 +31,11 @@
 //   * Operand tiles are staged in LDS by direct-to-LDS 16-byte loads, with
 //     16-byte chunks of each 128-byte tile row XOR-swizzled (swz) so the
 //     operand reads are free of bank conflicts.
-//   k_gemm_big  (M >= 1024): persistent, 256 x 256 tile, 8 waves, two LDS
-//     stages.
+//   k_gemm_pp   (M >= 1024, block scales): persistent, 256 x 256 tile, two
+//     LDS stages, 8 waves in two groups one phase apart (one group reads
+//     fragments while the other multiplies).
+//   k_gemm_big  (M >= 1024, row and E8M0 scales, grouped): the same tile and
+//     stages, all 8 waves in step.
 //   k_gemm_pipe (small M, and the MoE grouped GEMM): persistent, 128 x 128
 //     tile, 8 waves, a ring of four LDS stages with three in flight.
 #include <hip/hip_runtime.h>
@@ -48,6 +51,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;  // K step: one scale block
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left unconstrained (gfx9),
+// and for lgkmcnt(0) with the others unconstrained
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kLgkm0 = 0xC07F;
 constexpr int GRAN_BLOCK = 0, GRAN_ROW = 1, GRAN_MX = 2;  // MX: E8M0 block scales
 
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
@@ -324,7 +331,7 @@ struct BigScales {
 };
 
 // sched_group_barrier masks
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmem = 0x010, kSgDsRead = 0x100;
 
 __device__ __forceinline__ void promote(v4f& acc, const v4f& p, float s) {
 #pragma unroll
@@ -676,6 +683,367 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong large-M kernel (block scales, dense B = 1): the 256 x 256 tile,
+// the two LDS stages and the direct-to-LDS loads of k_gemm_big, with the 8
+// waves split into two groups of 4 (waves 0-3 and 4-7, one of each per SIMD)
+// that run one phase apart.  A wave alternates a memory phase (read the K
+// block's 4 X and 8 W fragments and its scales from LDS into registers) and
+// a compute phase (32 MFMAs from registers, each product promoted by 4 fp32
+// FMAs while the next MFMA runs).  Every phase ends at a workgroup barrier,
+// so while one group of a SIMD multiplies, the other reads: the matrix core
+// never waits on LDS, and the compute phase runs at the rate of an
+// all-register MFMA loop.
+//
+// Stage s % 2 holds K block s from the barrier before group 0 reads it
+// (phase 2s) until group 1 has read it (phase 2s + 1).  Group 0 issues its
+// share of block s + 1 at the start of its memory phase of block s (phase
+// 2s) and waits for it at the end of the following compute phase; group 1
+// issues its share of block s + 2 at the start of its compute phase of block
+// s (phase 2s + 2) and waits for it at the end of its next memory phase.
+// Both shares land before the barrier that opens phase 2s + 4.
+//
+// The output of a tile is stored in the memory phase of the next tile's
+// first block.  Lanes l and l + 16 swap packed columns (v_permlane16_swap),
+// so each lane writes 8 consecutive bf16 (16 bytes) and a store covers 64
+// contiguous bytes of each of 16 rows.
+// ---------------------------------------------------------------------------
+
+// Workgroup barrier without a memory fence: the waits that order LDS and
+// global traffic around it are explicit.
+__device__ __forceinline__ void pp_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Store a wave's 64 x 128 block (tile rows wm * 64 .., columns col0 ..)
+// through Yr, a buffer resource over the tile's valid rows of Y [.., ldy]:
+// rows past M fall outside it and the hardware drops their writes, so every
+// wave issues exactly kPPStores store instructions.  Clears the accumulators.
+constexpr int kPPStores = 16;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void pp_store(v4f (&acc)[4][8], __amdgpu_buffer_rsrc_t Yr, int ldy,
+                                         int col0, int wm, int lr, int lk) {
+    const int cq = 16 * (lk & 1) + 8 * (lk >> 1);  // lane's column inside a 32-column pair
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + lr;
+        const int off = (r * ldy + col0 + cq) * 2;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const v4f& a = acc[i][2 * p];
+            const v4f& b = acc[i][2 * p + 1];
+            // lane (lr, lk) holds columns 16 j + 4 lk .. + 3 of fragment j;
+            // the swap of rows 1, 3 of the first operand with rows 0, 2 of
+            // the second gives lane (lr, lk) the 8 columns starting at
+            // 32 p + cq
+            const auto s0 = __builtin_amdgcn_permlane16_swap(bf16x2_rne(a[0], a[1]),
+                                                             bf16x2_rne(b[0], b[1]), false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(bf16x2_rne(a[2], a[3]),
+                                                             bf16x2_rne(b[2], b[3]), false, false);
+            const v4u o = {s0[0], s1[0], s0[1], s1[1]};
+            __builtin_amdgcn_raw_buffer_store_b128(o, Yr, off + 64 * p, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Store tile k's block of this wave.
+__device__ __forceinline__ void pp_store_tile(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
+                                              int N, int wn, int wm, int lr, int lk) {
+    const __amdgpu_buffer_rsrc_t Yr =
+        buffer_rsrc(Y + (int64_t)t.tm * BM2 * N, t.rows * N * 2);
+    pp_store(acc, Yr, N, t.tn * BN2 + wn * 128, wm, lr, lk);
+}
+
+// Everything a ping-pong wave needs besides its registers.
+struct PPCtx {
+    const uint8_t* A;
+    const uint8_t* W;
+    const float* sA;
+    const float* sW;
+    uint16_t* Y;
+    BigGeom G;
+    int tm_count, tn_count, first, nwg, NS, KB, K;
+    int wave, wm, wn, lr, lk;
+    int off0;  // lane's byte offset of its first A / W chunk of a block
+    int offa;  // group 1: lane's byte offset of its sA word at kb = 0
+    int offw;  // group 1: lane's byte offset of its sW word at kb = 0
+};
+
+// Tile k of this workgroup (its fields made provably wave-uniform, so the
+// buffer resources built from them stay in scalar registers).
+__device__ __forceinline__ BigTile pp_tile(const PPCtx& c, int k) {
+    BigTile t = big_tile(c.first + k * c.nwg, c.tm_count, c.tn_count, c.G);
+    t.tm = __builtin_amdgcn_readfirstlane(t.tm);
+    t.tn = __builtin_amdgcn_readfirstlane(t.tn);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    return t;
+}
+
+// Sources of the blocks one wave loads: group 0 the W tile (r0), group 1 the
+// A tile (r0), its sA rows (r1) and sW blocks (r2).  Rows past M lie past the
+// A and sA resources, so their loads return zeros (never stored).
+struct PPSrc {
+    __amdgpu_buffer_rsrc_t r0, r1, r2;
+};
+
+template <int GRP>
+__device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
+    const BigTile t = pp_tile(c, tile);
+    const int K = c.K, KB = c.KB;
+    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    PPSrc S;
+    if (GRP == 0) {
+        S.r0 = buffer_rsrc(c.W + n0 * K, BN2 * K);
+        S.r1 = S.r2 = S.r0;
+    } else {
+        S.r0 = buffer_rsrc(c.A + row0 * K, t.rows * K);
+        S.r1 = buffer_rsrc(c.sA + row0 * KB, t.rows * KB * 4);
+        S.r2 = buffer_rsrc(c.sW + (n0 / BK) * KB, 2 * KB * 4);
+    }
+    return S;
+}
+
+// Cursor over the blocks a wave loads: block b, its tile and K block, and the
+// sources of that tile.  Blocks past the last one reload the last block into
+// their (free) stage, so the loads of a phase never depend on a branch.
+template <int GRP>
+struct PPCur {
+    int b, t, kb;
+    PPSrc S;
+    __device__ __forceinline__ void start(const PPCtx& c, int b0) {
+        b = b0;
+        const int bc = b0 < c.NS ? b0 : c.NS - 1;
+        t = bc / c.KB;
+        kb = bc - t * c.KB;
+        S = pp_src<GRP>(c, t);
+    }
+    __device__ __forceinline__ void next(const PPCtx& c) {
+        ++b;
+        if (b < c.NS && ++kb == c.KB) {
+            kb = 0;
+            ++t;
+            S = pp_src<GRP>(c, t);
+        }
+    }
+};
+
+// Loads of one phase.  A stage holds the A slice (256 rows x 128 bytes) and
+// the W slice (W half h = rows 128 h ..), each as 16-byte chunks p (tile row
+// p / 8, swizzled 16-byte column swz_pos of p % 8), and the scale words.
+// The wave with index q in its group covers chunks (i * 4 + q) * 64 + lane.
+// Group 1, load n of 10: n < 8 the A chunks with i = n, n = 8 its 64 sA rows,
+// n = 9 the two sW words (every wave of the group writes the same words).
+// Group 0, load n of 8: W half 1 of block cur (n < 4, i = n) or W half 0 of
+// block nxt (i = n - 4).
+__device__ __forceinline__ void pp_load1(uint8_t* lds, const PPCtx& c, const PPCur<1>& L, int o,
+                                         int n) {
+    const int q = c.wave & 3, st = L.b & 1;
+    uint8_t* la = lds + st * kStage2;
+    if (n < 8)
+        b2l(L.S.r0, la + (n * 4 + q) * 64 * 16, 16, o + n * 32 * c.K, L.kb * BK);
+    else if (n == 8)
+        b2l(L.S.r1, lds + 2 * kStage2 + st * BM2 * 4 + q * 256, 4, c.offa, L.kb * 4);
+    else
+        b2l(L.S.r2, lds + kSw2 + st * 256, 4, c.offw, L.kb * 4);
+}
+
+__device__ __forceinline__ void pp_load0(uint8_t* lds, const PPCtx& c, const PPCur<0>& cur,
+                                         const PPCur<0>& nxt, int o, int n) {
+    const int q = c.wave & 3, h = n < 4 ? 1 : 0, i = n & 3;
+    const PPCur<0>& L = h ? cur : nxt;
+    uint8_t* lb = lds + (L.b & 1) * kStage2 + BM2 * BK;
+    b2l(L.S.r0, lb + (h * 1024 + (i * 4 + q) * 64) * 16, 16, o + (h * 128 + i * 32) * c.K,
+        L.kb * BK);
+}
+
+// Memory phase of block s: the wave's X and W fragments and scales into
+// registers.
+__device__ __forceinline__ void pp_read(const uint8_t* lds, const PPCtx& c, int s, v8i (&x)[4],
+                                        v8i (&w)[8], float (&sc)[4]) {
+    const int slot = s & 1;
+    const uint8_t* la = lds + slot * kStage2;
+    const uint8_t* lbw = la + BM2 * BK;
+    const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + slot * BM2 * 4);
+    const float sw = reinterpret_cast<const float*>(lds + kSw2 + slot * 256)[c.wn];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = frag(la, c.wm * 64 + i * 16 + c.lr, c.lk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = frag(lbw, c.wn * 128 + j * 16 + c.lr, c.lk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = lsa[c.wm * 64 + i * 16 + c.lr] * sw;
+}
+
+// The phase loop of group GRP (0: waves 0-3, 1: waves 4-7; group 1 enters
+// one barrier later, so group 0 reads block s in global phase 2s and group 1
+// in 2s + 1).  Group 0 reads only W half 0 and group 1 only W half 1, so
+// the halves and the A slice of a stage free up at different phases, and
+// every load of the loop is issued in a compute phase, spread over its
+// MFMAs, at least one phase before it is read:
+//   group 1, compute phase of block s (global 2s + 2): A slice and scales of
+//     block s + 2; waits at the end of its next memory phase (2s + 3);
+//   group 0, compute phase of block s (global 2s + 1): W half 1 of block
+//     s + 1 and W half 0 of block s + 2; waits at the end of its next memory
+//     phase (2s + 2).
+// Each group has its own copy of the loop, so every wait is unconditional
+// and the compute phase is one straight block.
+template <int GRP>
+__device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>& cur) {
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    v8i x[4], w[8];
+    float sc[4];
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int NS = c.NS, KB = c.KB, wm = c.wm, wn = c.wn, lr = c.lr, lk = c.lk;
+    PPCur<GRP> nxt = cur;  // group 0: the block after cur
+
+    // the last product of a compute phase, promoted after its barrier so the
+    // other group's first MFMA queues right behind it
+    v4f carry = zero;
+    float carry_sc = 0.0f;
+    int ct = 0, ckb = 0;  // compute cursor: tile, K block
+    for (int s = 0; s < NS; ++s) {
+        // ---- memory phase of block s ----
+        promote(acc[3][7], carry, carry_sc);
+        const bool stored = ckb == 0 && s > 0;
+        if (stored)  // the previous tile is complete: store it
+            pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
+        pp_read(lds, c, s, x, w, sc);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);  // fragments and scales in registers
+        // the previous compute phase's loads; vector memory operations complete
+        // in issue order, so the stores just issued need not be waited for
+        if (stored)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPPStores));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        pp_barrier();
+        // ---- compute phase of block s ----
+        // advance the load cursor here, before the MFMAs: a branch after them
+        // would let the compiler sink their promotions past it
+        if (GRP == 0) {
+            nxt = cur;
+            nxt.next(c);  // cur: block s + 1, nxt: block s + 2
+        } else {
+            cur.next(c);  // block s + 2
+        }
+        int o = c.off0;
+        asm volatile("" : "+v"(o));  // recomputed per phase, not held across the loop
+        __builtin_amdgcn_sched_barrier(0);
+        v4f pr[2];
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+            pr[n & 1] = mfma_f8(w[n >> 2], x[n & 3], zero);
+            if (n > 0) {
+                const int m = n - 1;
+                promote(acc[m & 3][m >> 2], pr[m & 1], sc[m & 3]);
+            }
+            const bool ld = GRP == 0 ? (n & 3) == 0 : (n % 3 == 0 && n <= 27);
+            if (ld) {
+                if constexpr (GRP == 0)
+                    pp_load0(lds, c, cur, nxt, o, n >> 2);
+                else
+                    pp_load1(lds, c, cur, o, n / 3);
+            }
+            // MFMA; the 4 FMAs promoting the MFMA before it, plus the address
+            // add of a chunk load; then the load
+            const bool add = ld && (GRP == 0 || n / 3 < 8);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            if (n > 0 && add)
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
+            else if (n > 0)
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
+            else if (add)
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 1, 0);
+            if (ld) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        }
+        carry = pr[1];
+        carry_sc = sc[3];
+        __builtin_amdgcn_sched_barrier(0);
+        if (GRP == 0) cur = nxt;
+        pp_barrier();
+        if (++ckb == KB) {
+            ckb = 0;
+            ++ct;
+        }
+    }
+    if (GRP == 0) pp_barrier();  // the barrier count of group 1's offset
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last compute phase's loads
+    promote(acc[3][7], carry, carry_sc);
+    pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
+}
+
+__global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict__ A,
+                                                       const uint8_t* __restrict__ W,
+                                                       const float* __restrict__ sA,
+                                                       const float* __restrict__ sW,
+                                                       uint16_t* __restrict__ Y, BigGeom G) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
+    PPCtx c;
+    c.A = A; c.W = W; c.sA = sA; c.sW = sW; c.Y = Y; c.G = G;
+    c.tm_count = (int)((G.M + BM2 - 1) / BM2);
+    c.tn_count = (int)(G.N / BN2);
+    const int T = c.tm_count * c.tn_count;
+    c.K = (int)G.K;
+    c.KB = c.K / BK;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    c.nwg = ((int)gridDim.x - xcd + 7) >> 3;
+    const int q = T >> 3, rem = T & 7;
+    const int xbeg = xcd * q + (xcd < rem ? xcd : rem), tx = q + (xcd < rem ? 1 : 0);
+    if (idx >= tx) return;
+    const int nt = (tx - idx + c.nwg - 1) / c.nwg;
+    c.first = xbeg + idx;
+    c.NS = nt * c.KB;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = c.wave >> 2, wq = c.wave & 3;
+    c.wm = wq;
+    c.wn = grp;
+    c.lr = lane & 15;
+    c.lk = lane >> 4;
+    c.off0 = (wq * 8 + (lane >> 3)) * c.K + swz_pos(lane >> 3, lane & 7) * 16;
+    c.offa = (wq * 64 + lane) * c.KB * 4;
+    c.offw = (lane & 1) * c.KB * 4;
+    asm volatile("" ::"s"(Y));
+    // prologue: all of block 0 and, of block 1, everything but W half 1
+    // (group 0 loads it in its first compute phase)
+    if (grp == 0) {
+        PPCur<0> cur, nxt;
+        cur.start(c, 0);
+        nxt.start(c, 0);
+        const int o = c.off0;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) pp_load0(lds, c, cur, nxt, o, n);  // W halves 1, 0 of block 0
+        nxt.next(c);
+#pragma unroll
+        for (int n = 4; n < 8; ++n) pp_load0(lds, c, cur, nxt, o, n);  // W half 0 of block 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        pp_barrier();
+        pp_loop<0>(lds, c, nxt);  // cur = block 1
+    } else {
+        PPCur<1> cur;
+        cur.start(c, 0);
+        const int o = c.off0;
+#pragma unroll
+        for (int n = 0; n < 10; ++n) pp_load1(lds, c, cur, o, n);  // block 0
+        cur.next(c);
+#pragma unroll
+        for (int n = 0; n < 10; ++n) pp_load1(lds, c, cur, o, n);  // block 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        pp_barrier();
+        pp_barrier();  // group 1 runs one phase behind
+        pp_loop<1>(lds, c, cur);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small-M and grouped kernel: tile 128 x 128, K step 128, 512 threads as 2 x 4
 // waves of 64 x 32 (two waves per SIMD), the same transposed MFMA, promotion
 // and 8-byte stores as
@@ -700,8 +1068,6 @@ constexpr int kLdsP = NSTP * kStageP;
 static_assert(kLdsP + (3 * 1024 + 1) * 4 <= 160 * 1024,
               "gfx950 has 160 KiB of LDS per workgroup (stage ring + expert tables)");
 
-// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left unconstrained (gfx9)
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Where a stage's loads come from.  BUF (K <= 2^22): buffer resources over
 // the tile's rows and scales, with each lane's 32-bit offsets computed once
@@ -1281,7 +1647,12 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
         const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
         const BigGeom G{M, N, K, 1};
-        if (gran == GRAN_BLOCK)
+        // the ping-pong kernel addresses a tile's output rows with 32-bit
+        // buffer offsets (256 rows x N bf16)
+        if (gran == GRAN_BLOCK && N <= (int64_t(1) << 22))
+            hipLaunchKernelGGL(k_gemm_pp, dim3(grid), dim3(kThreads2), 0, st, A, Wp, a_s, w_s, Yp,
+                               G);
+        else if (gran == GRAN_BLOCK)
             hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
                                static_cast<const void*>(w_s), Yp, G, nullptr, 0);

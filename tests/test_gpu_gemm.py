@@ -57,10 +57,12 @@ def test_block_small_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1024, 256, 256), (1100, 768, 640), (2047, 512, 1152),
-                                   (8200, 2304, 256)])
+                                   (8200, 2304, 256), (1024, 512, 128), (4352, 4096, 128)])
 def test_block_large_m_shapes(M, N, K):
     # 8200 x 2304: 33 x 9 = 297 tiles of 256 x 256 on 256 workgroups, so some
-    # workgroups run two tiles; the last row tile holds 8 rows
+    # workgroups run two tiles; the last row tile holds 8 rows.  K = 128: one
+    # K block per tile (1024 x 512: one block per workgroup; 4352 x 4096: 272
+    # tiles, a new tile at every block of the workgroups that run two)
     say(f"block GEMM (large-M kernel) {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + N + K)
     W = synth.weight(N, K, seed=N + K + 1)
@@ -191,6 +193,27 @@ def test_small_m_gemm_in_graph_capture():
         diff = (y.float() - eager.float()).abs().max().item()
         assert diff <= 1e-2 * eager.float().abs().max().item()
         _ = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)  # eager work between
+
+
+def test_large_m_block_gemm_repeatable():
+    # 48 tiles per workgroup with two K blocks each: a tile boundary every
+    # other block, where the kernel stores a tile while the next blocks' loads
+    # are in flight; three runs must give the same bits, and sampled rows
+    # (incl. the ragged last tile) match the oracle
+    M, N, K = 12288 + 100, 8192, 256
+    say(f"block GEMM repeatable {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=21)
+    W = synth.weight(N, K, seed=22)
+    qa, sa = fp8.quantize_block(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_F32)
+    ys = [fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    rows = np.unique(np.concatenate([sample_rows(M, 12, seed=3), np.arange(M - 100, M)]))
+    y, ref = _block_pipeline(X, W, rows=rows)
+    assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    assert_rows_close(y, ref, rows=rows, what="repeatable")
 
 
 def test_ragged_m_full_k():
