@@ -1469,8 +1469,8 @@ __device__ __forceinline__ void sk_put(v4f* p, const v4f& v) { *p = v; }
 __device__ __forceinline__ v4f sk_get(const v4f* p) { return *p; }
 
 // A thread's 4 x 2 accumulator fragments (rows wm * 64 + i * 16 + lr of its
-// wave) to / from a partial slot; CHECK skips rows at or past `wrows` (rows
-// of the wave that exist), which only the wave holding row M - 1 needs.
+// wave) to a partial slot; CHECK skips rows at or past `wrows` (rows of the
+// wave that exist), which only the wave holding row M - 1 needs.
 template <bool CHECK>
 __device__ __forceinline__ void sk_write(v4f* mine, const v4f (&acc)[4][2], int wrows, int lr) {
 #pragma unroll
@@ -1479,26 +1479,6 @@ __device__ __forceinline__ void sk_write(v4f* mine, const v4f (&acc)[4][2], int 
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) sk_put(mine + (i * 2 + jj) * kThreadsP, acc[i][jj]);
 }
-__device__ __forceinline__ void sk_add(v4f (&sum)[4][2], const v4f (&p)[4][2]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum[i][jj][e] = sum[i][jj][e] + p[i][jj][e];
-}
-template <bool CHECK>
-__device__ __forceinline__ void sk_read_add(v4f (&sum)[4][2], const v4f* pp, int wrows, int lr) {
-    v4f p[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            p[i][jj] = (!CHECK || i * 16 + lr < wrows) ? sk_get(pp + (i * 2 + jj) * kThreadsP)
-                                                        : v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    sk_add(sum, p);
-}
-
 // first K step of rank c's range, and the rank owning step u
 __device__ __forceinline__ int64_t sk_start(int64_t c, int64_t Wt, int64_t G) {
     return c * Wt / G;
@@ -1595,44 +1575,68 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tile
     }
 }
 
-// Sum of the partials of each tile that the stream-K kernel split (one
-// workgroup per tile; a tile one workgroup covered whole exits at once), in
-// contributor order, then the tile's bf16 store.  Threads map to accumulator
-// fragments exactly as in the stream-K kernel.
+// Sum of the partials of each tile that the stream-K kernel split, in
+// contributor order (so the bytes do not depend on timing), then the bf16
+// store.  kSkRedSplit workgroups per tile, workgroup r of a tile taking row
+// fragment i = r of every wave (rows wm * 64 + 16 r + lr): one workgroup per
+// tile left three quarters of the chip idle at decode shapes and read 64 KiB
+// per partial through one CU.  A tile one workgroup covered whole exits at
+// once.  Threads map to accumulator fragments exactly as in the stream-K
+// kernel.
+constexpr int kSkRedSplit = 4;
+
 template <int GRAN>
 __global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t tiles, int64_t G,
                                                         const v4f* __restrict__ part) {
-    const int64_t t = blockIdx.x, KB = S.K / BK, Wt = tiles * KB;
+    const int64_t t = blockIdx.x / kSkRedSplit, KB = S.K / BK, Wt = tiles * KB;
+    const int i = (int)(blockIdx.x % kSkRedSplit);
     const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
     if (c_lo == c_hi) return;  // stored whole by its workgroup
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1, lr = lane & 15, lk = lane >> 4;
     const Tile ct = tile_at<GRAN, false>(S, t);
-    const int wrows = ct.rows - wm * 64;
-    v4f sum[4][2];
+    const int r = wm * 64 + i * 16 + lr;  // this thread's row of the tile
+    v4f sum[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+    if (r < ct.rows) {
+        for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+            const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
+            const v4f* pp = part + (cc * 2 + sl) * 8 * kThreadsP + tid;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int jj = 0; jj < 2; ++jj) {
+                const v4f p = sk_get(pp + (i * 2 + jj) * kThreadsP);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) sum[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
-        const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
-        const v4f* pp = part + (cc * 2 + sl) * 8 * kThreadsP + tid;
-        if (wrows >= 64)
-            sk_read_add<false>(sum, pp, wrows, lr);
-        else if (wrows > 0)
-            sk_read_add<true>(sum, pp, wrows, lr);
+                for (int e = 0; e < 4; ++e) sum[jj][e] = sum[jj][e] + p[e];
+            }
+        }
+        float sa = 1.0f;
+        if constexpr (GRAN == GRAN_ROW) sa = ct.sA[r];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            v4f v = sum[jj];
+            if constexpr (GRAN == GRAN_ROW) {
+                const v4f s4 = *reinterpret_cast<const v4f*>(ct.sW + wn * 32 + jj * 16 + 4 * lk);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+            }
+            uint2 o;
+            o.x = bf16x2_rne(v[0], v[1]);
+            o.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + wn * 32 + jj * 16 + 4 * lk) = o;
+        }
     }
-    pipe_store<GRAN>(ct, sum, S.N, wm, wn, lr, lk);
 }
 
 }  // namespace
 
 // The large-M kernel addresses a tile with 32-bit buffer offsets (256 rows x
-// K bytes, so K <= 2^22) and counts tiles and steps in int.
+// K bytes, so K <= 2^22) and counts tiles and steps in int.  It takes M >=
+// 1024, and smaller M when the 256 x 256 tiles alone fill most of the chip
+// (>= 192 of them: e.g. the gate_up projection at M = 512 runs 30% faster
+// than on the small-M kernel).
 bool gemm_small_path(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles2 = ((M + BM2 - 1) / BM2) * (N / BN2);
-    return !(M >= 1024 && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
+    return !((M >= 1024 || tiles2 >= 192) && N % BN2 == 0 && K <= (int64_t(1) << 22) &&
              (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31));
 }
 
@@ -1684,12 +1688,13 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         if (hipError_t e = hipGetLastError()) return e;
         if (steps % grid != 0 || (steps / grid) % (K / BK) != 0) {  // some tile is split
             if (gran == GRAN_BLOCK)
-                hipLaunchKernelGGL(k_sk_reduce<GRAN_BLOCK>, dim3((unsigned)tiles),
+                hipLaunchKernelGGL(k_sk_reduce<GRAN_BLOCK>, dim3((unsigned)(tiles * kSkRedSplit)),
                                    dim3(kThreadsP), 0, st, S, tiles, grid,
                                    static_cast<const v4f*>(sk.part));
             else
-                hipLaunchKernelGGL(k_sk_reduce<GRAN_ROW>, dim3((unsigned)tiles), dim3(kThreadsP),
-                                   0, st, S, tiles, grid, static_cast<const v4f*>(sk.part));
+                hipLaunchKernelGGL(k_sk_reduce<GRAN_ROW>, dim3((unsigned)(tiles * kSkRedSplit)),
+                                   dim3(kThreadsP), 0, st, S, tiles, grid,
+                                   static_cast<const v4f*>(sk.part));
         }
         return hipGetLastError();
     }

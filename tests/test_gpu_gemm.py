@@ -57,12 +57,15 @@ def test_block_small_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1024, 256, 256), (1100, 768, 640), (2047, 512, 1152),
-                                   (8200, 2304, 256), (1024, 512, 128), (4352, 4096, 128)])
+                                   (8200, 2304, 256), (1024, 512, 128), (4352, 4096, 128),
+                                   (700, 16384, 256)])
 def test_block_large_m_shapes(M, N, K):
     # 8200 x 2304: 33 x 9 = 297 tiles of 256 x 256 on 256 workgroups, so some
     # workgroups run two tiles; the last row tile holds 8 rows.  K = 128: one
     # K block per tile (1024 x 512: one block per workgroup; 4352 x 4096: 272
-    # tiles, a new tile at every block of the workgroups that run two)
+    # tiles, a new tile at every block of the workgroups that run two).
+    # 700 x 16384: 3 x 64 = 192 tiles, enough for the large-M kernel below
+    # M = 1024; the last row tile holds 188 rows
     say(f"block GEMM (large-M kernel) {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + N + K)
     W = synth.weight(N, K, seed=N + K + 1)
@@ -71,7 +74,8 @@ def test_block_large_m_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (130, 384, 512), (77, 256, 5120),
-                                   (1100, 768, 640), (1024, 256, 4096), (8200, 2304, 256)])
+                                   (1100, 768, 640), (1024, 256, 4096), (8200, 2304, 256),
+                                   (700, 16384, 256)])
 def test_row_small_shapes(M, N, K):
     say(f"row GEMM {M}x{N}x{K}")
     X = synth.act_col_outliers(M, K, seed=M + 3)
