@@ -31,10 +31,10 @@
 //   * Operand tiles are staged in LDS by direct-to-LDS 16-byte loads, with
 //     16-byte chunks of each 128-byte tile row XOR-swizzled (swz) so the
 //     operand reads are free of bank conflicts.
-//   k_gemm_pp   (M >= 1024, block scales): persistent, 256 x 256 tile, two
+//   k_gemm_pp   (M >= 1024, block or dense E8M0 scales): persistent, 256 x 256 tile, two
 //     LDS stages, 8 waves in two groups one phase apart (one group reads
 //     fragments while the other multiplies).
-//   k_gemm_big  (M >= 1024, row and E8M0 scales, grouped): the same tile and
+//   k_gemm_big  (M >= 1024, row scales, batched E8M0, grouped): the same tile and
 //     stages, all 8 waves in step.
 //   k_gemm_pipe (small M, and the MoE grouped GEMM): persistent, 128 x 128
 //     tile, 8 waves, a ring of four LDS stages with three in flight.
@@ -763,15 +763,15 @@ __device__ __forceinline__ void pp_store_tile(v4f (&acc)[4][8], const BigTile& t
 struct PPCtx {
     const uint8_t* A;
     const uint8_t* W;
-    const float* sA;
-    const float* sW;
+    const uint8_t* sA;  // fp32 (block scales) or E8M0 bytes (MX), per row and K block
+    const uint8_t* sW;  // per 128-row weight block and K block, same type
     uint16_t* Y;
     BigGeom G;
     int tm_count, tn_count, first, nwg, NS, KB, K;
     int wave, wm, wn, lr, lk;
     int off0;  // lane's byte offset of its first A / W chunk of a block
-    int offa;  // group 1: lane's byte offset of its sA word at kb = 0
-    int offw;  // group 1: lane's byte offset of its sW word at kb = 0
+    int offa;  // group 1: lane's byte offset of its sA scale at kb = 0
+    int offw;  // group 1: lane's byte offset of its sW scale at kb = 0
 };
 
 // Tile k of this workgroup (its fields made provably wave-uniform, so the
@@ -786,12 +786,13 @@ __device__ __forceinline__ BigTile pp_tile(const PPCtx& c, int k) {
 
 // Sources of the blocks one wave loads: group 0 the W tile (r0), group 1 the
 // A tile (r0), its sA rows (r1) and sW blocks (r2).  Rows past M lie past the
-// A and sA resources, so their loads return zeros (never stored).
+// A and sA resources, so their loads return zeros (never stored).  SB: bytes
+// per scale (4: fp32 block scales, 1: E8M0).
 struct PPSrc {
     __amdgpu_buffer_rsrc_t r0, r1, r2;
 };
 
-template <int GRP>
+template <int GRP, int SB>
 __device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
     const BigTile t = pp_tile(c, tile);
     const int K = c.K, KB = c.KB;
@@ -802,8 +803,8 @@ __device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
         S.r1 = S.r2 = S.r0;
     } else {
         S.r0 = buffer_rsrc(c.A + row0 * K, t.rows * K);
-        S.r1 = buffer_rsrc(c.sA + row0 * KB, t.rows * KB * 4);
-        S.r2 = buffer_rsrc(c.sW + (n0 / BK) * KB, 2 * KB * 4);
+        S.r1 = buffer_rsrc(c.sA + row0 * KB * SB, t.rows * KB * SB);
+        S.r2 = buffer_rsrc(c.sW + (n0 / BK) * KB * SB, 2 * KB * SB);
     }
     return S;
 }
@@ -811,7 +812,7 @@ __device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
 // Cursor over the blocks a wave loads: block b, its tile and K block, and the
 // sources of that tile.  Blocks past the last one reload the last block into
 // their (free) stage, so the loads of a phase never depend on a branch.
-template <int GRP>
+template <int GRP, int SB>
 struct PPCur {
     int b, t, kb;
     PPSrc S;
@@ -820,14 +821,14 @@ struct PPCur {
         const int bc = b0 < c.NS ? b0 : c.NS - 1;
         t = bc / c.KB;
         kb = bc - t * c.KB;
-        S = pp_src<GRP>(c, t);
+        S = pp_src<GRP, SB>(c, t);
     }
     __device__ __forceinline__ void next(const PPCtx& c) {
         ++b;
         if (b < c.NS && ++kb == c.KB) {
             kb = 0;
             ++t;
-            S = pp_src<GRP>(c, t);
+            S = pp_src<GRP, SB>(c, t);
         }
     }
 };
@@ -837,45 +838,63 @@ struct PPCur {
 // p / 8, swizzled 16-byte column swz_pos of p % 8), and the scale words.
 // The wave with index q in its group covers chunks (i * 4 + q) * 64 + lane.
 // Group 1, load n of 10: n < 8 the A chunks with i = n, n = 8 its 64 sA rows,
-// n = 9 the two sW words (every wave of the group writes the same words).
-// Group 0, load n of 8: W half 1 of block cur (n < 4, i = n) or W half 0 of
-// block nxt (i = n - 4).
-__device__ __forceinline__ void pp_load1(uint8_t* lds, const PPCtx& c, const PPCur<1>& L, int o,
-                                         int n) {
+// n = 9 the two sW words (every wave of the group writes the same words); an
+// E8M0 scale lands zero-extended in its 32-bit word.  Group 0, load n of 8:
+// W half 1 of block cur (n < 4, i = n) or W half 0 of block nxt (i = n - 4).
+template <int SB>
+__device__ __forceinline__ void pp_load1(uint8_t* lds, const PPCtx& c, const PPCur<1, SB>& L,
+                                         int o, int n) {
     const int q = c.wave & 3, st = L.b & 1;
     uint8_t* la = lds + st * kStage2;
     if (n < 8)
         b2l(L.S.r0, la + (n * 4 + q) * 64 * 16, 16, o + n * 32 * c.K, L.kb * BK);
     else if (n == 8)
-        b2l(L.S.r1, lds + 2 * kStage2 + st * BM2 * 4 + q * 256, 4, c.offa, L.kb * 4);
+        b2l(L.S.r1, lds + 2 * kStage2 + st * BM2 * 4 + q * 256, SB, c.offa, L.kb * SB);
     else
-        b2l(L.S.r2, lds + kSw2 + st * 256, 4, c.offw, L.kb * 4);
+        b2l(L.S.r2, lds + kSw2 + st * 256, SB, c.offw, L.kb * SB);
 }
 
-__device__ __forceinline__ void pp_load0(uint8_t* lds, const PPCtx& c, const PPCur<0>& cur,
-                                         const PPCur<0>& nxt, int o, int n) {
+template <int SB>
+__device__ __forceinline__ void pp_load0(uint8_t* lds, const PPCtx& c, const PPCur<0, SB>& cur,
+                                         const PPCur<0, SB>& nxt, int o, int n) {
     const int q = c.wave & 3, h = n < 4 ? 1 : 0, i = n & 3;
-    const PPCur<0>& L = h ? cur : nxt;
+    const PPCur<0, SB>& L = h ? cur : nxt;
     uint8_t* lb = lds + (L.b & 1) * kStage2 + BM2 * BK;
     b2l(L.S.r0, lb + (h * 1024 + (i * 4 + q) * 64) * 16, 16, o + (h * 128 + i * 32) * c.K,
         L.kb * BK);
 }
 
+// The scales of a wave's K block: BLOCK, sA * sW per X fragment (sc); MX,
+// the E8M0 words of its X fragments' rows (sa) and of its weight block (sw).
+struct PPScales {
+    float sc[4];
+    int sa[4];
+    int sw;
+};
+
 // Memory phase of block s: the wave's X and W fragments and scales into
 // registers.
+template <int GRAN>
 __device__ __forceinline__ void pp_read(const uint8_t* lds, const PPCtx& c, int s, v8i (&x)[4],
-                                        v8i (&w)[8], float (&sc)[4]) {
+                                        v8i (&w)[8], PPScales& ps) {
     const int slot = s & 1;
     const uint8_t* la = lds + slot * kStage2;
     const uint8_t* lbw = la + BM2 * BK;
-    const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + slot * BM2 * 4);
-    const float sw = reinterpret_cast<const float*>(lds + kSw2 + slot * 256)[c.wn];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = frag(la, c.wm * 64 + i * 16 + c.lr, c.lk);
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j] = frag(lbw, c.wn * 128 + j * 16 + c.lr, c.lk);
+    if constexpr (GRAN == GRAN_BLOCK) {
+        const float* lsa = reinterpret_cast<const float*>(lds + 2 * kStage2 + slot * BM2 * 4);
+        const float sw = reinterpret_cast<const float*>(lds + kSw2 + slot * 256)[c.wn];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = lsa[c.wm * 64 + i * 16 + c.lr] * sw;
+        for (int i = 0; i < 4; ++i) ps.sc[i] = lsa[c.wm * 64 + i * 16 + c.lr] * sw;
+    } else {
+        const int* lsa = reinterpret_cast<const int*>(lds + 2 * kStage2 + slot * BM2 * 4);
+        ps.sw = reinterpret_cast<const int*>(lds + kSw2 + slot * 256)[c.wn];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps.sa[i] = lsa[c.wm * 64 + i * 16 + c.lr];
+    }
 }
 
 // The phase loop of group GRP (0: waves 0-3, 1: waves 4-7; group 1 enters
@@ -891,18 +910,19 @@ __device__ __forceinline__ void pp_read(const uint8_t* lds, const PPCtx& c, int 
 //     phase (2s + 2).
 // Each group has its own copy of the loop, so every wait is unconditional
 // and the compute phase is one straight block.
-template <int GRP>
-__device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>& cur) {
+template <int GRAN, int GRP>
+__device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
+                                        PPCur<GRP, GRAN == GRAN_MX ? 1 : 4>& cur) {
     v4f acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     v8i x[4], w[8];
-    float sc[4];
+    PPScales ps;
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const int NS = c.NS, KB = c.KB, wm = c.wm, wn = c.wn, lr = c.lr, lk = c.lk;
-    PPCur<GRP> nxt = cur;  // group 0: the block after cur
+    PPCur<GRP, GRAN == GRAN_MX ? 1 : 4> nxt = cur;  // group 0: the block after cur
 
     // the last product of a compute phase, promoted after its barrier so the
     // other group's first MFMA queues right behind it
@@ -915,7 +935,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>
         const bool stored = ckb == 0 && s > 0;
         if (stored)  // the previous tile is complete: store it
             pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
-        pp_read(lds, c, s, x, w, sc);
+        pp_read<GRAN>(lds, c, s, x, w, ps);
         __builtin_amdgcn_s_waitcnt(kLgkm0);  // fragments and scales in registers
         // the previous compute phase's loads; vector memory operations complete
         // in issue order, so the stores just issued need not be waited for
@@ -939,10 +959,15 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>
         v4f pr[2];
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
-            pr[n & 1] = mfma_f8(w[n >> 2], x[n & 3], zero);
-            if (n > 0) {
-                const int m = n - 1;
-                promote(acc[m & 3][m >> 2], pr[m & 1], sc[m & 3]);
+            if constexpr (GRAN == GRAN_BLOCK) {
+                pr[n & 1] = mfma_f8(w[n >> 2], x[n & 3], zero);
+                if (n > 0) {
+                    const int m = n - 1;
+                    promote(acc[m & 3][m >> 2], pr[m & 1], ps.sc[m & 3]);
+                }
+            } else {
+                acc[n & 3][n >> 2] =
+                    mfma_mx(w[n >> 2], x[n & 3], acc[n & 3][n >> 2], ps.sw, ps.sa[n & 3]);
             }
             const bool ld = GRP == 0 ? (n & 3) == 0 : (n % 3 == 0 && n <= 27);
             if (ld) {
@@ -954,17 +979,20 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>
             // MFMA; the 4 FMAs promoting the MFMA before it, plus the address
             // add of a chunk load; then the load
             const bool add = ld && (GRP == 0 || n / 3 < 8);
+            const bool fma = GRAN == GRAN_BLOCK && n > 0;
             __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            if (n > 0 && add)
+            if (fma && add)
                 __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
-            else if (n > 0)
+            else if (fma)
                 __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
             else if (add)
                 __builtin_amdgcn_sched_group_barrier(kSgValu, 1, 0);
             if (ld) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
         }
-        carry = pr[1];
-        carry_sc = sc[3];
+        if constexpr (GRAN == GRAN_BLOCK) {
+            carry = pr[1];
+            carry_sc = ps.sc[3];
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (GRP == 0) cur = nxt;
         pp_barrier();
@@ -979,14 +1007,20 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c, PPCur<GRP>
     pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
 }
 
+// GRAN_BLOCK (fp32 scales, promotion FMAs) or GRAN_MX (E8M0 scales applied by
+// the MX-scaled MFMA, which accumulates); dense (B = 1), N % 256 == 0.
+template <int GRAN>
 __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict__ A,
                                                        const uint8_t* __restrict__ W,
-                                                       const float* __restrict__ sA,
-                                                       const float* __restrict__ sW,
+                                                       const void* __restrict__ sA,
+                                                       const void* __restrict__ sW,
                                                        uint16_t* __restrict__ Y, BigGeom G) {
+    constexpr int SB = GRAN == GRAN_MX ? 1 : 4;  // bytes per scale
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
     PPCtx c;
-    c.A = A; c.W = W; c.sA = sA; c.sW = sW; c.Y = Y; c.G = G;
+    c.A = A; c.W = W; c.Y = Y; c.G = G;
+    c.sA = static_cast<const uint8_t*>(sA);
+    c.sW = static_cast<const uint8_t*>(sW);
     c.tm_count = (int)((G.M + BM2 - 1) / BM2);
     c.tn_count = (int)(G.N / BN2);
     const int T = c.tm_count * c.tn_count;
@@ -1009,13 +1043,13 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
     c.lr = lane & 15;
     c.lk = lane >> 4;
     c.off0 = (wq * 8 + (lane >> 3)) * c.K + swz_pos(lane >> 3, lane & 7) * 16;
-    c.offa = (wq * 64 + lane) * c.KB * 4;
-    c.offw = (lane & 1) * c.KB * 4;
+    c.offa = (wq * 64 + lane) * c.KB * SB;
+    c.offw = (lane & 1) * c.KB * SB;
     asm volatile("" ::"s"(Y));
     // prologue: all of block 0 and, of block 1, everything but W half 1
     // (group 0 loads it in its first compute phase)
     if (grp == 0) {
-        PPCur<0> cur, nxt;
+        PPCur<0, SB> cur, nxt;
         cur.start(c, 0);
         nxt.start(c, 0);
         const int o = c.off0;
@@ -1026,9 +1060,9 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
         for (int n = 4; n < 8; ++n) pp_load0(lds, c, cur, nxt, o, n);  // W half 0 of block 1
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         pp_barrier();
-        pp_loop<0>(lds, c, nxt);  // cur = block 1
+        pp_loop<GRAN, 0>(lds, c, nxt);  // cur = block 1
     } else {
-        PPCur<1> cur;
+        PPCur<1, SB> cur;
         cur.start(c, 0);
         const int o = c.off0;
 #pragma unroll
@@ -1039,7 +1073,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         pp_barrier();
         pp_barrier();  // group 1 runs one phase behind
-        pp_loop<1>(lds, c, cur);
+        pp_loop<GRAN, 1>(lds, c, cur);
     }
 }
 
@@ -1654,7 +1688,8 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         // the ping-pong kernel addresses a tile's output rows with 32-bit
         // buffer offsets (256 rows x N bf16)
         if (gran == GRAN_BLOCK && N <= (int64_t(1) << 22))
-            hipLaunchKernelGGL(k_gemm_pp, dim3(grid), dim3(kThreads2), 0, st, A, Wp, a_s, w_s, Yp,
+            hipLaunchKernelGGL(k_gemm_pp<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
+                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
                                G);
         else if (gran == GRAN_BLOCK)
             hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
@@ -1751,6 +1786,15 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
     const int64_t tiles = B * ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
     const unsigned grid = (unsigned)(tiles < 256 ? tiles : 256);  // one per CU
     const BigGeom G{M, N, K, (int)B};
+    // dense, full 256-column tiles: the ping-pong kernel (32-bit offsets into
+    // 256 output rows x N bf16)
+    if (B == 1 && N % BN2 == 0 && N <= (int64_t(1) << 22)) {
+        hipLaunchKernelGGL(k_gemm_pp<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
+                           static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
+                           static_cast<const void*>(a_s), static_cast<const void*>(w_s),
+                           static_cast<uint16_t*>(y), G);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_gemm_big<GRAN_MX, false>), dim3(grid), dim3(kThreads2), 0, st,
                        static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                        static_cast<const void*>(a_s), static_cast<const void*>(w_s),
