@@ -31,10 +31,10 @@
 //   * Operand tiles are staged in LDS by direct-to-LDS 16-byte loads, with
 //     16-byte chunks of each 128-byte tile row XOR-swizzled (swz) so the
 //     operand reads are free of bank conflicts.
-//   k_gemm_pp   (M >= 1024, block or dense E8M0 scales): persistent, 256 x 256 tile, two
+//   k_gemm_pp   (M >= 1024; block, row or dense E8M0 scales): persistent, 256 x 256 tile, two
 //     LDS stages, 8 waves in two groups one phase apart (one group reads
 //     fragments while the other multiplies).
-//   k_gemm_big  (M >= 1024, row scales, batched E8M0, grouped): the same tile and
+//   k_gemm_big  (batched E8M0, grouped; N > 2^22): the same tile and
 //     stages, all 8 waves in step.
 //   k_gemm_pipe (small M, and the MoE grouped GEMM): persistent, 128 x 128
 //     tile, 8 waves, a ring of four LDS stages with three in flight.
@@ -889,11 +889,30 @@ __device__ __forceinline__ void pp_read(const uint8_t* lds, const PPCtx& c, int 
         const float sw = reinterpret_cast<const float*>(lds + kSw2 + slot * 256)[c.wn];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ps.sc[i] = lsa[c.wm * 64 + i * 16 + c.lr] * sw;
-    } else {
+    } else if constexpr (GRAN == GRAN_MX) {
         const int* lsa = reinterpret_cast<const int*>(lds + 2 * kStage2 + slot * BM2 * 4);
         ps.sw = reinterpret_cast<const int*>(lds + kSw2 + slot * 256)[c.wn];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ps.sa[i] = lsa[c.wm * 64 + i * 16 + c.lr];
+    }
+}
+
+// Row scales (GRAN_ROW): the tile's accumulators times sA[row] * sW[col],
+// once, before the store (the MFMA accumulated the unscaled products).
+__device__ __forceinline__ void pp_row_scale(v4f (&acc)[4][8], const PPCtx& c, const BigTile& t,
+                                             int wn, int wm, int lr, int lk) {
+    const float* sa = reinterpret_cast<const float*>(c.sA);
+    const float* sw = reinterpret_cast<const float*>(c.sW) + (int64_t)t.tn * BN2 + wn * 128 + 4 * lk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + lr;
+        const float a = sa[(int64_t)t.tm * BM2 + (r < t.rows ? r : t.rows - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const v4f b = *reinterpret_cast<const v4f*>(sw + j * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] * (a * b[e]);
+        }
     }
 }
 
@@ -933,8 +952,11 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
         // ---- memory phase of block s ----
         promote(acc[3][7], carry, carry_sc);
         const bool stored = ckb == 0 && s > 0;
-        if (stored)  // the previous tile is complete: store it
-            pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
+        if (stored) {  // the previous tile is complete: store it
+            const BigTile t = pp_tile(c, ct - 1);
+            if constexpr (GRAN == GRAN_ROW) pp_row_scale(acc, c, t, wn, wm, lr, lk);
+            pp_store_tile(acc, t, c.Y, (int)c.G.N, wn, wm, lr, lk);
+        }
         pp_read<GRAN>(lds, c, s, x, w, ps);
         __builtin_amdgcn_s_waitcnt(kLgkm0);  // fragments and scales in registers
         // the previous compute phase's loads; vector memory operations complete
@@ -965,20 +987,24 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
                     const int m = n - 1;
                     promote(acc[m & 3][m >> 2], pr[m & 1], ps.sc[m & 3]);
                 }
-            } else {
+            } else if constexpr (GRAN == GRAN_MX) {
                 acc[n & 3][n >> 2] =
                     mfma_mx(w[n >> 2], x[n & 3], acc[n & 3][n >> 2], ps.sw, ps.sa[n & 3]);
+            } else {
+                acc[n & 3][n >> 2] = mfma_f8(w[n >> 2], x[n & 3], acc[n & 3][n >> 2]);
             }
-            const bool ld = GRP == 0 ? (n & 3) == 0 : (n % 3 == 0 && n <= 27);
+            // group 0: 8 loads, one per 4 MFMAs; group 1: 10 (8 without
+            // per-block scales), one per 3 (4)
+            const bool ld = GRP == 0 || GRAN == GRAN_ROW ? (n & 3) == 0 : (n % 3 == 0 && n <= 27);
             if (ld) {
                 if constexpr (GRP == 0)
                     pp_load0(lds, c, cur, nxt, o, n >> 2);
                 else
-                    pp_load1(lds, c, cur, o, n / 3);
+                    pp_load1(lds, c, cur, o, GRAN == GRAN_ROW ? n >> 2 : n / 3);
             }
             // MFMA; the 4 FMAs promoting the MFMA before it, plus the address
             // add of a chunk load; then the load
-            const bool add = ld && (GRP == 0 || n / 3 < 8);
+            const bool add = ld && (GRP == 0 || GRAN == GRAN_ROW || n / 3 < 8);
             const bool fma = GRAN == GRAN_BLOCK && n > 0;
             __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
             if (fma && add)
@@ -1004,11 +1030,14 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
     if (GRP == 0) pp_barrier();  // the barrier count of group 1's offset
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last compute phase's loads
     promote(acc[3][7], carry, carry_sc);
-    pp_store_tile(acc, pp_tile(c, ct - 1), c.Y, (int)c.G.N, wn, wm, lr, lk);
+    const BigTile t = pp_tile(c, ct - 1);
+    if constexpr (GRAN == GRAN_ROW) pp_row_scale(acc, c, t, wn, wm, lr, lk);
+    pp_store_tile(acc, t, c.Y, (int)c.G.N, wn, wm, lr, lk);
 }
 
-// GRAN_BLOCK (fp32 scales, promotion FMAs) or GRAN_MX (E8M0 scales applied by
-// the MX-scaled MFMA, which accumulates); dense (B = 1), N % 256 == 0.
+// GRAN_BLOCK (fp32 scales, promotion FMAs), GRAN_MX (E8M0 scales applied by
+// the MX-scaled MFMA, which accumulates) or GRAN_ROW (the MFMA accumulates,
+// per-row x per-column scales at the store); dense (B = 1), N % 256 == 0.
 template <int GRAN>
 __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict__ A,
                                                        const uint8_t* __restrict__ W,
@@ -1016,6 +1045,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
                                                        const void* __restrict__ sW,
                                                        uint16_t* __restrict__ Y, BigGeom G) {
     constexpr int SB = GRAN == GRAN_MX ? 1 : 4;  // bytes per scale
+    constexpr int NL1 = GRAN == GRAN_ROW ? 8 : 10;  // group 1's loads per block
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
     PPCtx c;
     c.A = A; c.W = W; c.Y = Y; c.G = G;
@@ -1066,10 +1096,10 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
         cur.start(c, 0);
         const int o = c.off0;
 #pragma unroll
-        for (int n = 0; n < 10; ++n) pp_load1(lds, c, cur, o, n);  // block 0
+        for (int n = 0; n < NL1; ++n) pp_load1(lds, c, cur, o, n);  // block 0
         cur.next(c);
 #pragma unroll
-        for (int n = 0; n < 10; ++n) pp_load1(lds, c, cur, o, n);  // block 1
+        for (int n = 0; n < NL1; ++n) pp_load1(lds, c, cur, o, n);  // block 1
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         pp_barrier();
         pp_barrier();  // group 1 runs one phase behind
@@ -1695,6 +1725,10 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
             hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
                                static_cast<const void*>(w_s), Yp, G, nullptr, 0);
+        else if (N <= (int64_t(1) << 22))
+            hipLaunchKernelGGL(k_gemm_pp<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
+                               static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
+                               G);
         else
             hipLaunchKernelGGL((k_gemm_big<GRAN_ROW, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
