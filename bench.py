@@ -493,7 +493,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
         "traffic": recorded_traffic(),
-        "kernel": "block-scaled FP8 GEMM k_gemm_pp<0>, the 144 M=8192 launches of a "
+        "kernel": "block-scaled FP8 GEMM k_gemm_pp<0, false>, the 144 M=8192 launches of a "
                   "step",
     }
 

@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (source hash and file locations)
 import synth  # noqa: E402  (the dense shapes)
 
-KERNEL = "k_gemm_pp<0>"  # the dense block-scaled GEMM of the M=8192 linears
+KERNEL = "k_gemm_pp<0, false>"  # the dense block-scaled GEMM of the M=8192 linears
 
 
 def per_dispatch(folder: str, counter: str, name_filter) -> list[float]:
@@ -76,7 +76,7 @@ def main():
         alg += M * K + N * K + 4 * (M * (K // 128) + (N // 128) * (K // 128)) + 2 * M * N
     alg /= len(synth.DENSE_SHAPES)
 
-    print("# HBM traffic: block-scaled GEMM `k_gemm_pp<0>`, the M=8192 dense linears\n")
+    print("# HBM traffic: block-scaled GEMM `k_gemm_pp<0, false>`, the M=8192 dense linears\n")
     print("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own "
           "rocprofv3 run, over one step of the four M=8192 linears (qkv, o, gate_up, down; "
           "one launch each), scaled by the same counters over a plain 1 GiB device copy.\n")

@@ -542,6 +542,42 @@ __device__ __forceinline__ void big_store(v4f (&acc)[4][8], const BigTile& t, ui
 
 constexpr int kMaxExpertsBig = 1024;  // expert table size of the grouped form
 
+// The expert tables of a grouped large-M launch, built by wave 0 into tab (LDS):
+// pre[e] (e <= E) the prefix over experts of ceil(rows_e / 256) * tn_count,
+// then rlo[e] and rhi[e], expert e's rows [offsets[e], offsets[e + 1])
+// clamped to [0, M].  The caller synchronizes the workgroup before use.
+__device__ __forceinline__ void big_groups(uint8_t* tab, const int32_t* offsets, int E, int64_t M,
+                                           int tn_count) {
+    int32_t* s_pre = reinterpret_cast<int32_t*>(tab);
+    int32_t* s_rlo = s_pre + kMaxExpertsBig + 1;
+    int32_t* s_rhi = s_rlo + kMaxExpertsBig;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            int cnt = 0;
+            if (e < E) {
+                int64_t lo = offsets[e], hi = offsets[e + 1];
+                lo = lo < 0 ? 0 : (lo > M ? M : lo);
+                hi = hi < lo ? lo : (hi > M ? M : hi);
+                cnt = (int)((hi - lo + BM2 - 1) / BM2) * tn_count;
+                s_rlo[e] = (int32_t)lo;
+                s_rhi[e] = (int32_t)hi;
+            }
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int up = __shfl_up(incl, o);
+                if (lane >= o) incl += up;
+            }
+            if (e < E) s_pre[e] = base + incl - cnt;
+            base += __shfl(incl, 63);
+        }
+        if (lane == 0) s_pre[E] = base;
+    }
+}
+
 // Persistent: workgroup b runs on XCD b % 8; the XCD's workgroups share a
 // contiguous range of logical tiles and take them round-robin.  The steps
 // (tile, K block) of one workgroup form one stream through the two LDS
@@ -564,36 +600,10 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_big(const uint8_t* __restric
     BigGroups grp{};
     if constexpr (GROUPED) {
         // prefix over experts of their tile counts, and their row ranges (wave 0)
-        int32_t* s_pre = reinterpret_cast<int32_t*>(lds + kLds2);
-        int32_t* s_rlo = s_pre + kMaxExpertsBig + 1;
-        int32_t* s_rhi = s_rlo + kMaxExpertsBig;
-        if (threadIdx.x < 64) {
-            const int lane = threadIdx.x;
-            int base = 0;
-            for (int e0 = 0; e0 < E; e0 += 64) {
-                const int e = e0 + lane;
-                int cnt = 0;
-                if (e < E) {
-                    int64_t lo = offsets[e], hi = offsets[e + 1];
-                    lo = lo < 0 ? 0 : (lo > G.M ? G.M : lo);
-                    hi = hi < lo ? lo : (hi > G.M ? G.M : hi);
-                    cnt = (int)((hi - lo + BM2 - 1) / BM2) * tn_count;
-                    s_rlo[e] = (int32_t)lo;
-                    s_rhi[e] = (int32_t)hi;
-                }
-                int incl = cnt;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int up = __shfl_up(incl, o);
-                    if (lane >= o) incl += up;
-                }
-                if (e < E) s_pre[e] = base + incl - cnt;
-                base += __shfl(incl, 63);
-            }
-            if (lane == 0) s_pre[E] = base;
-        }
+        big_groups(lds + kLds2, offsets, E, G.M, tn_count);
         __syncthreads();
-        grp = BigGroups{s_pre, s_rlo, s_rhi, E};
+        const int32_t* s_pre = reinterpret_cast<const int32_t*>(lds + kLds2);
+        grp = BigGroups{s_pre, s_pre + kMaxExpertsBig + 1, s_pre + 2 * kMaxExpertsBig + 1, E};
         T = s_pre[E];
     }
     auto tile_of = [&](int logical) {
@@ -754,8 +764,7 @@ __device__ __forceinline__ void pp_store(v4f (&acc)[4][8], __amdgpu_buffer_rsrc_
 // Store tile k's block of this wave.
 __device__ __forceinline__ void pp_store_tile(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
                                               int N, int wn, int wm, int lr, int lk) {
-    const __amdgpu_buffer_rsrc_t Yr =
-        buffer_rsrc(Y + (int64_t)t.tm * BM2 * N, t.rows * N * 2);
+    const __amdgpu_buffer_rsrc_t Yr = buffer_rsrc(Y + t.row0 * N, t.rows * N * 2);
     pp_store(acc, Yr, N, t.tn * BN2 + wn * 128, wm, lr, lk);
 }
 
@@ -768,6 +777,8 @@ struct PPCtx {
     uint16_t* Y;
     BigGeom G;
     int tm_count, tn_count, first, nwg, NS, KB, K;
+    bool grouped;     // MoE: tiles over the expert tables in grp
+    BigGroups grp;
     int wave, wm, wn, lr, lk;
     int off0;  // lane's byte offset of its first A / W chunk of a block
     int offa;  // group 1: lane's byte offset of its sA scale at kb = 0
@@ -776,11 +787,17 @@ struct PPCtx {
 
 // Tile k of this workgroup (its fields made provably wave-uniform, so the
 // buffer resources built from them stay in scalar registers).
+// row0 is the first row of A and Y, e the weight batch (the expert).
 __device__ __forceinline__ BigTile pp_tile(const PPCtx& c, int k) {
-    BigTile t = big_tile(c.first + k * c.nwg, c.tm_count, c.tn_count, c.G);
-    t.tm = __builtin_amdgcn_readfirstlane(t.tm);
+    BigTile t = c.grouped ? big_tile_grouped(c.first + k * c.nwg, c.tn_count, c.G, c.grp)
+                          : big_tile(c.first + k * c.nwg, c.tm_count, c.tn_count, c.G);
+    if (!c.grouped) t.row0 = (int64_t)t.tm * BM2;
     t.tn = __builtin_amdgcn_readfirstlane(t.tn);
     t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)t.row0);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)t.row0 >> 32));
+    t.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
     return t;
 }
 
@@ -796,7 +813,7 @@ template <int GRP, int SB>
 __device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
     const BigTile t = pp_tile(c, tile);
     const int K = c.K, KB = c.KB;
-    const int64_t row0 = (int64_t)t.tm * BM2, n0 = (int64_t)t.tn * BN2;
+    const int64_t row0 = t.row0, n0 = (int64_t)t.e * c.G.N + (int64_t)t.tn * BN2;
     PPSrc S;
     if (GRP == 0) {
         S.r0 = buffer_rsrc(c.W + n0 * K, BN2 * K);
@@ -906,7 +923,7 @@ __device__ __forceinline__ void pp_row_scale(v4f (&acc)[4][8], const PPCtx& c, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wm * 64 + i * 16 + lr;
-        const float a = sa[(int64_t)t.tm * BM2 + (r < t.rows ? r : t.rows - 1)];
+        const float a = sa[t.row0 + (r < t.rows ? r : t.rows - 1)];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const v4f b = *reinterpret_cast<const v4f*>(sw + j * 16);
@@ -1038,22 +1055,37 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
 // GRAN_BLOCK (fp32 scales, promotion FMAs), GRAN_MX (E8M0 scales applied by
 // the MX-scaled MFMA, which accumulates) or GRAN_ROW (the MFMA accumulates,
 // per-row x per-column scales at the store); dense (B = 1), N % 256 == 0.
-template <int GRAN>
+// GROUPED (block scales): the MoE form over E experts, expert e's rows
+// [offsets[e], offsets[e + 1]) of A and Y against W[e] (G.M = total rows).
+template <int GRAN, bool GROUPED = false>
 __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict__ A,
                                                        const uint8_t* __restrict__ W,
                                                        const void* __restrict__ sA,
                                                        const void* __restrict__ sW,
-                                                       uint16_t* __restrict__ Y, BigGeom G) {
+                                                       uint16_t* __restrict__ Y, BigGeom G,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int E) {
     constexpr int SB = GRAN == GRAN_MX ? 1 : 4;  // bytes per scale
     constexpr int NL1 = GRAN == GRAN_ROW ? 8 : 10;  // group 1's loads per block
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2];
+    // one LDS object for the stage ring and (grouped) the expert tables
+    constexpr int kTab = GROUPED ? (3 * kMaxExpertsBig + 1) * 4 : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds2 + kTab];
     PPCtx c;
     c.A = A; c.W = W; c.Y = Y; c.G = G;
     c.sA = static_cast<const uint8_t*>(sA);
     c.sW = static_cast<const uint8_t*>(sW);
     c.tm_count = (int)((G.M + BM2 - 1) / BM2);
     c.tn_count = (int)(G.N / BN2);
-    const int T = c.tm_count * c.tn_count;
+    c.grouped = GROUPED;
+    c.grp = BigGroups{};
+    int T = c.tm_count * c.tn_count;
+    if constexpr (GROUPED) {
+        big_groups(lds + kLds2, offsets, E, G.M, c.tn_count);
+        __syncthreads();
+        const int32_t* s_pre = reinterpret_cast<const int32_t*>(lds + kLds2);
+        c.grp = BigGroups{s_pre, s_pre + kMaxExpertsBig + 1, s_pre + 2 * kMaxExpertsBig + 1, E};
+        T = s_pre[E];
+    }
     c.K = (int)G.K;
     c.KB = c.K / BK;
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
@@ -1720,7 +1752,7 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         if (gran == GRAN_BLOCK && N <= (int64_t(1) << 22))
             hipLaunchKernelGGL(k_gemm_pp<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
                                static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
-                               G);
+                               G, nullptr, 0);
         else if (gran == GRAN_BLOCK)
             hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
@@ -1728,7 +1760,7 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         else if (N <= (int64_t(1) << 22))
             hipLaunchKernelGGL(k_gemm_pp<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
                                static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
-                               G);
+                               G, nullptr, 0);
         else
             hipLaunchKernelGGL((k_gemm_big<GRAN_ROW, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
@@ -1799,6 +1831,12 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
     if (T >= 192 * E && K <= (int64_t(1) << 22) && max_tiles < (int64_t(1) << 31) &&
         (max_tiles / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
         const BigGeom G{T, N, K, 1};
+        if (N % BN2 == 0 && N <= (int64_t(1) << 22)) {  // full tiles: the ping-pong kernel
+            hipLaunchKernelGGL((k_gemm_pp<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
+                               dim3(kThreads2), 0, st, S.A, S.W, static_cast<const void*>(a_s),
+                               static_cast<const void*>(w_s), S.Y, G, offsets, (int)E);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
                            dim3(kThreads2), 0, st, S.A, S.W, static_cast<const void*>(a_s),
                            static_cast<const void*>(w_s), S.Y, G, offsets, (int)E);
@@ -1826,7 +1864,7 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
         hipLaunchKernelGGL(k_gemm_pp<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
                            static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                            static_cast<const void*>(a_s), static_cast<const void*>(w_s),
-                           static_cast<uint16_t*>(y), G);
+                           static_cast<uint16_t*>(y), G, nullptr, 0);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((k_gemm_big<GRAN_MX, false>), dim3(grid), dim3(kThreads2), 0, st,
