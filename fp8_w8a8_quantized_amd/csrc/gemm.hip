@@ -31,13 +31,15 @@
 //   * Operand tiles are staged in LDS by direct-to-LDS 16-byte loads, with
 //     16-byte chunks of each 128-byte tile row XOR-swizzled (swz) so the
 //     operand reads are free of bank conflicts.
-//   k_gemm_pp   (M >= 1024; block, row or dense E8M0 scales): persistent, 256 x 256 tile, two
-//     LDS stages, 8 waves in two groups one phase apart (one group reads
-//     fragments while the other multiplies).
-//   k_gemm_big  (batched E8M0, grouped; N > 2^22): the same tile and
+//   k_gemm_pp   (M >= 1024 or >= 192 tiles; block, row or dense E8M0
+//     scales; the MoE grouped GEMM when experts average >= 192 rows):
+//     persistent, 256 x 256 tile, two LDS stages, 8 waves in two groups one
+//     phase apart (one group reads fragments while the other multiplies).
+//   k_gemm_big  (batched E8M0, N % 256 == 128, N > 2^22): the same tile and
 //     stages, all 8 waves in step.
-//   k_gemm_pipe (small M, and the MoE grouped GEMM): persistent, 128 x 128
-//     tile, 8 waves, a ring of four LDS stages with three in flight.
+//   k_gemm_pipe / k_gemm_sk (small M, sparser MoE routing): persistent,
+//     128 x 128 tile, 8 waves, a ring of four LDS stages with three in
+//     flight; k_gemm_sk splits the K steps of all tiles evenly (stream-K).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"

@@ -273,9 +273,10 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   scaled and added in fp32), output rounded to bf16 (nearest even).
  *   bias must be NULL (FP8_ERR_ARG otherwise).  K % 128 != 0 or
  *   N % 128 != 0 -> FP8_ERR_SHAPE.  M is any value >= 0.
- *   Small M (below 1024; also N % 256 != 0 or K > 2^22) splits the K
- *   steps of all tiles evenly over the CUs (stream-K) and sums split tiles in
- *   a fixed order in a second kernel, so repeated calls give identical bytes.
+ *   Small M (below 1024 with fewer than 192 tiles of 256 x 256; also
+ *   N % 256 != 0 or K > 2^22) splits the K steps of all tiles evenly over the
+ *   CUs (stream-K) and sums split tiles in a fixed order in a second kernel,
+ *   so repeated calls give identical bytes.
  *   That needs a workspace of 32 MiB for the partial tiles, which the library
  *   allocates on the first such call on each (device, stream) and keeps until
  *   the process ends.
