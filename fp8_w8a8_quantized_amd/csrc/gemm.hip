@@ -737,10 +737,13 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void pp_store(v4f (&acc)[4][8], __amdgpu_buffer_rsrc_t Yr, int ldy,
                                          int col0, int wm, int lr, int lk) {
     const int cq = 16 * (lk & 1) + 8 * (lk >> 1);  // lane's column inside a 32-column pair
+    // the lane's byte offset of row wm * 64 + lr, recomputed here: kept across
+    // the whole loop, its four row offsets would take registers it lacks
+    int off0 = ((wm * 64 + lr) * ldy + col0 + cq) * 2;
+    asm volatile("" : "+v"(off0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + lr;
-        const int off = (r * ldy + col0 + cq) * 2;
+        const int off = off0 + i * 16 * ldy * 2;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const v4f& a = acc[i][2 * p];
@@ -962,13 +965,14 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
     const int NS = c.NS, KB = c.KB, wm = c.wm, wn = c.wn, lr = c.lr, lk = c.lk;
     PPCur<GRP, GRAN == GRAN_MX ? 1 : 4> nxt = cur;  // group 0: the block after cur
 
-    // the last product of a compute phase, promoted after its barrier so the
-    // other group's first MFMA queues right behind it
-    v4f carry = zero;
-    float carry_sc = 0.0f;
+    // the last two products of a compute phase, promoted after its barrier so
+    // the other group's first MFMA queues right behind them
+    v4f carry = zero, carry2 = zero;
+    float carry_sc = 0.0f, carry2_sc = 0.0f;
     int ct = 0, ckb = 0;  // compute cursor: tile, K block
     for (int s = 0; s < NS; ++s) {
         // ---- memory phase of block s ----
+        promote(acc[2][7], carry2, carry2_sc);
         promote(acc[3][7], carry, carry_sc);
         const bool stored = ckb == 0 && s > 0;
         if (stored) {  // the previous tile is complete: store it
@@ -997,14 +1001,14 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
         int o = c.off0;
         asm volatile("" : "+v"(o));  // recomputed per phase, not held across the loop
         __builtin_amdgcn_sched_barrier(0);
-        v4f pr[2];
+        v4f pr[3];
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
             if constexpr (GRAN == GRAN_BLOCK) {
-                pr[n & 1] = mfma_f8(w[n >> 2], x[n & 3], zero);
-                if (n > 0) {
-                    const int m = n - 1;
-                    promote(acc[m & 3][m >> 2], pr[m & 1], ps.sc[m & 3]);
+                pr[n % 3] = mfma_f8(w[n >> 2], x[n & 3], zero);
+                if (n > 1) {
+                    const int m = n - 2;
+                    promote(acc[m & 3][m >> 2], pr[m % 3], ps.sc[m & 3]);
                 }
             } else if constexpr (GRAN == GRAN_MX) {
                 acc[n & 3][n >> 2] =
@@ -1024,7 +1028,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
             // MFMA; the 4 FMAs promoting the MFMA before it, plus the address
             // add of a chunk load; then the load
             const bool add = ld && (GRP == 0 || GRAN == GRAN_ROW || n / 3 < 8);
-            const bool fma = GRAN == GRAN_BLOCK && n > 0;
+            const bool fma = GRAN == GRAN_BLOCK && n > 1;
             __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
             if (fma && add)
                 __builtin_amdgcn_sched_group_barrier(kSgValu, 5, 0);
@@ -1035,7 +1039,9 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
             if (ld) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
         }
         if constexpr (GRAN == GRAN_BLOCK) {
-            carry = pr[1];
+            carry2 = pr[30 % 3];
+            carry2_sc = ps.sc[2];
+            carry = pr[31 % 3];
             carry_sc = ps.sc[3];
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1048,6 +1054,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
     }
     if (GRP == 0) pp_barrier();  // the barrier count of group 1's offset
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the last compute phase's loads
+    promote(acc[2][7], carry2, carry2_sc);
     promote(acc[3][7], carry, carry_sc);
     const BigTile t = pp_tile(c, ct - 1);
     if constexpr (GRAN == GRAN_ROW) pp_row_scale(acc, c, t, wn, wm, lr, lk);
