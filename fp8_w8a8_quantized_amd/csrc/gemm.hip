@@ -35,7 +35,7 @@
 //     scales; the MoE grouped GEMM when experts average >= 192 rows):
 //     persistent, 256 x 256 tile, two LDS stages, 8 waves in two groups one
 //     phase apart (one group reads fragments while the other multiplies).
-//   k_gemm_big  (batched E8M0, N % 256 == 128, N > 2^22): the same tile and
+//   k_gemm_big  (batched E8M0, N % 256 == 128, N >= 2^22): the same tile and
 //     stages, all 8 waves in step.
 //   k_gemm_pipe / k_gemm_sk (small M, sparser MoE routing): persistent,
 //     128 x 128 tile, 8 waves, a ring of four LDS stages with three in
@@ -1757,8 +1757,8 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
         const unsigned grid = (unsigned)(tiles2 < 256 ? tiles2 : 256);  // one per CU
         const BigGeom G{M, N, K, 1};
         // the ping-pong kernel addresses a tile's output rows with 32-bit
-        // buffer offsets (256 rows x N bf16)
-        if (gran == GRAN_BLOCK && N <= (int64_t(1) << 22))
+        // buffer offsets (256 rows x N bf16 < 2^31 bytes)
+        if (gran == GRAN_BLOCK && N < (int64_t(1) << 22))
             hipLaunchKernelGGL(k_gemm_pp<GRAN_BLOCK>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
                                static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
                                G, nullptr, 0);
@@ -1766,7 +1766,7 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
             hipLaunchKernelGGL((k_gemm_big<GRAN_BLOCK, false>), dim3(grid), dim3(kThreads2), 0,
                                st, A, Wp, static_cast<const void*>(a_s),
                                static_cast<const void*>(w_s), Yp, G, nullptr, 0);
-        else if (N <= (int64_t(1) << 22))
+        else if (N < (int64_t(1) << 22))
             hipLaunchKernelGGL(k_gemm_pp<GRAN_ROW>, dim3(grid), dim3(kThreads2), 0, st, A, Wp,
                                static_cast<const void*>(a_s), static_cast<const void*>(w_s), Yp,
                                G, nullptr, 0);
@@ -1840,7 +1840,7 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
     if (T >= 192 * E && K <= (int64_t(1) << 22) && max_tiles < (int64_t(1) << 31) &&
         (max_tiles / 256 + 1) * (K / BK) < (int64_t(1) << 31)) {
         const BigGeom G{T, N, K, 1};
-        if (N % BN2 == 0 && N <= (int64_t(1) << 22)) {  // full tiles: the ping-pong kernel
+        if (N % BN2 == 0 && N < (int64_t(1) << 22)) {  // full tiles: the ping-pong kernel
             hipLaunchKernelGGL((k_gemm_pp<GRAN_BLOCK, true>), dim3((unsigned)kPersistentGrid),
                                dim3(kThreads2), 0, st, S.A, S.W, static_cast<const void*>(a_s),
                                static_cast<const void*>(w_s), S.Y, G, offsets, (int)E);
@@ -1869,7 +1869,7 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
     const BigGeom G{M, N, K, (int)B};
     // dense, full 256-column tiles: the ping-pong kernel (32-bit offsets into
     // 256 output rows x N bf16)
-    if (B == 1 && N % BN2 == 0 && N <= (int64_t(1) << 22)) {
+    if (B == 1 && N % BN2 == 0 && N < (int64_t(1) << 22)) {
         hipLaunchKernelGGL(k_gemm_pp<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
                            static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                            static_cast<const void*>(a_s), static_cast<const void*>(w_s),
