@@ -309,9 +309,12 @@ int fp8_batched_gemm_a8w8_mxscale(const void* a, const void* w, const void* a_s,
     if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8_ERR_ALIGN;
     if (int st = device_check()) return st;
+    fp8k::GemmWorkspace ws{};
+    const bool have_ws =
+        fp8k::mx_small_path(B, M, N) && gemm_workspace(as_stream(stream), &ws);
     return launched(fp8k::launch_batched_gemm_mx(a, w, static_cast<const uint8_t*>(a_s),
                                                  static_cast<const uint8_t*>(w_s), y, B, M, N, K,
-                                                 as_stream(stream)));
+                                                 have_ws ? &ws : nullptr, as_stream(stream)));
 }
 
 int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream) {

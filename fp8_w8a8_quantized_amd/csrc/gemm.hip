@@ -1205,12 +1205,13 @@ struct PipeLoad {
                 s.offa[i] = ra * k + c * 16;
                 s.offw[i] = r * k + c * 16;
             }
-            if constexpr (GRAN == GRAN_BLOCK) {
+            if constexpr (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) {
+                constexpr int sb = GRAN == GRAN_MX ? 1 : 4;  // bytes per scale
                 const int r = (wave & 1) * 64 + lane;
                 const int rr = r < t.rows ? r : t.rows - 1;
-                s.sa = buffer_rsrc(t.sA, t.rows * kbn * 4);
-                s.sw = buffer_rsrc(t.sW, kbn * 4);
-                s.offsa = rr * kbn * 4;
+                s.sa = buffer_rsrc(t.sA, t.rows * kbn * sb);
+                s.sw = buffer_rsrc(t.sW, kbn * sb);
+                s.offsa = rr * kbn * sb;
             }
         }
     }
@@ -1228,10 +1229,12 @@ __device__ __forceinline__ void stage_pipe(uint8_t* lds, int st, const PipeLoad<
             b2l(L.s.a, la + pbase * 16, 16, L.s.offa[i], kb * BK);
             b2l(L.s.w, lb + pbase * 16, 16, L.s.offw[i], kb * BK);
         }
-        if constexpr (GRAN == GRAN_BLOCK) {
-            b2l(L.s.sa, la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256, 4,
-                L.s.offsa, kb * 4);
-            b2l(L.s.sw, la + kSwP + wave * 256, 4, 0, kb * 4);  // every lane the same word
+        if constexpr (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) {
+            // an E8M0 byte lands zero-extended in its lane's 32-bit word
+            constexpr int sb = GRAN == GRAN_MX ? 1 : 4;
+            b2l(L.s.sa, la + kStageTileP + (wave >> 1) * (BMP * 4) + (wave & 1) * 256, sb,
+                L.s.offsa, kb * sb);
+            b2l(L.s.sw, la + kSwP + wave * 256, sb, 0, kb * sb);  // every lane the same word
         }
     } else {
         const Tile& t = L.t;
@@ -1257,7 +1260,7 @@ __device__ __forceinline__ void stage_pipe(uint8_t* lds, int st, const PipeLoad<
 template <int GRAN, bool BUF>
 __device__ __forceinline__ void wait_stage(int kb, int KB) {
     // loads per stage per thread
-    constexpr int per = GRAN == GRAN_BLOCK ? (BUF ? 6 : 5) : 4;
+    constexpr int per = GRAN == GRAN_BLOCK || GRAN == GRAN_MX ? (BUF ? 6 : 5) : 4;
     if (kb + 2 < KB)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per));
     else if (kb + 1 < KB)
@@ -1329,6 +1332,11 @@ __device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
     }
     t.A = S.A + row0 * S.K;
     t.sA = GRAN == GRAN_BLOCK ? S.sA + row0 * KB : S.sA + row0;
+    if constexpr (GRAN == GRAN_MX) {  // E8M0 bytes [M, KB] and [N/128, KB] (dense)
+        t.sA = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(S.sA) + row0 * KB);
+        t.sW = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(S.sW) +
+                                              (n0 / BNP) * KB);
+    }
     t.Y = S.Y + row0 * S.N + n0;
     t.rows = (int)rows;
     return t;
@@ -1336,7 +1344,8 @@ __device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
 
 // One K step of a 128 x 128 tile from LDS stage `la`: BLOCK promotes each
 // 16 x 16 product by its row scale x the weight block scale into acc (the FMA
-// of a product trails its MFMA by one); ROW accumulates in the MFMA.
+// of a product trails its MFMA by one); ROW accumulates in the MFMA; MX
+// accumulates in the MX-scaled MFMA, which applies the E8M0 scales.
 template <int GRAN, bool BUF>
 __device__ __forceinline__ void pipe_mma(const uint8_t* la, const float* sW, int kb,
                                          v4f (&acc)[4][2], int wm, int wn, int lr, int lk) {
@@ -1377,6 +1386,22 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* la, const float* sW, int
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[3][1][e] = __builtin_fmaf(prev[e], sc[3], acc[3][1][e]);
+    } else if constexpr (GRAN == GRAN_MX) {  // BUF: scales staged with the stage
+        const int sw = *reinterpret_cast<const int*>(la + kSwP + (wm | (wn << 1)) * 256);
+        const int* lsa = reinterpret_cast<const int*>(la + kStageTileP);
+        int sa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = lsa[wm * 64 + i * 16 + lr];
+        v8i wcur = frag(lb, wn * 32 + lr, lk);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            v8i wnext = wcur;
+            if (jj < 1) wnext = frag(lb, wn * 32 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][jj] = mfma_mx(wcur, x[i], acc[i][jj], sw, sa[i]);
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         v8i wcur = frag(lb, wn * 32 + lr, lk);
 #pragma unroll
@@ -1745,6 +1770,42 @@ bool gemm_small_path(int64_t M, int64_t N, int64_t K) {
              (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31));
 }
 
+// The small-M GEMM (128 x 128 tiles) of a dense tile space: stream-K with its
+// fixed-order reduce when a workspace is given, else one tile per workgroup at
+// a time.  MX shapes always take buffer loads (B K <= 2^22).
+template <int G>
+static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipStream_t st) {
+    const int64_t N = S.N, K = S.K;
+    const int64_t tiles = S.tm_count * (N / BNP);
+    const int64_t steps = tiles * (K / BK);
+    const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
+    if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
+        // stream-K: every workgroup gets at least one K step (grid <= steps)
+        const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
+        const SkWork sk{static_cast<v4f*>(ws->part)};
+        if (G == GRAN_MX || buf)
+            hipLaunchKernelGGL((k_gemm_sk<G, true>), dim3((unsigned)grid), dim3(kThreadsP), 0, st,
+                               S, tiles, sk);
+        else if constexpr (G != GRAN_MX)
+            hipLaunchKernelGGL((k_gemm_sk<G, false>), dim3((unsigned)grid), dim3(kThreadsP), 0,
+                               st, S, tiles, sk);
+        if (hipError_t e = hipGetLastError()) return e;
+        if (steps % grid != 0 || (steps / grid) % (K / BK) != 0)  // some tile is split
+            hipLaunchKernelGGL(k_sk_reduce<G>, dim3((unsigned)(tiles * kSkRedSplit)),
+                               dim3(kThreadsP), 0, st, S, tiles, grid,
+                               static_cast<const v4f*>(sk.part));
+        return hipGetLastError();
+    }
+    const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
+    if (G == GRAN_MX || buf)
+        hipLaunchKernelGGL((k_gemm_pipe<G, false, true>), dim3((unsigned)grid), dim3(kThreadsP),
+                           0, st, S, tiles);
+    else if constexpr (G != GRAN_MX)
+        hipLaunchKernelGGL((k_gemm_pipe<G, false, false>), dim3((unsigned)grid), dim3(kThreadsP),
+                           0, st, S, tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                        void* y, int64_t M, int64_t N, int64_t K, int gran,
                        const GemmWorkspace* ws, hipStream_t st) {
@@ -1780,45 +1841,8 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
     S.A = A; S.W = Wp; S.sA = a_s; S.sW = w_s; S.Y = Yp;
     S.M = M; S.N = N; S.K = K; S.E = 0;
     S.tm_count = (M + BMP - 1) / BMP;
-    const int64_t tiles = S.tm_count * (N / BNP);
-    const int64_t steps = tiles * (K / BK);
-    const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
-    if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
-        // stream-K: every workgroup gets at least one K step (grid <= steps)
-        const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
-        const SkWork sk{static_cast<v4f*>(ws->part)};
-#define FP8_SK(G, B) \
-    hipLaunchKernelGGL((k_gemm_sk<G, B>), dim3((unsigned)grid), dim3(kThreadsP), 0, st, S, tiles, sk)
-        if (gran == GRAN_BLOCK) {
-            if (buf) FP8_SK(GRAN_BLOCK, true); else FP8_SK(GRAN_BLOCK, false);
-        } else {
-            if (buf) FP8_SK(GRAN_ROW, true); else FP8_SK(GRAN_ROW, false);
-        }
-#undef FP8_SK
-        if (hipError_t e = hipGetLastError()) return e;
-        if (steps % grid != 0 || (steps / grid) % (K / BK) != 0) {  // some tile is split
-            if (gran == GRAN_BLOCK)
-                hipLaunchKernelGGL(k_sk_reduce<GRAN_BLOCK>, dim3((unsigned)(tiles * kSkRedSplit)),
-                                   dim3(kThreadsP), 0, st, S, tiles, grid,
-                                   static_cast<const v4f*>(sk.part));
-            else
-                hipLaunchKernelGGL(k_sk_reduce<GRAN_ROW>, dim3((unsigned)(tiles * kSkRedSplit)),
-                                   dim3(kThreadsP), 0, st, S, tiles, grid,
-                                   static_cast<const v4f*>(sk.part));
-        }
-        return hipGetLastError();
-    }
-    const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
-#define FP8_PIPE(G, B) \
-    hipLaunchKernelGGL((k_gemm_pipe<G, false, B>), dim3((unsigned)grid), dim3(kThreadsP), 0, st, S, \
-                       tiles)
-    if (gran == GRAN_BLOCK) {
-        if (buf) FP8_PIPE(GRAN_BLOCK, true); else FP8_PIPE(GRAN_BLOCK, false);
-    } else {
-        if (buf) FP8_PIPE(GRAN_ROW, true); else FP8_PIPE(GRAN_ROW, false);
-    }
-#undef FP8_PIPE
-    return hipGetLastError();
+    if (gran == GRAN_BLOCK) return launch_small<GRAN_BLOCK>(S, ws, st);
+    return launch_small<GRAN_ROW>(S, ws, st);
 }
 
 hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
@@ -1860,10 +1884,26 @@ hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, c
     return hipGetLastError();
 }
 
+bool mx_small_path(int64_t B, int64_t M, int64_t N) {
+    const int64_t tiles2 = ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
+    return B == 1 && M < 1024 && tiles2 < 192;
+}
+
 hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a_s,
                                   const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
-                                  int64_t K, hipStream_t st) {
+                                  int64_t K, const GemmWorkspace* ws, hipStream_t st) {
     if (M == 0 || B == 0) return hipSuccess;
+    if (mx_small_path(B, M, N)) {  // dense small M: the 128 x 128 kernels
+        TileSpace S{};
+        S.A = static_cast<const uint8_t*>(a);
+        S.W = static_cast<const uint8_t*>(w);
+        S.sA = reinterpret_cast<const float*>(a_s);  // E8M0 bytes, addressed as bytes
+        S.sW = reinterpret_cast<const float*>(w_s);
+        S.Y = static_cast<uint16_t*>(y);
+        S.M = M; S.N = N; S.K = K; S.E = 0;
+        S.tm_count = (M + BMP - 1) / BMP;
+        return launch_small<GRAN_MX>(S, ws, st);
+    }
     const int64_t tiles = B * ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
     const unsigned grid = (unsigned)(tiles < 256 ? tiles : 256);  // one per CU
     const BigGeom G{M, N, K, (int)B};

@@ -34,11 +34,7 @@ hipError_t launch_rmsnorm_quant(void* q, const void* x, void* res, float* s, con
                                 float eps, int64_t M, int64_t K, int group_size,
                                 hipStream_t st);
 hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, hipStream_t st);
-// B batches: A [M, B, K], W [B, N, K], E8M0 scales [M, B, K/128] and
-// [B, N/128, K/128], Y [M, B, N].  Requires B * K <= 2^22 and int tile counts.
-hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a_s,
-                                  const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
-                                  int64_t K, hipStream_t st);
+
 hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st);
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 
@@ -59,5 +55,13 @@ hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const flo
 hipError_t launch_grouped_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                                const int32_t* offsets, void* y, int64_t T, int64_t E,
                                int64_t N, int64_t K, hipStream_t st);
+// true when launch_batched_gemm_mx takes the small-M (128 x 128 tile) path
+bool mx_small_path(int64_t B, int64_t M, int64_t N);
+// B batches: A [M, B, K], W [B, N, K], E8M0 scales [M, B, K/128] and
+// [B, N/128, K/128], Y [M, B, N].  Requires B * K <= 2^22 and int tile counts.
+// ws as for launch_gemm (used by the small-M path, B == 1).
+hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a_s,
+                                  const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
+                                  int64_t K, const GemmWorkspace* ws, hipStream_t st);
 
 }  // namespace fp8k

@@ -328,6 +328,9 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const f
  *   N % 128 != 0, K % 128 != 0 or B * K > 2^22 -> FP8_ERR_SHAPE; M, B < 0 ->
  *   FP8_ERR_ARG; M == 0 or B == 0 launch nothing.  Scale pointers need no
  *   alignment.
+ *   Dense small M (B = 1, M below 1024 with fewer than 192 tiles of 256 x 256)
+ *   takes the stream-K kernels of fp8_gemm_a8w8_scaled and shares that call's
+ *   per-stream workspace (same allocation, ordering and graph-capture rules).
  */
 int fp8_batched_gemm_a8w8_mxscale(const void* a_e4m3, const void* w_e4m3, const void* a_s,
                                   const void* w_s, void* y_bf16, int64_t B, int64_t M, int64_t N,

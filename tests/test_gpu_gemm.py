@@ -453,6 +453,20 @@ def test_inverse_rope_quant_into_batched_mx_gemm():
     assert_rows_close(got, ref.reshape(rows.size * G, N), what="rope -> mx gemm")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 8960, 640), (3, 1024, 12288), (256, 4096, 4096)])
+def test_mx_small_m_stream_k(M, N, K):
+    # dense small M takes the stream-K kernels with E8M0 scales: tiles split
+    # across workgroups (200 x 8960: 140 tiles, ranges of 2-3 steps), a long K
+    # over few tiles, and a decode-size linear
+    say(f"MX GEMM small-M stream-K {M}x{N}x{K}")
+    X = synth.act_col_outliers(M, K, seed=M + N + 7)
+    W = synth.weight(N, K, seed=N + K + 9)
+    y, ref = _mx_pipeline(X, W)
+    assert_rows_close(y, ref, what=f"mx sk {M}x{N}x{K}")
+    y2, _ = _mx_pipeline(X, W, rows=[0])
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # fixed-order reduce
+
+
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_mx_dense_full_size_sampled(name):
     N, K = synth.DENSE_SHAPES[name]
