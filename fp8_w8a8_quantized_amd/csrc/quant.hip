@@ -540,8 +540,8 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
         const int64_t gidc = gid < G ? gid : G - 1;  // lanes past the end re-read the last group
         const int64_t t = gidc / GI, j = gidc - t * GI;
         const int64_t row = t * GI * 32;             // uint4 index of gu[t][0]
-        gv[u] = gu[row + j * 16 + li];
-        uv[u] = gu[row + GI * 16 + j * 16 + li];
+        gv[u] = load_nt16(gu + row + j * 16 + li);
+        uv[u] = load_nt16(gu + row + GI * 16 + j * 16 + li);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
         swiglu8(gv[u], uv[u], y);
         const GroupDiv g = group_div(max_16lanes(amax8(y)));
         if (gid < G) {
-            q[gid * 16 + li] = encode8(y, g);
+            store_nt8(q + gid * 16 + li, encode8(y, g));
             if (li == 0) s[gid] = g.s;
         }
     }
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(256) void k_quant_gather(const uint4* __restrict__ 
         unpack8(v[u], f);
         const GroupDiv g = group_div(max_16lanes(amax8(f)));
         if (gid < G) {
-            q[gid * 16 + li] = encode8(f, g);
+            store_nt8(q + gid * 16 + li, encode8(f, g));
             if (li == 0) s[gid] = g.s;
         }
     }
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
         p[u] = -1;
         if (gid < G) {  // both loads in bounds; an invalid position zeroes the row after
             p[u] = pos[gid / GK];
-            v[u] = o[(int64_t)gid * 16 + li];
+            v[u] = load_nt16(o + (int64_t)gid * 16 + li);
         }
     }
 #pragma unroll
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
 #pragma unroll
         for (int k = 0; k < 8; ++k) t8[k] = f[k] * inv;
         if (gid < G) {
-            q[(int64_t)gid * 16 + li] = e4m3x8(t8);
+            store_nt8(q + (int64_t)gid * 16 + li, e4m3x8(t8));
             if (li == 0) s[gid] = (uint8_t)(e + 127);
         }
     }
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(256) void k_tens_amax(TensBatch b) {
     const uint4* x = static_cast<const uint4*>(d.x);
     uint4 v[kTensVpt];
 #pragma unroll
-    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero(x, base + 256 * i, d.nvec);
+    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero_nt(x, base + 256 * i, d.nvec);
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < kTensVpt; ++i) {
@@ -766,14 +766,14 @@ __global__ __launch_bounds__(256) void k_tens_quant(TensBatch b) {
     const GroupDiv g = group_div(__uint_as_float(*reinterpret_cast<const uint32_t*>(d.s)));
     uint4 v[kTensVpt];
 #pragma unroll
-    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero(x, base + 256 * i, d.nvec);
+    for (int i = 0; i < kTensVpt; ++i) v[i] = load_or_zero_nt(x, base + 256 * i, d.nvec);
 #pragma unroll
     for (int i = 0; i < kTensVpt; ++i) {
         const int64_t idx = base + 256 * i;
         if (idx < d.nvec) {
             float f[8];
             unpack8(v[i], f);
-            q[idx] = encode8(f, g);
+            store_nt8(q + idx, encode8(f, g));
         }
     }
 }
