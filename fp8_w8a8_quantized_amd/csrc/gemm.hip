@@ -40,6 +40,9 @@
 //   k_gemm_pipe / k_gemm_sk (small M, sparser MoE routing): persistent,
 //     128 x 128 tile, 8 waves, a ring of four LDS stages with three in
 //     flight; k_gemm_sk splits the K steps of all tiles evenly (stream-K).
+//   k_gemm_dk (small M above 128 rows with >= 8 K steps per workgroup):
+//     stream-K on 256 x 128 tiles, so each weight block is read once per
+//     256 rows; three LDS stages, scales of 4 K blocks loaded together.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -1587,7 +1590,7 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
 //   of a workgroup's range, slot 1: its last), in register order (v4f index
 //   (slot * 8 + i * 2 + jj) * 512 + tid).
 // ---------------------------------------------------------------------------
-static_assert(kGemmWsPartBytes == kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
+static_assert(kGemmWsPartBytes >= kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
 
 struct SkWork {
     v4f* part;
@@ -1757,6 +1760,377 @@ __global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t ti
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K small-M kernel on 256 x 128 tiles (128 < M on the small-M path).
+// A 128-row tile reads a weight block once per row tile, so at M = 256 every
+// weight byte is fetched twice (the second time from the Infinity Cache at
+// best); the 256-row tile fetches it once and halves the K steps.  512
+// threads as 4 x 2 waves of 64 x 64 (wave w: rows 64 (w & 3), columns
+// 64 (w >> 2)); a ring of 3 stages (two in flight, 96 KiB) of 48 KiB operands
+// plus scales, filled by direct-to-LDS buffer loads (K <= 2^22).  Ranges,
+// partial slots and the fixed-order reduce work as in k_gemm_sk, with
+// 256 x 128 fp32 slots (v4f index (slot * 16 + i * 4 + jj) * 512 + tid).
+// ---------------------------------------------------------------------------
+constexpr int BMD = 256, NSD = 3;
+constexpr int kSaD = (BMD + BNP) * BK;        // 48 KiB of operands, then the 256 row scales
+constexpr int kSwD = kSaD + BMD * 4;          // the block scale (64 copies of one word)
+constexpr int kStageD = kSwD + 256;
+// SG (K / 128 % 4 == 0): the scales of 4 K blocks are loaded together, once
+// per 4 steps, into a ring of two group slots after the stages: 256 rows x 16
+// bytes (fp32; E8M0: 4 bytes per row) and 64 copies of the block scales.
+constexpr int kGrpD = NSD * kStageD, kGrpSlotD = BMD * 16 + 1024;
+constexpr int kLdsD = kGrpD + 2 * kGrpSlotD;
+static_assert(kLdsD <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+static_assert(kGemmWsPartBytes >= kPersistentGrid * 2 * BMD * BNP * 4, "partial slots");
+
+struct DkSrc {
+    __amdgpu_buffer_rsrc_t a, w, sa, sw;
+    int offa[4], offw[2], offsa;
+};
+
+// Tile `logical` of a dense space of ceil(M / 256) x N / 128 tiles, row tiles
+// of one column tile adjacent.
+template <int GRAN>
+__device__ __forceinline__ Tile dk_tile(const TileSpace& S, int64_t logical) {
+    const int64_t KB = S.K / BK;
+    const int64_t tm = logical % S.tm_count, tn = logical / S.tm_count;
+    const int64_t row0 = tm * BMD, n0 = tn * BNP;
+    Tile t;
+    t.rows = (int)((S.M - row0) < BMD ? (S.M - row0) : BMD);
+    t.A = S.A + row0 * S.K;
+    t.W = S.W + n0 * S.K;
+    if constexpr (GRAN == GRAN_MX) {  // E8M0 bytes [M, KB] and [N/128, KB]
+        t.sA = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(S.sA) + row0 * KB);
+        t.sW = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(S.sW) + tn * KB);
+    } else {
+        t.sA = GRAN == GRAN_BLOCK ? S.sA + row0 * KB : S.sA + row0;
+        t.sW = GRAN == GRAN_BLOCK ? S.sW + tn * KB : S.sW + n0;
+    }
+    t.Y = S.Y + row0 * S.N + n0;
+    return t;
+}
+
+template <int GRAN>
+__device__ __forceinline__ void dk_src(DkSrc& s, const Tile& t, int K, int KB, int wave,
+                                       int lane) {
+    s.a = buffer_rsrc(t.A, t.rows * K);
+    s.w = buffer_rsrc(t.W, BNP * K);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // LDS chunk p holds chunk swz_pos(r, p % 8) of row r = p / 8
+        const int p = (i * 8 + wave) * 64 + lane;
+        const int r = p >> 3;
+        const int ra = r < t.rows ? r : t.rows - 1;
+        s.offa[i] = ra * K + swz_pos(r, p & 7) * 16;
+        if (i < 2) s.offw[i] = r * K + swz_pos(r, p & 7) * 16;
+    }
+    if constexpr (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) {
+        constexpr int sb = GRAN == GRAN_MX ? 1 : 4;  // bytes per scale
+        const int r = (wave & 3) * 64 + lane;
+        const int rr = r < t.rows ? r : t.rows - 1;
+        s.sa = buffer_rsrc(t.sA, t.rows * KB * sb);
+        s.sw = buffer_rsrc(t.sW, KB * sb);
+        s.offsa = rr * KB * sb;
+    }
+}
+
+// Loads per stage per thread: 4 A chunks and 2 W chunks; with block or E8M0
+// scales waves 0-3 also load the row scales (one gather of 64 rows each) and
+// wave 4 the block scale.  A scale gather touches 64 cache lines, so it is
+// issued once per row, not once per wave.
+template <int GRAN>
+__device__ __forceinline__ bool dk_scale_wave(int wave) {
+    return (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) && wave < 5;
+}
+
+// Stage st of K block kb; with SG, grp is the group slot to fill when this
+// stage starts a scale group (null otherwise).
+template <int GRAN, bool SG>
+__device__ __forceinline__ void dk_stage(uint8_t* lds, int st, const DkSrc& s, int kb, int wave,
+                                         uint8_t* grp) {
+    uint8_t* la = lds + st * kStageD;
+    uint8_t* lb = la + BMD * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b2l(s.a, la + (i * 8 + wave) * 1024, 16, s.offa[i], kb * BK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) b2l(s.w, lb + (i * 8 + wave) * 1024, 16, s.offw[i], kb * BK);
+    if constexpr (SG) {
+        // fp32: 16 bytes (4 scales) per row; E8M0: 4 bytes, one 32-bit word
+        constexpr int gb = GRAN == GRAN_MX ? 4 : 16;
+        const int k0 = (kb & ~3) * (gb / 4);
+        if (grp != nullptr) {
+            if (wave < 4)
+                b2l(s.sa, grp + wave * 64 * gb, gb, s.offsa, k0);
+            else if (wave == 4)
+                b2l(s.sw, grp + BMD * 16, gb, 0, k0);  // every lane the same bytes
+        }
+    } else if constexpr (GRAN == GRAN_BLOCK || GRAN == GRAN_MX) {
+        // an E8M0 byte lands zero-extended in its lane's 32-bit word
+        constexpr int sb = GRAN == GRAN_MX ? 1 : 4;
+        if (wave < 4)
+            b2l(s.sa, la + kSaD + wave * 256, sb, s.offsa, kb * sb);
+        else if (wave == 4)
+            b2l(s.sw, la + kSwD, sb, 0, kb * sb);  // every lane the same word
+    }
+}
+
+// Wait for stage g: only stage g + 1 may stay in flight.  next_scale: stage
+// g + 1 carries a scale load for this wave.
+__device__ __forceinline__ void dk_wait(int g, int ng, bool next_scale) {
+    if (g + 1 >= ng)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else if (next_scale)  // wave-uniform
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(7));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
+}
+
+// This lane's scales for K block kb: BLOCK sc[i] = row scale x block scale,
+// MX the E8M0 bytes (sa[i], sw); from the stage (SG false) or the group slot.
+template <int GRAN, bool SG>
+__device__ __forceinline__ void dk_scales(const uint8_t* la, const uint8_t* gp, int kb, int wm,
+                                          int lr, float (&sc)[4], int (&sa)[4], int& sw) {
+    if constexpr (GRAN == GRAN_BLOCK) {
+        float w;
+        if constexpr (SG) {
+            w = *reinterpret_cast<const float*>(gp + BMD * 16 + (kb & 3) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[i] = *reinterpret_cast<const float*>(gp + (wm * 64 + i * 16 + lr) * 16 +
+                                                        (kb & 3) * 4) * w;
+        } else {
+            w = *reinterpret_cast<const float*>(la + kSwD);
+            const float* lsa = reinterpret_cast<const float*>(la + kSaD);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = lsa[wm * 64 + i * 16 + lr] * w;
+        }
+    } else if constexpr (GRAN == GRAN_MX) {
+        if constexpr (SG) {
+            const int sh = (kb & 3) * 8;
+            sw = (*reinterpret_cast<const int*>(gp + BMD * 16) >> sh) & 0xFF;
+            const int* lsa = reinterpret_cast<const int*>(gp);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] = (lsa[wm * 64 + i * 16 + lr] >> sh) & 0xFF;
+        } else {
+            sw = *reinterpret_cast<const int*>(la + kSwD);
+            const int* lsa = reinterpret_cast<const int*>(la + kSaD);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] = lsa[wm * 64 + i * 16 + lr];
+        }
+    }
+}
+
+// One K step of a wave's 64 x 64 block from stage `la` (promotion as in
+// pipe_mma: each product's FMAs trail its MFMA by one).
+template <int GRAN, bool SG>
+__device__ __forceinline__ void dk_mma(const uint8_t* la, const uint8_t* gp, int kb,
+                                       v4f (&acc)[4][4], int wm, int wn, int lr, int lk) {
+    const uint8_t* lb = la + BMD * BK;
+    v8i x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = frag(la, wm * 64 + i * 16 + lr, lk);
+    float sc[4];
+    int sa[4] = {0, 0, 0, 0}, sw = 0;
+    dk_scales<GRAN, SG>(la, gp, kb, wm, lr, sc, sa, sw);
+    if constexpr (GRAN == GRAN_BLOCK) {
+        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        v8i wcur = frag(lb, wn * 64 + lr, lk);
+        v4f prev;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            v8i wnext = wcur;
+            if (jj < 3) wnext = frag(lb, wn * 64 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v4f pk = mfma_f8(wcur, x[i], zero);
+                if (i > 0 || jj > 0) {
+                    const int pi = i > 0 ? i - 1 : 3, pj = i > 0 ? jj : jj - 1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[pi][pj][e] = __builtin_fmaf(prev[e], sc[pi], acc[pi][pj][e]);
+                }
+                prev = pk;
+            }
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[3][3][e] = __builtin_fmaf(prev[e], sc[3], acc[3][3][e]);
+    } else {
+        v8i wcur = frag(lb, wn * 64 + lr, lk);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            v8i wnext = wcur;
+            if (jj < 3) wnext = frag(lb, wn * 64 + (jj + 1) * 16 + lr, lk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (GRAN == GRAN_MX)
+                    acc[i][jj] = mfma_mx(wcur, x[i], acc[i][jj], sw, sa[i]);
+                else
+                    acc[i][jj] = mfma_f8(wcur, x[i], acc[i][jj]);
+            }
+            wcur = wnext;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// bf16 store of a wave's row fragment i (rows wm * 64 + 16 i + lr, 64
+// columns); ROW scales by the row and column scales first.
+template <int GRAN>
+__device__ __forceinline__ void dk_store_frag(const Tile& ct, const v4f (&v4)[4], int64_t N,
+                                              int r, int wn, int lk) {
+    if (r >= ct.rows) return;
+    float sa = 1.0f;
+    if constexpr (GRAN == GRAN_ROW) sa = ct.sA[r];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        v4f v = v4[jj];
+        if constexpr (GRAN == GRAN_ROW) {
+            const v4f s4 = *reinterpret_cast<const v4f*>(ct.sW + wn * 64 + jj * 16 + 4 * lk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+        }
+        uint2 o;
+        o.x = bf16x2_rne(v[0], v[1]);
+        o.y = bf16x2_rne(v[2], v[3]);
+        *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * N + wn * 64 + jj * 16 + 4 * lk) = o;
+    }
+}
+
+template <int GRAN, bool SG>
+__global__ __launch_bounds__(kThreadsP) void k_gemm_dk(TileSpace S, int64_t tiles, SkWork ws) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsD];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int64_t KB = S.K / BK, Wt = tiles * KB, G = gridDim.x;
+    // XCD-contiguous rank, as in k_gemm_sk
+    const int64_t bid = blockIdx.x, xcd = bid & 7;
+    const int64_t q8 = G >> 3, r8 = G & 7;
+    const int64_t c = xcd * q8 + (xcd < r8 ? xcd : r8) + (bid >> 3);
+    const int64_t u0 = sk_start(c, Wt, G), u1 = sk_start(c + 1, Wt, G);
+    const int ng = (int)(u1 - u0);
+    if (ng <= 0) return;  // whole workgroup leaves together
+    const int64_t t_first = u0 / KB;
+    const int K = (int)S.K, kbn = (int)KB;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int64_t l_t = t_first;  // tile and k block of the next stage to load
+    int l_kb = (int)(u0 - t_first * KB);
+    DkSrc src;
+    dk_src<GRAN>(src, dk_tile<GRAN>(S, l_t), K, kbn, wave, lane);
+    // SG: scale groups loaded (gl) and in use (gc); a group starts at a K block
+    // that is a multiple of 4 or at the first step of the range
+    int gl = 0, gc = -1;
+    auto group_slot = [&](bool starts) -> uint8_t* {
+        if (!SG || !starts) return nullptr;
+        return lds + kGrpD + ((gl++) & 1) * kGrpSlotD;
+    };
+#pragma unroll
+    for (int st = 0; st < NSD - 1; ++st) {
+        if (st < ng) {
+            dk_stage<GRAN, SG>(lds, st, src, l_kb, wave, group_slot(st == 0 || (l_kb & 3) == 0));
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_t;
+                if (l_t < tiles) dk_src<GRAN>(src, dk_tile<GRAN>(S, l_t), K, kbn, wave, lane);
+            }
+        }
+    }
+    int64_t c_t = t_first;  // tile being multiplied, its k block, where this range entered it
+    int kb = (int)(u0 - t_first * KB);
+    int kb_in = kb;
+    Tile ct = dk_tile<GRAN>(S, c_t);
+
+    for (int g = 0; g < ng; ++g) {
+        asm volatile("" ::: "memory");
+        {
+            const int kb1 = kb + 1 == kbn ? 0 : kb + 1;  // K block of stage g + 1
+            dk_wait(g, ng, dk_scale_wave<GRAN>(wave) && (!SG || (kb1 & 3) == 0));
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (g + NSD - 1 < ng) {  // refill the stage consumed at g - 1
+            dk_stage<GRAN, SG>(lds, (g + NSD - 1) % NSD, src, l_kb, wave,
+                               group_slot((l_kb & 3) == 0));
+            if (++l_kb == kbn) {
+                l_kb = 0;
+                ++l_t;
+                if (l_t < tiles) dk_src<GRAN>(src, dk_tile<GRAN>(S, l_t), K, kbn, wave, lane);
+            }
+        }
+        if (g == 0 || (kb & 3) == 0) ++gc;
+        dk_mma<GRAN, SG>(lds + (g % NSD) * kStageD, lds + kGrpD + (gc & 1) * kGrpSlotD, kb, acc,
+                         wm, wn, lr, lk);
+
+        if (kb == kbn - 1 || g == ng - 1) {  // this range's part of tile c_t is done
+            if (kb_in == 0 && kb == kbn - 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dk_store_frag<GRAN>(ct, acc[i], S.N, wm * 64 + i * 16 + lr, wn, lk);
+            } else {
+                const int slot = (c_t == t_first) ? 0 : 1;
+                v4f* mine = ws.part + (c * 2 + slot) * 16 * kThreadsP + tid;
+                const int wrows = ct.rows - wm * 64;  // rows of this wave that exist
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (i * 16 + lr < wrows)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            sk_put(mine + (i * 4 + jj) * kThreadsP, acc[i][jj]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (++kb == kbn) {
+            kb = 0;
+            kb_in = 0;
+            ++c_t;
+            if (c_t < tiles) ct = dk_tile<GRAN>(S, c_t);
+        }
+    }
+}
+
+// Sum of the partials of each split 256 x 128 tile in contributor order, then
+// the bf16 store; 4 workgroups per tile, workgroup i taking row fragment i of
+// every wave.
+template <int GRAN>
+__global__ __launch_bounds__(kThreadsP) void k_dk_reduce(TileSpace S, int64_t tiles, int64_t G,
+                                                        const v4f* __restrict__ part) {
+    const int64_t t = blockIdx.x >> 2, KB = S.K / BK, Wt = tiles * KB;
+    const int i = (int)(blockIdx.x & 3);
+    const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
+    if (c_lo == c_hi) return;  // stored whole by its workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3, wn = wave >> 2, lr = lane & 15, lk = lane >> 4;
+    const Tile ct = dk_tile<GRAN>(S, t);
+    const int r = wm * 64 + i * 16 + lr;
+    if (r >= ct.rows) return;
+    v4f sum[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) sum[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+        const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
+        const v4f* pp = part + (cc * 2 + sl) * 16 * kThreadsP + tid;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const v4f p = sk_get(pp + (i * 4 + jj) * kThreadsP);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[jj][e] = sum[jj][e] + p[e];
+        }
+    }
+    dk_store_frag<GRAN>(ct, sum, S.N, r, wn, lk);
+}
+
 }  // namespace
 
 // The large-M kernel addresses a tile with 32-bit buffer offsets (256 rows x
@@ -1779,6 +2153,35 @@ static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipS
     const int64_t tiles = S.tm_count * (N / BNP);
     const int64_t steps = tiles * (K / BK);
     const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
+    if (ws != nullptr && S.M > BMP && buf) {  // 256-row tiles: each weight block read once
+        TileSpace S2 = S;
+        S2.tm_count = (S.M + BMD - 1) / BMD;
+        const int64_t tiles2 = S2.tm_count * (N / BNP), steps2 = tiles2 * (K / BK);
+        // with fewer than 8 K steps per workgroup the larger stages' fill and
+        // partials cost more than the second weight read saves
+        if (steps2 >= 8 * kPersistentGrid && tiles2 <= kGemmWsMaxTiles &&
+            steps2 < (int64_t(1) << 31)) {
+            const int64_t grid = steps2 < kPersistentGrid ? steps2 : kPersistentGrid;
+            const SkWork sk{static_cast<v4f*>(ws->part)};
+            // scale groups of 4 K blocks: whole groups per row, aligned group loads
+            const int64_t salign = G == GRAN_MX ? 4 : 16;
+            const bool sg = G != GRAN_ROW && (K / BK) % 4 == 0 &&
+                            reinterpret_cast<uintptr_t>(S.sA) % salign == 0 &&
+                            reinterpret_cast<uintptr_t>(S.sW) % salign == 0;
+            if constexpr (G != GRAN_ROW)
+                if (sg)
+                    hipLaunchKernelGGL((k_gemm_dk<G, true>), dim3((unsigned)grid), dim3(kThreadsP),
+                                       0, st, S2, tiles2, sk);
+            if (!sg)
+                hipLaunchKernelGGL((k_gemm_dk<G, false>), dim3((unsigned)grid), dim3(kThreadsP),
+                                   0, st, S2, tiles2, sk);
+            if (hipError_t e = hipGetLastError()) return e;
+            if (steps2 % grid != 0 || (steps2 / grid) % (K / BK) != 0)  // some tile is split
+                hipLaunchKernelGGL(k_dk_reduce<G>, dim3((unsigned)(tiles2 * 4)), dim3(kThreadsP),
+                                   0, st, S2, tiles2, grid, static_cast<const v4f*>(sk.part));
+            return hipGetLastError();
+        }
+    }
     if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
         // stream-K: every workgroup gets at least one K step (grid <= steps)
         const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;

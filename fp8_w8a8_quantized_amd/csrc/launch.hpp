@@ -39,9 +39,9 @@ hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 
 // Workspace of the stream-K small-M GEMM (device memory, one per stream):
-// 256 workgroups x 2 partial 128 x 128 fp32 tiles.  Tile counts above
-// kGemmWsMaxTiles (one reduce workgroup per tile) run without stream-K.
-constexpr int64_t kGemmWsPartBytes = int64_t(256) * 2 * 128 * 128 * 4;
+// 256 workgroups x 2 partial tiles of up to 256 x 128 fp32.  Tile counts
+// above kGemmWsMaxTiles run without stream-K.
+constexpr int64_t kGemmWsPartBytes = int64_t(256) * 2 * 256 * 128 * 4;
 constexpr int64_t kGemmWsMaxTiles = int64_t(1) << 16;
 struct GemmWorkspace {
     void* part;

@@ -276,8 +276,9 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   Small M (below 1024 with fewer than 192 tiles of 256 x 256; also
  *   N % 256 != 0 or K > 2^22) splits the K steps of all tiles evenly over the
  *   CUs (stream-K) and sums split tiles in a fixed order in a second kernel,
- *   so repeated calls give identical bytes.
- *   That needs a workspace of 32 MiB for the partial tiles, which the library
+ *   so repeated calls give identical bytes.  Above 128 rows the tiles are
+ *   256 x 128 (each weight block read once per 256 rows), else 128 x 128.
+ *   That needs a workspace of 64 MiB for the partial tiles, which the library
  *   allocates on the first such call on each (device, stream) and keeps until
  *   the process ends.
  *   Calls on one stream share it (they are ordered); calls on different

@@ -101,7 +101,8 @@ def test_dense_linears_full_size_sampled(name, M):
 
 
 # Small-M shapes run stream-K: the tiles' K steps are split evenly over the
-# workgroups and a tile cut between workgroups is summed by its last arriver.
+# workgroups and a tile cut between workgroups is summed, in a fixed order, by
+# a second kernel.
 @pytest.mark.parametrize("M,N,K", [(200, 8960, 640),    # 140 tiles, ranges of 2-3 steps
                                    (1000, 5120, 384),   # 320 tiles (> one per CU)
                                    (3, 1024, 12288),    # 8 tiles, 96 steps each
@@ -114,10 +115,44 @@ def test_block_stream_k_shapes(M, N, K):
     assert_rows_close(y, ref, what=f"{M}x{N}x{K}")
 
 
+# Above 128 rows, a small-M GEMM with at least 8 K steps per workgroup runs
+# stream-K on 256 x 128 tiles: scales of 4 K blocks loaded together when
+# K / 128 % 4 == 0, per step otherwise; ragged M over two row tiles.
+DK_SHAPES = [(256, 8192, 4096),    # 64 tiles x 32 steps, grouped scale loads
+             (300, 2048, 8192),    # 2 row tiles, the second 44 rows
+             (160, 16384, 2176)]   # K / 128 = 17: per-step scale loads
+
+
+@pytest.mark.parametrize("M,N,K", DK_SHAPES)
+def test_block_stream_k_256_row_tiles(M, N, K):
+    say(f"block GEMM stream-K 256-row tiles {M}x{N}x{K}, sampled rows")
+    X = synth.act_col_outliers(M, K, seed=M + N + 3 * K)
+    W = synth.weight(N, K, seed=N + 3 * K)
+    rows = sample_rows(M, 24, seed=M + K)
+    y, ref = _block_pipeline(X, W, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what=f"dk {M}x{N}x{K}")
+    y2, _ = _block_pipeline(X, W, rows=[0])
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # fixed-order reduce
+
+
+@pytest.mark.parametrize("M,N,K", DK_SHAPES)
+def test_row_stream_k_256_row_tiles(M, N, K):
+    say(f"row GEMM stream-K 256-row tiles {M}x{N}x{K}, sampled rows")
+    X = synth.act_col_outliers(M, K, seed=M + 5)
+    W = synth.weight(N, K, seed=K + 7)
+    qa, sa = fp8.quantize_token(X.to(dev()))
+    qw, sw = fp8.quantize_token(W.to(dev()))
+    y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_ROW)
+    rows = sample_rows(M, 24, seed=M + N)
+    oqa, osa = oracle.quantize_token(X[torch.as_tensor(rows)])
+    oqw, osw = oracle.quantize_token(W)
+    ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_ROW)
+    assert_rows_close(y, ref, rows=rows, what=f"row dk {M}x{N}x{K}")
+
+
 def test_stream_k_repeatable_across_interleaved_shapes():
-    """Outputs do not depend on arrival order, and every launch leaves the
-    arrival counters zero: A, B, A give bit-identical A outputs, all within
-    tolerance of the oracle."""
+    """Outputs do not depend on timing or on the shapes run before: A, B, A
+    give bit-identical A outputs, all within tolerance of the oracle."""
     say("stream-K repeatability: shapes A, B, A on one stream")
     shapes = [(256, 4096, 12288), (96, 6144, 4096)]
     ops = []
@@ -463,6 +498,18 @@ def test_mx_small_m_stream_k(M, N, K):
     W = synth.weight(N, K, seed=N + K + 9)
     y, ref = _mx_pipeline(X, W)
     assert_rows_close(y, ref, what=f"mx sk {M}x{N}x{K}")
+    y2, _ = _mx_pipeline(X, W, rows=[0])
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # fixed-order reduce
+
+
+@pytest.mark.parametrize("M,N,K", DK_SHAPES)
+def test_mx_stream_k_256_row_tiles(M, N, K):
+    say(f"MX GEMM stream-K 256-row tiles {M}x{N}x{K}, sampled rows")
+    X = synth.act_col_outliers(M, K, seed=M + N + 11)
+    W = synth.weight(N, K, seed=N + K + 13)
+    rows = sample_rows(M, 24, seed=M + 2 * K)
+    y, ref = _mx_pipeline(X, W, rows=rows)
+    assert_rows_close(y, ref, rows=rows, what=f"mx dk {M}x{N}x{K}")
     y2, _ = _mx_pipeline(X, W, rows=[0])
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))  # fixed-order reduce
 
