@@ -178,9 +178,10 @@ def test_stream_k_repeatable_across_interleaved_shapes():
 
 
 def test_stream_k_concurrent_streams():
-    """Small-M GEMMs issued on two streams at once: each stream has its own
-    stream-K workspace, so the overlapping launches do not mix partials or
-    counters.  Every result matches the same GEMM run alone."""
+    """Small-M GEMMs issued on two streams at once (one on 256-row tiles, one
+    on 128-row tiles): each stream has its own stream-K workspace, so the
+    overlapping launches do not mix partials.  Every result matches the same
+    GEMM run alone."""
     say("stream-K GEMMs on two concurrent streams")
     shapes = [(256, 4096, 12288), (200, 6144, 4096)]
     ops, solo = [], []
