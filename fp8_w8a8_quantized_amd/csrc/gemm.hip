@@ -1760,6 +1760,89 @@ __global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t ti
     }
 }
 
+// k_sk_reduce for tiles with many contributors: SPLIT workgroups per tile
+// (8 or more), each taking NF = 8 / SPLIT of the eight
+// accumulator fragments (i * 2 + jj: rows wm * 64 + 16 i + lr, columns
+// wn * 32 + 16 jj + 4 lk) of every wave; one workgroup per tile left most of
+// the chip idle at decode shapes.  A thread sums one 16-byte value per
+// contributor and fragment, four such loads issued together (over 4 / NF
+// contributors) and added in contributor order.  A tile one workgroup covered whole exits
+// at once.  Threads map to accumulator fragments exactly as in the stream-K
+// kernel.
+template <int GRAN, int SPLIT>
+__global__ __launch_bounds__(kThreadsP) void k_sk_reduce_wide(TileSpace S, int64_t tiles, int64_t G,
+                                                        const v4f* __restrict__ part) {
+    constexpr int NF = 8 / SPLIT;
+    const int64_t t = blockIdx.x / SPLIT, KB = S.K / BK, Wt = tiles * KB;
+    const int f0 = (int)(blockIdx.x % SPLIT) * NF;
+    const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
+    if (c_lo == c_hi) return;  // stored whole by its workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1, lr = lane & 15, lk = lane >> 4;
+    const Tile ct = tile_at<GRAN, false>(S, t);
+    const int r = wm * 64 + (f0 >> 1) * 16 + lr;  // the NF fragments share a row
+    if (r >= ct.rows) return;
+    // contributor cc's partial slot (0 if its range starts in tile t), at this
+    // thread's first fragment
+    auto base = [&](int64_t cc) {
+        const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
+        return part + (cc * 2 + sl) * 8 * kThreadsP + f0 * kThreadsP + tid;
+    };
+    v4f sum[NF];
+#pragma unroll
+    for (int n = 0; n < NF; ++n) sum[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int QB = NF >= 4 ? 1 : 4 / NF;  // contributors per batch: 4 loads in flight
+    int64_t cc = c_lo;
+    for (; cc + QB - 1 <= c_hi; cc += QB) {
+        v4f p[QB][NF];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const v4f* b = base(cc + q);
+#pragma unroll
+            for (int n = 0; n < NF; ++n) p[q][n] = sk_get(b + n * kThreadsP);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+            for (int n = 0; n < NF; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum[n][e] = sum[n][e] + p[q][n][e];
+    }
+    for (; cc <= c_hi; ++cc) {
+        const v4f* b = base(cc);
+#pragma unroll
+        for (int n = 0; n < NF; ++n) {
+            const v4f p = sk_get(b + n * kThreadsP);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[n][e] = sum[n][e] + p[e];
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+        const int col = wn * 32 + ((f0 + n) & 1) * 16 + 4 * lk;
+        v4f v = sum[n];
+        if constexpr (GRAN == GRAN_ROW) {
+            const float sa = ct.sA[r];
+            const v4f s4 = *reinterpret_cast<const v4f*>(ct.sW + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+        }
+        uint2 o;
+        o.x = bf16x2_rne(v[0], v[1]);
+        o.y = bf16x2_rne(v[2], v[3]);
+        *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + col) = o;
+    }
+}
+
+// The wide reduce (one fragment per workgroup, four contributors' loads in
+// flight) when each split tile has many contributors (ranges shorter than a
+// quarter of a tile); with up to four contributors a tile's reduce is short
+// and the narrow form, with fewer workgroups to start, is faster.
+__host__ inline bool reduce_wide(int64_t steps, int64_t grid, int64_t KB) {
+    return 4 * (steps / grid) < KB;
+}
+
 // ---------------------------------------------------------------------------
 // Stream-K small-M kernel on 256 x 128 tiles (128 < M on the small-M path).
 // A 128-row tile reads a weight block once per row tile, so at M = 256 every
@@ -2131,6 +2214,75 @@ __global__ __launch_bounds__(kThreadsP) void k_dk_reduce(TileSpace S, int64_t ti
     dk_store_frag<GRAN>(ct, sum, S.N, r, wn, lk);
 }
 
+// k_dk_reduce for tiles with many contributors: SPLIT workgroups per tile,
+// each taking NF = 16 / SPLIT of the sixteen fragments (i * 4 + jj) of every
+// wave, as k_sk_reduce_wide does.
+template <int GRAN, int SPLIT>
+__global__ __launch_bounds__(kThreadsP) void k_dk_reduce_wide(TileSpace S, int64_t tiles, int64_t G,
+                                                        const v4f* __restrict__ part) {
+    constexpr int NF = 16 / SPLIT;
+    const int64_t t = blockIdx.x / SPLIT, KB = S.K / BK, Wt = tiles * KB;
+    const int f0 = (int)(blockIdx.x % SPLIT) * NF;
+    const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
+    if (c_lo == c_hi) return;  // stored whole by its workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3, wn = wave >> 2, lr = lane & 15, lk = lane >> 4;
+    const Tile ct = dk_tile<GRAN>(S, t);
+    const int r = wm * 64 + (f0 >> 2) * 16 + lr;  // the NF fragments share a row
+    if (r >= ct.rows) return;
+    // contributor cc's partial slot (0 if its range starts in tile t), at this
+    // thread's first fragment
+    auto base = [&](int64_t cc) {
+        const int sl = (sk_start(cc, Wt, G) / KB == t) ? 0 : 1;
+        return part + (cc * 2 + sl) * 16 * kThreadsP + f0 * kThreadsP + tid;
+    };
+    v4f sum[NF];
+#pragma unroll
+    for (int n = 0; n < NF; ++n) sum[n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int QB = NF >= 4 ? 1 : 4 / NF;  // contributors per batch: 4 loads in flight
+    int64_t cc = c_lo;
+    for (; cc + QB - 1 <= c_hi; cc += QB) {
+        v4f p[QB][NF];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const v4f* b = base(cc + q);
+#pragma unroll
+            for (int n = 0; n < NF; ++n) p[q][n] = sk_get(b + n * kThreadsP);
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+#pragma unroll
+            for (int n = 0; n < NF; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum[n][e] = sum[n][e] + p[q][n][e];
+    }
+    for (; cc <= c_hi; ++cc) {
+        const v4f* b = base(cc);
+#pragma unroll
+        for (int n = 0; n < NF; ++n) {
+            const v4f p = sk_get(b + n * kThreadsP);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[n][e] = sum[n][e] + p[e];
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+        const int col = wn * 64 + ((f0 + n) & 3) * 16 + 4 * lk;
+        v4f v = sum[n];
+        if constexpr (GRAN == GRAN_ROW) {
+            const float sa = ct.sA[r];
+            const v4f s4 = *reinterpret_cast<const v4f*>(ct.sW + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = v[e] * (sa * s4[e]);
+        }
+        uint2 o;
+        o.x = bf16x2_rne(v[0], v[1]);
+        o.y = bf16x2_rne(v[2], v[3]);
+        *reinterpret_cast<uint2*>(ct.Y + (int64_t)r * S.N + col) = o;
+    }
+}
+
 }  // namespace
 
 // The large-M kernel addresses a tile with 32-bit buffer offsets (256 rows x
@@ -2177,8 +2329,15 @@ static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipS
                                    0, st, S2, tiles2, sk);
             if (hipError_t e = hipGetLastError()) return e;
             if (steps2 % grid != 0 || (steps2 / grid) % (K / BK) != 0)  // some tile is split
-                hipLaunchKernelGGL(k_dk_reduce<G>, dim3((unsigned)(tiles2 * 4)), dim3(kThreadsP),
-                                   0, st, S2, tiles2, grid, static_cast<const v4f*>(sk.part));
+            {
+                const v4f* part = static_cast<const v4f*>(sk.part);
+                if (reduce_wide(steps2, grid, K / BK))
+                    hipLaunchKernelGGL((k_dk_reduce_wide<G, 16>), dim3((unsigned)(tiles2 * 16)),
+                                       dim3(kThreadsP), 0, st, S2, tiles2, grid, part);
+                else
+                    hipLaunchKernelGGL(k_dk_reduce<G>, dim3((unsigned)(tiles2 * 4)),
+                                       dim3(kThreadsP), 0, st, S2, tiles2, grid, part);
+            }
             return hipGetLastError();
         }
     }
@@ -2194,9 +2353,15 @@ static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipS
                                st, S, tiles, sk);
         if (hipError_t e = hipGetLastError()) return e;
         if (steps % grid != 0 || (steps / grid) % (K / BK) != 0)  // some tile is split
-            hipLaunchKernelGGL(k_sk_reduce<G>, dim3((unsigned)(tiles * kSkRedSplit)),
-                               dim3(kThreadsP), 0, st, S, tiles, grid,
-                               static_cast<const v4f*>(sk.part));
+        {
+            const v4f* part = static_cast<const v4f*>(sk.part);
+            if (reduce_wide(steps, grid, K / BK))
+                hipLaunchKernelGGL((k_sk_reduce_wide<G, 8>), dim3((unsigned)(tiles * 8)),
+                                   dim3(kThreadsP), 0, st, S, tiles, grid, part);
+            else
+                hipLaunchKernelGGL(k_sk_reduce<G>, dim3((unsigned)(tiles * kSkRedSplit)),
+                                   dim3(kThreadsP), 0, st, S, tiles, grid, part);
+        }
         return hipGetLastError();
     }
     const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
