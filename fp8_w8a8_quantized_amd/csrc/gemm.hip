@@ -1835,6 +1835,17 @@ __global__ __launch_bounds__(kThreadsP) void k_sk_reduce_wide(TileSpace S, int64
     }
 }
 
+// Grid that deals whole tiles out evenly (n = ceil(tiles / 256) per
+// workgroup) when that keeps at least 3/4 of the CUs busy, else 0 (stream-K).
+// A split tile costs its partial stores and a second kernel that reads them
+// back; at decode shapes the chip's bandwidth, not each CU's, bounds the
+// GEMM, so idle CUs cost less (gate_up at M=256: 192 tiles on 192 CUs 46.7 µs,
+// stream-K over 256 CUs with its reduce 52.4 µs).
+__host__ inline int64_t whole_tile_grid(int64_t tiles) {
+    const int64_t n = (tiles + kPersistentGrid - 1) / kPersistentGrid;
+    return tiles % n == 0 && 4 * tiles >= 3 * kPersistentGrid * n ? tiles / n : 0;
+}
+
 // The wide reduce (one fragment per workgroup, four contributors' loads in
 // flight) when each split tile has many contributors (ranges shorter than a
 // quarter of a tile); with up to four contributors a tile's reduce is short
@@ -2313,7 +2324,9 @@ static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipS
         // partials cost more than the second weight read saves
         if (steps2 >= 8 * kPersistentGrid && tiles2 <= kGemmWsMaxTiles &&
             steps2 < (int64_t(1) << 31)) {
-            const int64_t grid = steps2 < kPersistentGrid ? steps2 : kPersistentGrid;
+            const int64_t whole = whole_tile_grid(tiles2);
+            const int64_t grid =
+                whole > 0 ? whole : (steps2 < kPersistentGrid ? steps2 : kPersistentGrid);
             const SkWork sk{static_cast<v4f*>(ws->part)};
             // scale groups of 4 K blocks: whole groups per row, aligned group loads
             const int64_t salign = G == GRAN_MX ? 4 : 16;
@@ -2342,8 +2355,11 @@ static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipS
         }
     }
     if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
-        // stream-K: every workgroup gets at least one K step (grid <= steps)
-        const int64_t grid = steps < kPersistentGrid ? steps : kPersistentGrid;
+        // stream-K: every workgroup gets at least one K step (grid <= steps),
+        // or whole tiles when they fill the chip evenly
+        const int64_t whole = whole_tile_grid(tiles);
+        const int64_t grid =
+            whole > 0 ? whole : (steps < kPersistentGrid ? steps : kPersistentGrid);
         const SkWork sk{static_cast<v4f*>(ws->part)};
         if (G == GRAN_MX || buf)
             hipLaunchKernelGGL((k_gemm_sk<G, true>), dim3((unsigned)grid), dim3(kThreadsP), 0, st,

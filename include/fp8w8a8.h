@@ -278,6 +278,8 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   CUs (stream-K) and sums split tiles in a fixed order in a second kernel,
  *   so repeated calls give identical bytes.  Above 128 rows the tiles are
  *   256 x 128 (each weight block read once per 256 rows), else 128 x 128.
+ *   When whole tiles fill at least 3/4 of the CUs evenly, each workgroup
+ *   takes whole tiles instead and no tile is split.
  *   That needs a workspace of 64 MiB for the partial tiles, which the library
  *   allocates on the first such call on each (device, stream) and keeps until
  *   the process ends.

@@ -150,6 +150,33 @@ def test_row_stream_k_256_row_tiles(M, N, K):
     assert_rows_close(y, ref, rows=rows, what=f"row dk {M}x{N}x{K}")
 
 
+# When whole tiles fill at least 3/4 of the CUs evenly, the small-M kernels
+# deal out whole tiles (no split tiles, no reduce): 192 tiles of 256 x 128,
+# 384 tiles of 128 x 128 (two per workgroup), 192 tiles of 128 x 128.
+WHOLE_SHAPES = [(200, 24576, 2048), (256, 24576, 1024), (100, 24576, 1024)]
+
+
+@pytest.mark.parametrize("gran", ["block", "row", "mx"])
+@pytest.mark.parametrize("M,N,K", WHOLE_SHAPES)
+def test_small_m_whole_tile_grids(M, N, K, gran):
+    say(f"{gran} GEMM small-M whole-tile grid {M}x{N}x{K}, sampled rows")
+    X = synth.act_col_outliers(M, K, seed=M + K + 17)
+    W = synth.weight(N, K, seed=N + K + 19)
+    rows = sample_rows(M, 16, seed=M + 3 * K)
+    if gran == "block":
+        y, ref = _block_pipeline(X, W, rows=rows)
+    elif gran == "mx":
+        y, ref = _mx_pipeline(X, W, rows=rows)
+    else:
+        qa, sa = fp8.quantize_token(X.to(dev()))
+        qw, sw = fp8.quantize_token(W.to(dev()))
+        y = fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_ROW)
+        oqa, osa = oracle.quantize_token(X[torch.as_tensor(rows)])
+        oqw, osw = oracle.quantize_token(W)
+        ref = oracle.gemm(oqa, oqw, osa, osw, oracle.GRAN_ROW)
+    assert_rows_close(y, ref, rows=rows, what=f"{gran} whole {M}x{N}x{K}")
+
+
 def test_stream_k_repeatable_across_interleaved_shapes():
     """Outputs do not depend on timing or on the shapes run before: A, B, A
     give bit-identical A outputs, all within tolerance of the oracle."""
