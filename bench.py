@@ -114,11 +114,12 @@ def one_gemm(M: int, N: int, K: int, reps: int):
     a = fp8.quantize_block(X)
     (w,) = fp8.requantize_weights([W], fp8.SCALE_F32)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((max(fp8.gemm_workspace_size(M, N, K), 16),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK, out=y)
+        fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK, out=y, workspace=ws)
     e1.record()
     torch.cuda.synchronize(dev)
     us = e0.elapsed_time(e1) * 1e3 / reps
@@ -310,6 +311,13 @@ def main():
         m = moe[which]
         mdescs[i] = fp8._WeightDesc(m["W"].data_ptr(), m["Wq"].data_ptr(), m["Ws"].data_ptr(),
                                     m["E"] * m["N"], m["K"])
+    # the small-M GEMMs' partial-tile workspace: one buffer of the largest size
+    # any shape queries, shared by the calls of the one stream
+    ws_bytes = max(int(L.fp8_gemm_workspace_size(M, N, K, fp8.GRAN_BLOCK))
+                   for (name, (N, K)) in shapes for M in Ms)
+    ws_bytes = max(ws_bytes, int(L.fp8_gemm_workspace_size(RM, RN, RK, fp8.GRAN_ROW)))
+    gws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    gwsa = (vp(gws.data_ptr()), gws.numel())
     torch.cuda.synchronize(dev)
 
     # ---- pre-marshalled calls of one step, grouped by kernel category ----
@@ -325,7 +333,8 @@ def main():
                 calls.append((f"gemm_m{M}", L.fp8_gemm_a8w8_scaled,
                               (vp(Xq[key].data_ptr()), vp(Wq[wi].data_ptr()),
                                vp(Xs[key].data_ptr()), vp(Ws[wi].data_ptr()), None,
-                               vp(Y[(j, M)].data_ptr()), M, N, K, fp8.GRAN_BLOCK, sptr)))
+                               vp(Y[(j, M)].data_ptr()), M, N, K, fp8.GRAN_BLOCK, *gwsa,
+                               sptr)))
     calls.append(("rmsnorm_quant", L.fp8_rmsnorm_quant,
                   (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hs.data_ptr()), vp(gamma.data_ptr()),
                    synth.RMS_EPS, RM, RK, 0, sptr)))
@@ -336,7 +345,7 @@ def main():
                   (vp(Wr.data_ptr()), RN, RK, vp(Wrq.data_ptr()), vp(Wrs.data_ptr()), sptr)))
     calls.append(("gemm_row", L.fp8_gemm_a8w8_scaled,
                   (vp(hq.data_ptr()), vp(Wrq.data_ptr()), vp(hs.data_ptr()), vp(Wrs.data_ptr()),
-                   None, vp(Yr.data_ptr()), RM, RN, RK, fp8.GRAN_ROW, sptr)))
+                   None, vp(Yr.data_ptr()), RM, RN, RK, fp8.GRAN_ROW, *gwsa, sptr)))
     calls.append(("requant_e8m0", L.fp8_requantize_weights,
                   (descs8, len(W), fp8.SCALE_E8M0, sptr)))
     for j, (name, (N, K)) in enumerate(shapes):
@@ -346,7 +355,8 @@ def main():
                        vp(Xs8[j].data_ptr()), sptr)))
         calls.append(("gemm_mx_m8192", L.fp8_batched_gemm_a8w8_mxscale,
                       (vp(Xq8[j].data_ptr()), vp(Wq8[j].data_ptr()), vp(Xs8[j].data_ptr()),
-                       vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, sptr)))
+                       vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, *gwsa,
+                       sptr)))
     calls.append(("quant_kv_tensor", L.fp8_quantize_tensors, (kvdescs, len(kv_x), sptr)))
     calls.append(("requant_e8m0_wo", L.fp8_requantize_weights, (rdesc, 1, fp8.SCALE_E8M0, sptr)))
     calls.append(("rope_quant_m8192", L.fp8_inverse_rope_group_quant,
@@ -356,7 +366,7 @@ def main():
                    sptr)))
     calls.append(("gemm_mx_wo_m8192", L.fp8_batched_gemm_a8w8_mxscale,
                   (vp(rq.data_ptr()), vp(rWq.data_ptr()), vp(rs.data_ptr()), vp(rWs.data_ptr()),
-                   vp(rY.data_ptr()), OG, OT, ON, OKG, sptr)))
+                   vp(rY.data_ptr()), OG, OT, ON, OKG, *gwsa, sptr)))
     calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
     # the expert chain: 1x128 quant of the routed rows, gate_up GEMM, SwiGLU +
     # 1x128 quant of its output, down GEMM

@@ -12,7 +12,9 @@ divisions and square roots stay correctly rounded (hipcc's default).
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import subprocess
 import sys
 
@@ -20,6 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8w8a8.so")
 SOURCES = ["api.hip", "quant.hip", "gemm.hip"]
+INCLUDE = os.path.join(os.path.dirname(HERE), "include", "fp8w8a8.h")
+HASH_TAG = b"FP8W8A8_SOURCE_SHA256="
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,11 +34,40 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """SHA-256 over every file the library is built from (csrc/ and the C
+    header), in name order."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".hpp", ".h")))
+    for path in files + [INCLUDE]:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def built_hash(lib: str = LIB):
+    """The source hash recorded in a built library (None if absent)."""
+    try:
+        with open(lib, "rb") as f:
+            m = re.search(re.escape(HASH_TAG) + rb"([0-9a-f]{64})", f.read())
+    except OSError:
+        return None
+    return m.group(1).decode() if m else None
+
+
+def is_current(lib: str = LIB) -> bool:
+    """True when ``lib`` exists and was built from the sources as they are."""
+    return built_hash(lib) == source_hash()
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``fp8_w8a8_quantized_amd/libfp8w8a8.so``."""
+    """Compile every HIP source into ``fp8_w8a8_quantized_amd/libfp8w8a8.so``,
+    recording the sources' hash in it (fp8_build_source_hash)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, f'-DFP8W8A8_SOURCE_SHA256="{source_hash()}"', *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -12,7 +12,6 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
-#include <vector>
 
 #include "../../include/fp8w8a8.h"
 #include "launch.hpp"
@@ -50,46 +49,25 @@ int launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// Stream-K workspace of the small-M GEMM (partial tiles), one per (device,
-// stream): allocated on the first GEMM call that needs it and held until the
-// process ends.  No allocation is attempted while the stream is being
-// captured into a graph: then the GEMM runs without stream-K.  Calls on one
-// stream are ordered, so they may share the workspace; calls on different
-// streams get their own.
-struct WsEntry {
-    int dev;
-    hipStream_t stream;
-    fp8k::GemmWorkspace ws;
-};
-std::mutex g_ws_mu;
-std::vector<WsEntry> g_ws;
+// Element counts whose byte sizes (up to 4 bytes per element) fit in int64.
+bool count_ok(int64_t rows, int64_t cols) { return rows <= INT64_MAX / 4 / cols; }
 
-bool gemm_workspace(hipStream_t st, fp8k::GemmWorkspace* out) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    for (const WsEntry& e : g_ws)
-        if (e.dev == dev && e.stream == st) {
-            *out = e.ws;
-            return true;
-        }
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
-        (void)hipGetLastError();
-        return false;
-    }
-    void* part = nullptr;
-    if (hipMalloc(&part, size_t(fp8k::kGemmWsPartBytes)) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    WsEntry e{dev, st, {part}};
-    g_ws.push_back(e);
-    *out = e.ws;
-    return true;
+// GEMM dimensions the kernels' index arithmetic covers: each below 2^31 and
+// every operand below 2^48 bytes (far past any device memory), so no tile or
+// step count overflows.
+bool gemm_dims_ok(int64_t M, int64_t N, int64_t K) {
+    const int64_t lim = int64_t(1) << 48;
+    return M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX && M * K < lim && N * K < lim &&
+           M * N < lim / 2;
+}
+
+// The workspace argument pair of the GEMMs: NULL with 0 bytes runs the plan
+// without a split; otherwise the pointer must be 16-byte aligned and hold at
+// least `need` bytes.
+int workspace_check(const void* ws, size_t bytes, int64_t need) {
+    if (ws == nullptr) return bytes == 0 ? FP8_OK : FP8_ERR_ARG;
+    if (!aligned(ws, 16)) return FP8_ERR_ALIGN;
+    return bytes >= (size_t)need ? FP8_OK : FP8_ERR_ARG;
 }
 
 }  // namespace
@@ -97,6 +75,14 @@ bool gemm_workspace(hipStream_t st, fp8k::GemmWorkspace* out) {
 extern "C" {
 
 int fp8_abi_version(void) { return FP8W8A8_ABI_VERSION; }
+
+#ifndef FP8W8A8_SOURCE_SHA256
+#define FP8W8A8_SOURCE_SHA256 "unknown"
+#endif
+// The tag makes the hash findable in the file without loading it.
+static const char kSourceHash[] = "FP8W8A8_SOURCE_SHA256=" FP8W8A8_SOURCE_SHA256;
+
+const char* fp8_build_source_hash(void) { return kSourceHash + 22; }
 
 const char* fp8_status_string(int status) {
     switch (status) {
@@ -112,7 +98,7 @@ const char* fp8_status_string(int status) {
 
 int fp8_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s, void* stream) {
     if (M < 0 || K <= 0) return K <= 0 ? FP8_ERR_SHAPE : FP8_ERR_ARG;
-    if (K % 128 != 0) return FP8_ERR_SHAPE;
+    if (K % 128 != 0 || !count_ok(M, K)) return FP8_ERR_SHAPE;
     if (M == 0) return FP8_OK;
     if (!x || !q || !s) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
@@ -123,7 +109,7 @@ int fp8_quantize_block(const void* x, int64_t M, int64_t K, void* q, float* s, v
 int fp8_quantize_block_e8m0(const void* x, int64_t M, int64_t K, void* q, void* s,
                             void* stream) {
     if (M < 0 || K <= 0) return K <= 0 ? FP8_ERR_SHAPE : FP8_ERR_ARG;
-    if (K % 128 != 0) return FP8_ERR_SHAPE;
+    if (K % 128 != 0 || !count_ok(M, K)) return FP8_ERR_SHAPE;
     if (M == 0) return FP8_OK;
     if (!x || !q || !s) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
@@ -133,7 +119,7 @@ int fp8_quantize_block_e8m0(const void* x, int64_t M, int64_t K, void* q, void* 
 
 int fp8_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s, void* stream) {
     if (M < 0) return FP8_ERR_ARG;
-    if (K <= 0 || K % 8 != 0) return FP8_ERR_SHAPE;
+    if (K <= 0 || K % 8 != 0 || !count_ok(M, K)) return FP8_ERR_SHAPE;
     if (M == 0) return FP8_OK;
     if (!x || !q || !s) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
@@ -144,7 +130,7 @@ int fp8_quantize_token(const void* x, int64_t M, int64_t K, void* q, float* s, v
 int fp8_rmsnorm_quant(void* q, const void* x, float* s, const void* gamma, float eps, int64_t M,
                       int64_t K, int group_size, void* stream) {
     if (M < 0 || (group_size != 0 && group_size != 128)) return FP8_ERR_ARG;
-    if (K <= 0 || K % (group_size == 0 ? 8 : 128) != 0) return FP8_ERR_SHAPE;
+    if (K <= 0 || K % (group_size == 0 ? 8 : 128) != 0 || !count_ok(M, K)) return FP8_ERR_SHAPE;
     if (M == 0) return FP8_OK;
     if (!x || !q || !s || !gamma) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(gamma, 16) || !aligned(s, 4))
@@ -261,24 +247,31 @@ int fp8_quantize_tensors(const fp8_tensor_desc* descs, int n, void* stream) {
     return flush();
 }
 
+size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int gran) {
+    if (gran != FP8_GRAN_BLOCK && gran != FP8_GRAN_ROW) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return 0;
+    if (!gemm_dims_ok(M, N, K)) return 0;
+    return (size_t)fp8k::gemm_workspace_bytes(M, N, K);
+}
+
 int fp8_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s, const float* w_s,
                          const void* bias, void* y, int64_t M, int64_t N, int64_t K, int gran,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
     if (bias != nullptr) return FP8_ERR_ARG;
     if (gran != FP8_GRAN_BLOCK && gran != FP8_GRAN_ROW) return FP8_ERR_ARG;
     if (M < 0) return FP8_ERR_ARG;
     if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (!gemm_dims_ok(M, N, K)) return FP8_ERR_SHAPE;
     if (M == 0) return FP8_OK;
     if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(a_s, 4) ||
         !aligned(w_s, 4))
         return FP8_ERR_ALIGN;
+    if (int st = workspace_check(workspace, workspace_bytes, fp8k::gemm_workspace_bytes(M, N, K)))
+        return st;
     if (int st = device_check()) return st;
-    fp8k::GemmWorkspace ws{};
-    const bool have_ws =
-        fp8k::gemm_small_path(M, N, K) && gemm_workspace(as_stream(stream), &ws);
-    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, have_ws ? &ws : nullptr,
-                                      as_stream(stream)));
+    const fp8k::GemmWorkspace ws{workspace, (int64_t)workspace_bytes};
+    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, &ws, as_stream(stream)));
 }
 
 int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
@@ -286,6 +279,8 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
                                  int64_t E, int64_t N, int64_t K, void* stream) {
     if (T < 0 || E < 1 || E > 1024 || T > INT32_MAX) return FP8_ERR_ARG;
     if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (!gemm_dims_ok(T, N, K) || E * N > INT32_MAX || !gemm_dims_ok(T, E * N, K))
+        return FP8_ERR_SHAPE;
     if (T == 0) return FP8_OK;
     if (!a || !w || !a_s || !w_s || !offsets || !y) return FP8_ERR_ARG;
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(a_s, 4) ||
@@ -296,25 +291,39 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s,
                                               as_stream(stream)));
 }
 
-int fp8_batched_gemm_a8w8_mxscale(const void* a, const void* w, const void* a_s, const void* w_s,
-                                  void* y, int64_t B, int64_t M, int64_t N, int64_t K,
-                                  void* stream) {
-    if (M < 0 || B < 0) return FP8_ERR_ARG;
+// Shape limits of the batched MX GEMM: 32-bit tile offsets (256 rows of B * K
+// bytes), tile and step counts in int.
+static int mx_shape_check(int64_t B, int64_t M, int64_t N, int64_t K) {
     if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
-    if (M == 0 || B == 0) return FP8_OK;
-    // 32-bit tile offsets: 256 rows of B * K bytes; tile and step counts in int
-    if (B * K > (int64_t(1) << 22)) return FP8_ERR_SHAPE;
+    if (B <= 0 || M <= 0) return FP8_OK;
+    if (B > (int64_t(1) << 22) / K) return FP8_ERR_SHAPE;  // B * K > 2^22
+    if (N > INT32_MAX || !gemm_dims_ok(M, B * N, B * K)) return FP8_ERR_SHAPE;
     const int64_t tiles = B * ((M + 255) / 256) * ((N + 255) / 256);
     if (tiles > INT32_MAX || (tiles / 256 + 1) * (K / 128) > INT32_MAX) return FP8_ERR_SHAPE;
+    return FP8_OK;
+}
+
+size_t fp8_batched_gemm_mxscale_workspace_size(int64_t B, int64_t M, int64_t N, int64_t K) {
+    if (B <= 0 || M <= 0 || mx_shape_check(B, M, N, K) != FP8_OK) return 0;
+    return (size_t)fp8k::mx_workspace_bytes(B, M, N, K);
+}
+
+int fp8_batched_gemm_a8w8_mxscale(const void* a, const void* w, const void* a_s, const void* w_s,
+                                  void* y, int64_t B, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || B < 0) return FP8_ERR_ARG;
+    if (int st = mx_shape_check(B, M, N, K)) return st;
+    if (M == 0 || B == 0) return FP8_OK;
     if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
     if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8_ERR_ALIGN;
+    if (int st = workspace_check(workspace, workspace_bytes,
+                                 fp8k::mx_workspace_bytes(B, M, N, K)))
+        return st;
     if (int st = device_check()) return st;
-    fp8k::GemmWorkspace ws{};
-    const bool have_ws =
-        fp8k::mx_small_path(B, M, N) && gemm_workspace(as_stream(stream), &ws);
+    const fp8k::GemmWorkspace ws{workspace, (int64_t)workspace_bytes};
     return launched(fp8k::launch_batched_gemm_mx(a, w, static_cast<const uint8_t*>(a_s),
                                                  static_cast<const uint8_t*>(w_s), y, B, M, N, K,
-                                                 have_ws ? &ws : nullptr, as_stream(stream)));
+                                                 &ws, as_stream(stream)));
 }
 
 int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream) {
@@ -339,7 +348,7 @@ int fp8_bf16_round_f32_bits(uint64_t first_bits, int64_t n, void* out, void* str
 
 int fp8_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s, void* stream) {
     if (T < 0) return FP8_ERR_ARG;
-    if (I <= 0 || I % 128 != 0) return FP8_ERR_SHAPE;
+    if (I <= 0 || I % 128 != 0 || I > INT64_MAX / 8 || !count_ok(T, 2 * I)) return FP8_ERR_SHAPE;
     if (T == 0) return FP8_OK;
     if (!gu || !q || !s) return FP8_ERR_ARG;
     if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8_ERR_ALIGN;
@@ -350,7 +359,7 @@ int fp8_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s, vo
 int fp8_quantize_block_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,
                               int64_t T, void* q, float* s, void* stream) {
     if (T < 0 || n_src < 0 || n_src > INT32_MAX) return FP8_ERR_ARG;
-    if (K <= 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (K <= 0 || K % 128 != 0 || !count_ok(T, K) || !count_ok(n_src, K)) return FP8_ERR_SHAPE;
     if (T == 0) return FP8_OK;
     if (!row_token || !q || !s || (n_src > 0 && !x)) return FP8_ERR_ARG;
     if (!aligned(x, 16) || !aligned(row_token, 4) || !aligned(q, 16) || !aligned(s, 4))
@@ -369,7 +378,7 @@ int fp8_inverse_rope_group_quant(const void* o, const int64_t* positions, const 
     if (H <= 0 || D <= 0 || D % 8 != 0 || rope_dim > D || H % num_groups != 0 ||
         D > INT32_MAX || H > (INT32_MAX - 1) / D)  // a row's offsets fit in int
         return FP8_ERR_SHAPE;
-    if ((H / num_groups) * D % 128 != 0) return FP8_ERR_SHAPE;
+    if ((H / num_groups) * D % 128 != 0 || !count_ok(T, H * D)) return FP8_ERR_SHAPE;
     if (rope_dim > 0 && max_pos == 0) return FP8_ERR_ARG;
     if (max_pos > INT64_MAX / (rope_dim / 2 + 1)) return FP8_ERR_ARG;
     if (T == 0) return FP8_OK;

@@ -1590,7 +1590,7 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_pipe(TileSpace S, int64_t de
 //   of a workgroup's range, slot 1: its last), in register order (v4f index
 //   (slot * 8 + i * 2 + jj) * 512 + tid).
 // ---------------------------------------------------------------------------
-static_assert(kGemmWsPartBytes >= kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
+static_assert(kGemmWsMaxBytes >= kPersistentGrid * 2 * BMP * BNP * 4, "partial slots");
 
 struct SkWork {
     v4f* part;
@@ -1875,7 +1875,7 @@ constexpr int kStageD = kSwD + 256;
 constexpr int kGrpD = NSD * kStageD, kGrpSlotD = BMD * 16 + 1024;
 constexpr int kLdsD = kGrpD + 2 * kGrpSlotD;
 static_assert(kLdsD <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-static_assert(kGemmWsPartBytes >= kPersistentGrid * 2 * BMD * BNP * 4, "partial slots");
+static_assert(kGemmWsMaxBytes >= kPersistentGrid * 2 * BMD * BNP * 4, "partial slots");
 
 struct DkSrc {
     __amdgpu_buffer_rsrc_t a, w, sa, sw;
@@ -2307,87 +2307,139 @@ bool gemm_small_path(int64_t M, int64_t N, int64_t K) {
              (tiles2 / 256 + 1) * (K / BK) < (int64_t(1) << 31));
 }
 
-// The small-M GEMM (128 x 128 tiles) of a dense tile space: stream-K with its
-// fixed-order reduce when a workspace is given, else one tile per workgroup at
-// a time.  MX shapes always take buffer loads (B K <= 2^22).
-template <int G>
-static hipError_t launch_small(const TileSpace& S, const GemmWorkspace* ws, hipStream_t st) {
-    const int64_t N = S.N, K = S.K;
-    const int64_t tiles = S.tm_count * (N / BNP);
-    const int64_t steps = tiles * (K / BK);
-    const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
-    if (ws != nullptr && S.M > BMP && buf) {  // 256-row tiles: each weight block read once
-        TileSpace S2 = S;
-        S2.tm_count = (S.M + BMD - 1) / BMD;
-        const int64_t tiles2 = S2.tm_count * (N / BNP), steps2 = tiles2 * (K / BK);
+// Launch plan of the small-M GEMM of a dense tile space.  Without a split
+// there are no partials: the 256 x 128 kernel when the tiles' whole grid fills
+// the chip, else the 128 x 128 one, else one tile per workgroup at a time.
+// With a workspace of at least ws_bytes, tiles are split between workgroups
+// (stream-K) and a second kernel sums the partials.
+enum { SP_PIPE = 0, SP_SK = 1, SP_DK = 2 };
+struct SmallPlan {
+    int kind;
+    int64_t tm_count;  // row tiles (128 or 256 rows)
+    int64_t tiles, steps, grid;
+    bool split;        // some tile is cut between workgroups
+    int64_t ws_bytes;  // workspace the split needs (0 without a split)
+};
+
+static SmallPlan plan_small(int64_t M, int64_t N, int64_t K, bool with_ws) {
+    SmallPlan p{};
+    const int64_t KB = K / BK;
+    const bool buf = K <= (int64_t(1) << 22);  // 256 rows x K bytes fit 32-bit buffer offsets
+    if (M > BMP && buf) {  // 256-row tiles: each weight block read once
+        const int64_t tm = (M + BMD - 1) / BMD, tiles = tm * (N / BNP), steps = tiles * KB;
         // with fewer than 8 K steps per workgroup the larger stages' fill and
         // partials cost more than the second weight read saves
-        if (steps2 >= 8 * kPersistentGrid && tiles2 <= kGemmWsMaxTiles &&
-            steps2 < (int64_t(1) << 31)) {
-            const int64_t whole = whole_tile_grid(tiles2);
-            const int64_t grid =
-                whole > 0 ? whole : (steps2 < kPersistentGrid ? steps2 : kPersistentGrid);
-            const SkWork sk{static_cast<v4f*>(ws->part)};
-            // scale groups of 4 K blocks: whole groups per row, aligned group loads
-            const int64_t salign = G == GRAN_MX ? 4 : 16;
-            const bool sg = G != GRAN_ROW && (K / BK) % 4 == 0 &&
-                            reinterpret_cast<uintptr_t>(S.sA) % salign == 0 &&
-                            reinterpret_cast<uintptr_t>(S.sW) % salign == 0;
-            if constexpr (G != GRAN_ROW)
-                if (sg)
-                    hipLaunchKernelGGL((k_gemm_dk<G, true>), dim3((unsigned)grid), dim3(kThreadsP),
-                                       0, st, S2, tiles2, sk);
-            if (!sg)
-                hipLaunchKernelGGL((k_gemm_dk<G, false>), dim3((unsigned)grid), dim3(kThreadsP),
-                                   0, st, S2, tiles2, sk);
-            if (hipError_t e = hipGetLastError()) return e;
-            if (steps2 % grid != 0 || (steps2 / grid) % (K / BK) != 0)  // some tile is split
-            {
-                const v4f* part = static_cast<const v4f*>(sk.part);
-                if (reduce_wide(steps2, grid, K / BK))
-                    hipLaunchKernelGGL((k_dk_reduce_wide<G, 16>), dim3((unsigned)(tiles2 * 16)),
-                                       dim3(kThreadsP), 0, st, S2, tiles2, grid, part);
-                else
-                    hipLaunchKernelGGL(k_dk_reduce<G>, dim3((unsigned)(tiles2 * 4)),
-                                       dim3(kThreadsP), 0, st, S2, tiles2, grid, part);
+        if (steps >= 8 * kPersistentGrid && tiles <= kGemmWsMaxTiles &&
+            steps < (int64_t(1) << 31)) {
+            const int64_t whole = whole_tile_grid(tiles);
+            if (whole > 0 || with_ws) {
+                p.kind = SP_DK;
+                p.tm_count = tm; p.tiles = tiles; p.steps = steps;
+                p.grid = whole > 0 ? whole : (steps < kPersistentGrid ? steps : kPersistentGrid);
+                p.split = steps % p.grid != 0 || (steps / p.grid) % KB != 0;
+                p.ws_bytes = p.split ? p.grid * 2 * BMD * BNP * 4 : 0;
+                return p;
             }
-            return hipGetLastError();
         }
     }
-    if (ws != nullptr && tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
+    const int64_t tm = (M + BMP - 1) / BMP, tiles = tm * (N / BNP), steps = tiles * KB;
+    p.tm_count = tm; p.tiles = tiles; p.steps = steps;
+    if (tiles <= kGemmWsMaxTiles && steps < (int64_t(1) << 31)) {
         // stream-K: every workgroup gets at least one K step (grid <= steps),
         // or whole tiles when they fill the chip evenly
         const int64_t whole = whole_tile_grid(tiles);
-        const int64_t grid =
-            whole > 0 ? whole : (steps < kPersistentGrid ? steps : kPersistentGrid);
-        const SkWork sk{static_cast<v4f*>(ws->part)};
-        if (G == GRAN_MX || buf)
-            hipLaunchKernelGGL((k_gemm_sk<G, true>), dim3((unsigned)grid), dim3(kThreadsP), 0, st,
-                               S, tiles, sk);
-        else if constexpr (G != GRAN_MX)
-            hipLaunchKernelGGL((k_gemm_sk<G, false>), dim3((unsigned)grid), dim3(kThreadsP), 0,
-                               st, S, tiles, sk);
+        if (whole > 0 || with_ws) {
+            p.kind = SP_SK;
+            p.grid = whole > 0 ? whole : (steps < kPersistentGrid ? steps : kPersistentGrid);
+            p.split = steps % p.grid != 0 || (steps / p.grid) % KB != 0;
+            p.ws_bytes = p.split ? p.grid * 2 * BMP * BNP * 4 : 0;
+            return p;
+        }
+    }
+    p.kind = SP_PIPE;
+    p.grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
+    return p;
+}
+
+// The plan a call runs: the split plan when the workspace holds its partials,
+// else the plan without a split.
+static SmallPlan plan_small_ws(int64_t M, int64_t N, int64_t K, const GemmWorkspace* ws) {
+    const SmallPlan p = plan_small(M, N, K, true);
+    if (!p.split || (ws != nullptr && ws->part != nullptr && ws->bytes >= p.ws_bytes)) return p;
+    return plan_small(M, N, K, false);
+}
+
+// The small-M GEMM of a dense tile space (see plan_small).  MX shapes always
+// take buffer loads (B K <= 2^22).
+template <int G>
+static hipError_t launch_small(TileSpace S, const GemmWorkspace* ws, hipStream_t st) {
+    const int64_t K = S.K;
+    const SmallPlan p = plan_small_ws(S.M, S.N, K, ws);
+    const bool buf = K <= (int64_t(1) << 22);  // 128 rows x K bytes fit 32-bit buffer offsets
+    S.tm_count = p.tm_count;
+    const SkWork sk{p.split ? static_cast<v4f*>(ws->part) : nullptr};
+    if (p.kind == SP_DK) {
+        // scale groups of 4 K blocks: whole groups per row, aligned group loads
+        const int64_t salign = G == GRAN_MX ? 4 : 16;
+        const bool sg = G != GRAN_ROW && (K / BK) % 4 == 0 &&
+                        reinterpret_cast<uintptr_t>(S.sA) % salign == 0 &&
+                        reinterpret_cast<uintptr_t>(S.sW) % salign == 0;
+        if constexpr (G != GRAN_ROW)
+            if (sg)
+                hipLaunchKernelGGL((k_gemm_dk<G, true>), dim3((unsigned)p.grid), dim3(kThreadsP),
+                                   0, st, S, p.tiles, sk);
+        if (!sg)
+            hipLaunchKernelGGL((k_gemm_dk<G, false>), dim3((unsigned)p.grid), dim3(kThreadsP), 0,
+                               st, S, p.tiles, sk);
         if (hipError_t e = hipGetLastError()) return e;
-        if (steps % grid != 0 || (steps / grid) % (K / BK) != 0)  // some tile is split
-        {
-            const v4f* part = static_cast<const v4f*>(sk.part);
-            if (reduce_wide(steps, grid, K / BK))
-                hipLaunchKernelGGL((k_sk_reduce_wide<G, 8>), dim3((unsigned)(tiles * 8)),
-                                   dim3(kThreadsP), 0, st, S, tiles, grid, part);
+        if (p.split) {
+            if (reduce_wide(p.steps, p.grid, K / BK))
+                hipLaunchKernelGGL((k_dk_reduce_wide<G, 16>), dim3((unsigned)(p.tiles * 16)),
+                                   dim3(kThreadsP), 0, st, S, p.tiles, p.grid,
+                                   static_cast<const v4f*>(sk.part));
             else
-                hipLaunchKernelGGL(k_sk_reduce<G>, dim3((unsigned)(tiles * kSkRedSplit)),
-                                   dim3(kThreadsP), 0, st, S, tiles, grid, part);
+                hipLaunchKernelGGL(k_dk_reduce<G>, dim3((unsigned)(p.tiles * 4)), dim3(kThreadsP),
+                                   0, st, S, p.tiles, p.grid, static_cast<const v4f*>(sk.part));
         }
         return hipGetLastError();
     }
-    const int64_t grid = tiles < kPersistentGrid ? tiles : kPersistentGrid;
+    if (p.kind == SP_SK) {
+        if (G == GRAN_MX || buf)
+            hipLaunchKernelGGL((k_gemm_sk<G, true>), dim3((unsigned)p.grid), dim3(kThreadsP), 0,
+                               st, S, p.tiles, sk);
+        else if constexpr (G != GRAN_MX)
+            hipLaunchKernelGGL((k_gemm_sk<G, false>), dim3((unsigned)p.grid), dim3(kThreadsP), 0,
+                               st, S, p.tiles, sk);
+        if (hipError_t e = hipGetLastError()) return e;
+        if (p.split) {
+            if (reduce_wide(p.steps, p.grid, K / BK))
+                hipLaunchKernelGGL((k_sk_reduce_wide<G, 8>), dim3((unsigned)(p.tiles * 8)),
+                                   dim3(kThreadsP), 0, st, S, p.tiles, p.grid,
+                                   static_cast<const v4f*>(sk.part));
+            else
+                hipLaunchKernelGGL(k_sk_reduce<G>, dim3((unsigned)(p.tiles * kSkRedSplit)),
+                                   dim3(kThreadsP), 0, st, S, p.tiles, p.grid,
+                                   static_cast<const v4f*>(sk.part));
+        }
+        return hipGetLastError();
+    }
     if (G == GRAN_MX || buf)
-        hipLaunchKernelGGL((k_gemm_pipe<G, false, true>), dim3((unsigned)grid), dim3(kThreadsP),
-                           0, st, S, tiles);
+        hipLaunchKernelGGL((k_gemm_pipe<G, false, true>), dim3((unsigned)p.grid), dim3(kThreadsP),
+                           0, st, S, p.tiles);
     else if constexpr (G != GRAN_MX)
-        hipLaunchKernelGGL((k_gemm_pipe<G, false, false>), dim3((unsigned)grid), dim3(kThreadsP),
-                           0, st, S, tiles);
+        hipLaunchKernelGGL((k_gemm_pipe<G, false, false>), dim3((unsigned)p.grid),
+                           dim3(kThreadsP), 0, st, S, p.tiles);
     return hipGetLastError();
+}
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || !gemm_small_path(M, N, K)) return 0;
+    return plan_small(M, N, K, true).ws_bytes;
+}
+
+int64_t mx_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || !mx_small_path(B, M, N)) return 0;
+    return plan_small(M, N, K, true).ws_bytes;
 }
 
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,

@@ -38,17 +38,23 @@ hipError_t launch_requant(const ReqBatch& batch, int64_t total_blocks, int fmt, 
 hipError_t launch_encode_bits(uint64_t first, int64_t n, void* q, hipStream_t st);
 hipError_t launch_bf16_bits(uint64_t first, int64_t n, void* out, hipStream_t st);
 
-// Workspace of the stream-K small-M GEMM (device memory, one per stream):
-// 256 workgroups x 2 partial tiles of up to 256 x 128 fp32.  Tile counts
-// above kGemmWsMaxTiles run without stream-K.
-constexpr int64_t kGemmWsPartBytes = int64_t(256) * 2 * 256 * 128 * 4;
+// Workspace of the stream-K small-M GEMM (caller-provided device memory):
+// partial tiles of up to 256 workgroups x 2 slots of up to 256 x 128 fp32.
+// Tile counts above kGemmWsMaxTiles run without a split.
+constexpr int64_t kGemmWsMaxBytes = int64_t(256) * 2 * 256 * 128 * 4;
 constexpr int64_t kGemmWsMaxTiles = int64_t(1) << 16;
 struct GemmWorkspace {
     void* part;
+    int64_t bytes;
 };
+// Workspace bytes launch_gemm / launch_batched_gemm_mx use for a shape (0 when
+// the shape's path splits no tile); a smaller workspace runs the plan without
+// a split.
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t mx_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K);
 // true when launch_gemm takes the small-M (128 x 128 tile) path for this shape
 bool gemm_small_path(int64_t M, int64_t N, int64_t K);
-// ws null: the small-M path runs without stream-K
+// ws null or smaller than gemm_workspace_bytes: no tile is split
 hipError_t launch_gemm(const void* a, const void* w, const float* a_s, const float* w_s,
                        void* y, int64_t M, int64_t N, int64_t K, int gran,
                        const GemmWorkspace* ws, hipStream_t st);

@@ -40,9 +40,9 @@
  *     on it; the call returns before the kernels finish.
  *   * The caller owns and allocates every input and output buffer, and the
  *     library keeps no pointer to them after the call returns (the kernels
- *     use the buffers until the stream reaches them).  The one allocation of
- *     the library is the workspace of fp8_gemm_a8w8_scaled at small M (see
- *     there).
+ *     use the buffers until the stream reaches them).  The library allocates
+ *     no memory: the GEMMs' partial-tile workspace is the caller's too (see
+ *     fp8_gemm_workspace_size).
  *   * Errors: argument, shape and device checks run on the host before any
  *     launch; on error nothing is written and a negative fp8_status returns.
  *     Launch failures return FP8_ERR_LAUNCH.  Faults inside kernels surface
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FP8W8A8_ABI_VERSION 1
+#define FP8W8A8_ABI_VERSION 2
 
 typedef enum {
     FP8_OK = 0,
@@ -86,6 +86,11 @@ typedef enum {
 
 /* Version of this header's ABI (FP8W8A8_ABI_VERSION). */
 int fp8_abi_version(void);
+
+/* SHA-256 (hex) of the sources this library was built from (csrc/ and this
+ * header), or "unknown"; lets a test session check that the binary it loads
+ * matches the source tree. */
+const char* fp8_build_source_hash(void);
 
 /* Static, human-readable name of a status code. */
 const char* fp8_status_string(int status);
@@ -262,6 +267,14 @@ int fp8_quantize_tensors(const fp8_tensor_desc* descs, int n, void* stream);
 int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream);
 
 /*
+ * Workspace of fp8_gemm_a8w8_scaled: the bytes of device memory its split-tile
+ * path needs for this shape and granularity (0 when the path splits no tile;
+ * also 0 for arguments the GEMM would refuse).  At most 64 MiB (256
+ * workgroups x 2 partial tiles of 256 x 128 fp32).
+ */
+size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int gran);
+
+/*
  * Scaled W8A8 GEMM, Y = X W^T with bf16 output (SGLang page §3 argument order:
  * A, B, A-scale, B-scale, bias, out; DeepSeek V4 page §3 for block scales).
  *   a : E4M3 [M, K]    w : E4M3 [N, K]    y : bf16 [M, N] (out)
@@ -274,26 +287,28 @@ int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, v
  *   bias must be NULL (FP8_ERR_ARG otherwise).  K % 128 != 0 or
  *   N % 128 != 0 -> FP8_ERR_SHAPE.  M is any value >= 0.
  *   Small M (below 1024 with fewer than 192 tiles of 256 x 256; also
- *   N % 256 != 0 or K > 2^22) splits the K steps of all tiles evenly over the
- *   CUs (stream-K) and sums split tiles in a fixed order in a second kernel,
- *   so repeated calls give identical bytes.  Above 128 rows the tiles are
+ *   N % 256 != 0 or K > 2^22): when whole tiles fill at least 3/4 of the CUs
+ *   evenly, each workgroup takes whole tiles; otherwise, given a workspace,
+ *   the K steps of all tiles are split evenly over the CUs (stream-K) and a
+ *   second kernel sums each split tile's fp32 partials in a fixed order, so
+ *   repeated calls give identical bytes.  Above 128 rows the tiles are
  *   256 x 128 (each weight block read once per 256 rows), else 128 x 128.
- *   When whole tiles fill at least 3/4 of the CUs evenly, each workgroup
- *   takes whole tiles instead and no tile is split.
- *   That needs a workspace of 64 MiB for the partial tiles, which the library
- *   allocates on the first such call on each (device, stream) and keeps until
- *   the process ends.
- *   Calls on one stream share it (they are ordered); calls on different
- *   streams use different workspaces.  While the stream is being captured
- *   into a graph and has no workspace yet, no allocation is made and a
- *   kernel without the split runs instead (same results within the GEMM
- *   tolerance, not the same bytes).  A graph captured on a stream that
- *   already had a workspace records that workspace: replays of it must not
- *   overlap other small-M GEMMs issued on that stream, or each other.
+ *   workspace, workspace_bytes : device memory the split path writes its
+ *     partial tiles to (16-byte aligned, at least
+ *     fp8_gemm_workspace_size(M, N, K, gran) bytes; FP8_ERR_ARG if smaller,
+ *     FP8_ERR_ALIGN if misaligned).  It must not overlap the other buffers,
+ *     and it is in use until the stream reaches the end of the call: calls
+ *     that may run at the same time (other streams, overlapping graph
+ *     replays) need distinct workspaces.  NULL with 0 bytes is allowed: then
+ *     no tile is split (one tile per workgroup at a time where whole tiles do
+ *     not fill the chip), with results within the GEMM tolerance but not the
+ *     same bytes as the split path.  A graph captured with a workspace
+ *     records its address.
  */
 int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_s,
                          const float* w_s, const void* bias, void* y_bf16, int64_t M,
-                         int64_t N, int64_t K, int gran, void* stream);
+                         int64_t N, int64_t K, int gran, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Grouped (MoE) block-scaled W8A8 GEMM ("FP8-RL" abstract: MoE models; DeepSeek
@@ -316,6 +331,13 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const f
                                  int64_t T, int64_t E, int64_t N, int64_t K, void* stream);
 
 /*
+ * Workspace of fp8_batched_gemm_a8w8_mxscale for this shape, as
+ * fp8_gemm_workspace_size (0 unless B == 1 takes the small-M path and splits
+ * tiles; 0 for arguments the GEMM would refuse).
+ */
+size_t fp8_batched_gemm_mxscale_workspace_size(int64_t B, int64_t M, int64_t N, int64_t K);
+
+/*
  * Batched W8A8 GEMM with E8M0 block scales (DeepSeek V4 page §3
  * batched_gemm_a8w8_mxscale(A, W, A-scale, W-scale, bf16); §2 weight view
  * (groups, out, in) and scale view (groups, out/128, in/128)), on the gfx950
@@ -332,12 +354,14 @@ int fp8_grouped_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const f
  *   FP8_ERR_ARG; M == 0 or B == 0 launch nothing.  Scale pointers need no
  *   alignment.
  *   Dense small M (B = 1, M below 1024 with fewer than 192 tiles of 256 x 256)
- *   takes the stream-K kernels of fp8_gemm_a8w8_scaled and shares that call's
- *   per-stream workspace (same allocation, ordering and graph-capture rules).
+ *   takes the small-M kernels of fp8_gemm_a8w8_scaled; workspace and
+ *   workspace_bytes follow that call's rules, sized by
+ *   fp8_batched_gemm_mxscale_workspace_size.
  */
 int fp8_batched_gemm_a8w8_mxscale(const void* a_e4m3, const void* w_e4m3, const void* a_s,
                                   const void* w_s, void* y_bf16, int64_t B, int64_t M, int64_t N,
-                                  int64_t K, void* stream);
+                                  int64_t K, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * Diagnostic: the device E4M3 encoder alone.  q[i] = E4M3(float with bit

@@ -18,6 +18,17 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
 
 
+def pytest_sessionstart(session):
+    """Tie the library under test to the source tree: a libfp8w8a8.so that is
+    missing, or was built from other sources (the hash it records differs),
+    is rebuilt before any test loads it."""
+    from fp8_w8a8_quantized_amd import build
+
+    if not build.is_current():
+        print("libfp8w8a8.so missing or built from other sources: rebuilding", flush=True)
+        build.build()
+
+
 def _gpu_present() -> bool:
     try:
         import torch

@@ -55,3 +55,41 @@ def sample_rows(M: int, n: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = set([0, M - 1]) | set(rng.choice(M, size=min(n, M), replace=False).tolist())
     return np.array(sorted(pick), dtype=np.int64)
+
+
+def assert_gemm_all_rows(y_gpu: torch.Tensor, oqa, osa, oqw, osw, gran, what="", tol=None,
+                         chunk: int = 1024):
+    """Every row of y_gpu [M, N] against the oracle's fp64 product of the
+    quantized operands (codes and scales from the oracle's own quantizers):
+    the weight is dequantized once (oracle.dequant_weight) and the rows are
+    compared in chunks of ``chunk`` (oracle.dequant_act, then the fp64
+    product, as oracle.gemm computes it)."""
+    import oracle
+
+    W = oracle.dequant_weight(oqw, osw, gran)
+    M = y_gpu.shape[0]
+    worst = 0.0
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        ref = oracle.dequant_act(oqa[r0:r1], osa[r0:r1], gran) @ W.T
+        worst = max(worst, assert_rows_close(y_gpu[r0:r1], ref, what=f"{what} rows {r0}..{r1}",
+                                             tol=tol))
+    return worst
+
+
+def bf16_from_f64(h: np.ndarray) -> torch.Tensor:
+    """The nearest bf16 (ties to even) to each fp64 value, as a bf16 CPU
+    tensor.  Rounding to fp32 first can land exactly on a bf16 midpoint the
+    fp64 value is not on; such fp32 values are moved one fp32 ulp toward the
+    fp64 value before the fp32 -> bf16 rounding, which then picks the side the
+    fp64 value lies on."""
+    import oracle
+
+    f = h.astype(np.float32)
+    bits = f.view(np.uint32)
+    fix = ((bits & 0xFFFF) == 0x8000) & (f.astype(np.float64) != h)
+    if np.any(fix):
+        toward = np.where(h[fix] > f[fix], np.float32(np.inf), np.float32(-np.inf))
+        f[fix] = np.nextafter(f[fix], toward)
+    b = oracle.bf16_rne_array(f.reshape(-1)).reshape(h.shape)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)

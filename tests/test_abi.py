@@ -42,7 +42,8 @@ def test_header_declares_the_calls():
                      "fp8_quantize_block_e8m0", "fp8_batched_gemm_a8w8_mxscale",
                      "fp8_quantize_tensors", "fp8_add_rmsnorm_quant", "fp8_swiglu_quant",
                      "fp8_silu_f32_of_bf16", "fp8_quantize_block_gather",
-                     "fp8_inverse_rope_group_quant"):
+                     "fp8_inverse_rope_group_quant", "fp8_gemm_workspace_size",
+                     "fp8_batched_gemm_mxscale_workspace_size", "fp8_build_source_hash"):
         assert required in names
 
 
@@ -55,8 +56,14 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
+def test_library_built_from_these_sources(L):
+    from fp8_w8a8_quantized_amd import build
+
+    assert L.fp8_build_source_hash().decode() == build.source_hash()
+
+
 def test_version_and_status_strings(L):
-    assert L.fp8_abi_version() == 1
+    assert L.fp8_abi_version() == 2
     for st in (OK, ARG, SHAPE, ALIGN, DEVICE, LAUNCH):
         assert fp8.status_string(st) and fp8.status_string(st) != "unknown status"
     assert fp8.status_string(123) == "unknown status"
@@ -174,12 +181,13 @@ def test_inverse_rope_validation(L):
 def test_gemm_validation(L):
     vp = ctypes.c_void_p
     f = vp(FAKE)
-    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, f, f, 16, 256, 256, 0, None) == ARG  # bias
-    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 200, 256, 0, None) == SHAPE
-    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 200, 1, None) == SHAPE
-    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 256, 7, None) == ARG
-    assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, vp(FAKE + 8), 16, 256, 256, 0, None) == ALIGN
-    assert L.fp8_gemm_a8w8_scaled(None, None, None, None, None, None, 0, 256, 256, 0, None) == OK
+    g = L.fp8_gemm_a8w8_scaled
+    assert g(f, f, f, f, f, f, 16, 256, 256, 0, None, 0, None) == ARG  # bias
+    assert g(f, f, f, f, None, f, 16, 200, 256, 0, None, 0, None) == SHAPE
+    assert g(f, f, f, f, None, f, 16, 256, 200, 1, None, 0, None) == SHAPE
+    assert g(f, f, f, f, None, f, 16, 256, 256, 7, None, 0, None) == ARG
+    assert g(f, f, f, f, None, vp(FAKE + 8), 16, 256, 256, 0, None, 0, None) == ALIGN
+    assert g(None, None, None, None, None, None, 0, 256, 256, 0, None, 0, None) == OK
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 0, 256, 256, None) == ARG
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 4, 256, 100, None) == SHAPE
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, f, f, 64, 1025, 256, 256, None) == ARG
@@ -187,17 +195,60 @@ def test_gemm_validation(L):
     assert L.fp8_grouped_gemm_a8w8_scaled(f, f, f, f, vp(FAKE + 2), f, 64, 4, 256, 256,
                                           None) == ALIGN
     mx = L.fp8_batched_gemm_a8w8_mxscale
-    assert mx(f, f, f, f, f, 1, -1, 256, 256, None) == ARG
-    assert mx(f, f, f, f, f, -1, 16, 256, 256, None) == ARG
-    assert mx(f, f, f, f, f, 1, 16, 200, 256, None) == SHAPE
-    assert mx(f, f, f, f, f, 1, 16, 256, 200, None) == SHAPE
-    assert mx(f, f, f, f, f, 4, 16, 256, 1 << 21, None) == SHAPE  # B * K > 2^22
-    assert mx(f, f, f, f, vp(FAKE + 8), 1, 16, 256, 256, None) == ALIGN
-    assert mx(None, None, None, None, None, 1, 0, 256, 256, None) == OK
-    assert mx(None, None, None, None, None, 0, 16, 256, 256, None) == OK
+    assert mx(f, f, f, f, f, 1, -1, 256, 256, None, 0, None) == ARG
+    assert mx(f, f, f, f, f, -1, 16, 256, 256, None, 0, None) == ARG
+    assert mx(f, f, f, f, f, 1, 16, 200, 256, None, 0, None) == SHAPE
+    assert mx(f, f, f, f, f, 1, 16, 256, 200, None, 0, None) == SHAPE
+    assert mx(f, f, f, f, f, 4, 16, 256, 1 << 21, None, 0, None) == SHAPE  # B * K > 2^22
+    assert mx(f, f, f, f, vp(FAKE + 8), 1, 16, 256, 256, None, 0, None) == ALIGN
+    assert mx(None, None, None, None, None, 1, 0, 256, 256, None, 0, None) == OK
+    assert mx(None, None, None, None, None, 0, 16, 256, 256, None, 0, None) == OK
     if not _gpu():
-        assert L.fp8_gemm_a8w8_scaled(f, f, f, f, None, f, 16, 256, 256, 0, None) == DEVICE
-        assert mx(f, f, f, f, f, 1, 16, 256, 256, None) == DEVICE
+        assert g(f, f, f, f, None, f, 16, 256, 256, 0, None, 0, None) == DEVICE
+        assert mx(f, f, f, f, f, 1, 16, 256, 256, None, 0, None) == DEVICE
+
+
+# Stream-K shapes: 128 x 128 tiles (M <= 128) or 256 x 128 tiles (M > 128 with
+# >= 8 K steps per workgroup); the workspace is 256 workgroups x 2 partial
+# slots of one tile's fp32 accumulators when a tile is split.
+def test_gemm_workspace_sizes(L):
+    ws = L.fp8_gemm_workspace_size
+    slot1, slot2 = 128 * 128 * 4, 256 * 128 * 4
+    assert ws(256, 6144, 4096, 0) == 256 * 2 * slot1   # qkv at decode: 128-row stream-K
+    assert ws(256, 4096, 12288, 0) == 256 * 2 * slot2  # down: 256-row stream-K
+    assert ws(256, 4096, 12288, 1) == 256 * 2 * slot2  # the row form takes the same plan
+    assert ws(256, 24576, 4096, 0) == 0                # gate_up: 192 whole 256 x 128 tiles
+    assert ws(100, 24576, 1024, 0) == 0                # 192 whole 128 x 128 tiles
+    assert ws(129, 128, 128, 0) == 0                   # 2 tiles, 1 step each: no split
+    assert ws(3, 1024, 12288, 0) == 256 * 2 * slot1    # 8 tiles x 96 steps over 256 ranks
+    assert ws(8192, 24576, 4096, 0) == 0               # large-M kernel
+    # N % 256 == 128 keeps even large M on the small-M kernels: 32 x 33 tiles of
+    # 256 x 128 do not divide evenly over the CUs, so they are split
+    assert ws(8192, 4224, 4096, 0) == 256 * 2 * slot2
+    assert ws(0, 256, 256, 0) == 0
+    assert ws(16, 200, 256, 0) == 0 and ws(16, 256, 256, 5) == 0  # refused arguments
+    mxws = L.fp8_batched_gemm_mxscale_workspace_size
+    assert mxws(1, 256, 4096, 12288) == 256 * 2 * slot2
+    assert mxws(4, 256, 4096, 1024) == 0               # batched: the large-tile kernel
+    assert mxws(1, 256, 4096, 200) == 0
+
+
+def test_gemm_workspace_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    g = L.fp8_gemm_a8w8_scaled
+    need = L.fp8_gemm_workspace_size(256, 4096, 12288, 0)
+    assert need > 0
+    assert g(f, f, f, f, None, f, 256, 4096, 12288, 0, None, 64, None) == ARG    # bytes, no ptr
+    assert g(f, f, f, f, None, f, 256, 4096, 12288, 0, f, need - 16, None) == ARG  # too small
+    assert g(f, f, f, f, None, f, 256, 4096, 12288, 0, vp(FAKE + 8), need, None) == ALIGN
+    mx = L.fp8_batched_gemm_a8w8_mxscale
+    assert mx(f, f, f, f, f, 1, 256, 4096, 12288, f, need - 1, None) == ARG
+    if not _gpu():
+        # a large enough workspace, or none at all, passes validation
+        assert g(f, f, f, f, None, f, 256, 4096, 12288, 0, f, need, None) == DEVICE
+        assert g(f, f, f, f, None, f, 256, 4096, 12288, 0, None, 0, None) == DEVICE
+        assert mx(f, f, f, f, f, 1, 256, 4096, 12288, f, need, None) == DEVICE
 
 
 def test_requant_validation(L):
@@ -260,3 +311,104 @@ def test_quotient_path_equals_ieee_division_exhaustively(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "mismatches 0" in r.stdout
+
+
+# ---------------------------------------------- Python binding validation --
+# Buffers passed by raw pointer are checked (dtype, exact shape, contiguity,
+# device) before any call: a wrong buffer raises TypeError / ValueError on the
+# host.  These run on CPU tensors; the device check comes last, so reaching it
+# ("must be on a HIP device") means every other check passed.
+import torch  # noqa: E402
+
+
+def _cpu(shape, dtype):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_quantizer_out_checks():
+    x = _cpu((4, 256), torch.bfloat16)
+    good = (_cpu((4, 256), torch.uint8), _cpu((4, 2), torch.float32))
+    with pytest.raises(ValueError, match="HIP device"):
+        fp8.quantize_block(x, out=good)
+    with pytest.raises(ValueError, match="shape"):
+        fp8.quantize_block(x, out=(_cpu((4, 128), torch.uint8), good[1]))      # undersized q
+    with pytest.raises(ValueError, match="shape"):
+        fp8.quantize_block(x, out=(good[0], _cpu((4,), torch.float32)))        # row scales
+    with pytest.raises(TypeError):
+        fp8.quantize_block(x, out=(good[0], _cpu((4, 2), torch.float16)))      # dtype
+    with pytest.raises(ValueError, match="contiguous"):
+        fp8.quantize_block(x, out=(_cpu((256, 4), torch.uint8).t(), good[1]))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.quantize_token(x, out=(good[0], _cpu((4, 2), torch.float32)))
+    with pytest.raises(TypeError):
+        fp8.quantize_block_e8m0(x, out=(good[0], _cpu((4, 2), torch.float32)))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.rmsnorm_quant(x, _cpu((128,), torch.bfloat16))                    # gamma length
+    with pytest.raises(ValueError, match="shape"):
+        fp8.rmsnorm_quant(x, _cpu((256,), torch.bfloat16), group_size=128,
+                          out=(good[0], _cpu((4,), torch.float32)))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.add_rmsnorm_quant(x, _cpu((4, 128), torch.bfloat16), _cpu((256,), torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.swiglu_quant(x, out=(_cpu((4, 256), torch.uint8), _cpu((4, 1), torch.float32)))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.quantize_block_gather(x, _cpu((3,), torch.int32),
+                                  out=(_cpu((4, 256), torch.uint8), good[1]))
+    with pytest.raises(ValueError, match="num_groups"):
+        fp8.inverse_rope_group_quant(_cpu((2, 4, 128), torch.bfloat16), _cpu((2,), torch.int64),
+                                     _cpu((16, 32), torch.float32), _cpu((16, 32), torch.float32),
+                                     3)
+    with pytest.raises(ValueError, match="shape"):
+        fp8.inverse_rope_group_quant(_cpu((2, 4, 128), torch.bfloat16), _cpu((2,), torch.int64),
+                                     _cpu((16, 32), torch.float32), _cpu((16, 16), torch.float32),
+                                     1)
+    with pytest.raises(ValueError, match="shape"):
+        fp8.requantize_weights([_cpu((256, 256), torch.bfloat16)],
+                               out=[(_cpu((256, 256), torch.uint8), _cpu((2, 1), torch.float32))])
+    with pytest.raises(TypeError):
+        fp8.requantize_weights([_cpu((256, 256), torch.bfloat16)], fp8.SCALE_E8M0,
+                               out=[(_cpu((256, 256), torch.uint8), _cpu((2, 2), torch.float32))])
+    with pytest.raises(ValueError, match="shape"):
+        fp8.quantize_tensors([_cpu((4, 8), torch.bfloat16)],
+                             out=[(_cpu((4, 8), torch.uint8), _cpu((2,), torch.float32))])
+
+
+def test_binding_gemm_operand_checks():
+    M, N, K = 16, 256, 512
+    qa, qw = _cpu((M, K), torch.uint8), _cpu((N, K), torch.uint8)
+    sa, sw = _cpu((M, K // 128), torch.float32), _cpu((N // 128, K // 128), torch.float32)
+    with pytest.raises(ValueError, match="HIP device"):
+        fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK)
+    with pytest.raises(ValueError, match="shape"):                       # row scales, block mode
+        fp8.gemm_a8w8_scaled((qa, _cpu((M,), torch.float32)), (qw, sw), fp8.GRAN_BLOCK)
+    with pytest.raises(ValueError, match="shape"):
+        fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_ROW)
+    with pytest.raises(ValueError, match="shape"):                       # w's K
+        fp8.gemm_a8w8_scaled((qa, sa), (_cpu((N, K - 128), torch.uint8), sw), fp8.GRAN_BLOCK)
+    with pytest.raises(TypeError):
+        fp8.gemm_a8w8_scaled((qa, sa.double()), (qw, sw), fp8.GRAN_BLOCK)
+    with pytest.raises(ValueError, match="shape"):                       # undersized out
+        fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), fp8.GRAN_BLOCK,
+                             out=_cpu((M, N - 128), torch.bfloat16))
+    with pytest.raises(ValueError):
+        fp8.gemm_a8w8_scaled((qa, sa), (qw, sw), 5)
+    with pytest.raises(ValueError, match="shape"):                       # grouped: w's K
+        fp8.grouped_gemm_a8w8_scaled((qa, sa), (_cpu((2, N, 256), torch.uint8),
+                                                 _cpu((2, 2, 2), torch.float32)),
+                                     _cpu((3,), torch.int32))
+    with pytest.raises(ValueError, match="shape"):                       # offsets length
+        fp8.grouped_gemm_a8w8_scaled((qa, sa), (_cpu((2, N, K), torch.uint8),
+                                                 _cpu((2, 2, 4), torch.float32)),
+                                     _cpu((2,), torch.int32))
+    with pytest.raises(ValueError, match="HIP device"):
+        fp8.grouped_gemm_a8w8_scaled((qa, sa), (_cpu((2, N, K), torch.uint8),
+                                                 _cpu((2, 2, 4), torch.float32)),
+                                     _cpu((3,), torch.int32))
+    sa8, sw8 = _cpu((M, K // 128), torch.uint8), _cpu((N // 128, K // 128), torch.uint8)
+    with pytest.raises(ValueError, match="HIP device"):
+        fp8.batched_gemm_a8w8_mxscale((qa, sa8), (qw, sw8))
+    with pytest.raises(TypeError):                                       # fp32 scale bytes
+        fp8.batched_gemm_a8w8_mxscale((qa, sa), (qw, sw8))
+    with pytest.raises(ValueError, match="shape"):
+        fp8.batched_gemm_a8w8_mxscale((qa.view(M, 1, K), sa8.view(M, 1, -1)),
+                                      (_cpu((2, N, K), torch.uint8), _cpu((2, 2, 4), torch.uint8)))

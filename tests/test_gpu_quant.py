@@ -5,7 +5,7 @@ Sizes: small shapes that span several groups/rows with ragged edges, the
 special groups (all zero, signed zero, subnormal amax, constant magnitude),
 and the full workload sizes (dense linears at M = 8192, the MoE activations,
 the rmsnorm workload [4096, 5120], the per-row weight [12288, 5120], the
-36-layer policy) with the oracle run on sampled rows or block rows.
+36-layer policy), each compared in full: every code and every scale.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ import torch
 import fp8_w8a8_quantized_amd as fp8
 import oracle
 import synth
-from tests.gpu_util import dev, ensure_library, host, sample_rows, say
+from tests.gpu_util import dev, ensure_library, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -65,10 +65,10 @@ def test_block_special_groups():
 
 
 @pytest.mark.parametrize("M,K", [(8192, 4096), (8192, 12288), (32768, 2048), (32768, 768)])
-def test_block_full_size_sampled(M, K):
-    say(f"quantize_block full [{M}, {K}] sampled rows")
+def test_block_full_size(M, K):
+    say(f"quantize_block full [{M}, {K}], every row")
     X = synth.act_col_outliers(M, K, seed=1)
-    _eq_block(X, rows=sample_rows(M, 96, seed=M + K))
+    _eq_block(X)
 
 
 def _eq_block_e8m0(xb: torch.Tensor, rows=None):
@@ -105,10 +105,10 @@ def test_block_e8m0_special_groups():
 
 
 @pytest.mark.parametrize("M,K", [(8192, 4096), (32768, 768)])
-def test_block_e8m0_full_size_sampled(M, K):
-    say(f"quantize_block_e8m0 full [{M}, {K}] sampled rows")
+def test_block_e8m0_full_size(M, K):
+    say(f"quantize_block_e8m0 full [{M}, {K}], every row")
     X = synth.act_col_outliers(M, K, seed=2)
-    _eq_block_e8m0(X, rows=sample_rows(M, 96, seed=M + K + 7))
+    _eq_block_e8m0(X)
 
 
 def _eq_tensors(xs):
@@ -169,10 +169,10 @@ def test_token_shapes(M, K):
     _eq_token(synth.act_col_outliers(M, K, seed=M * 7 + K))
 
 
-def test_token_full_size_weight_sampled():
-    say("quantize_token full W [12288, 5120] sampled rows")
+def test_token_full_size_weight():
+    say("quantize_token full W [12288, 5120], every row")
     W = synth.weight(12288, 5120, seed=5)
-    _eq_token(W, rows=sample_rows(12288, 128, seed=9))
+    _eq_token(W)
 
 
 def _eq_rms(h, gamma, group_size, eps=1e-6, rows=None):
@@ -205,10 +205,10 @@ def test_rmsnorm_quant_shapes(M, K, gs):
     _eq_rms(h, gamma, gs)
 
 
-def test_rmsnorm_quant_group128_full_workload_sampled():
-    say("rmsnorm_quant full [4096, 5120], group_size 128, sampled rows")
+def test_rmsnorm_quant_group128_full_workload():
+    say("rmsnorm_quant full [4096, 5120], group_size 128, every row")
     h, gamma = synth.rms_inputs(seed=1)
-    _eq_rms(h, gamma, 128, rows=sample_rows(4096, 128, seed=2))
+    _eq_rms(h, gamma, 128)
 
 
 def _eq_add_rms(x, r, gamma, group_size, eps=1e-6, rows=None):
@@ -243,7 +243,7 @@ def test_add_rmsnorm_quant_full_workload(gs):
     say(f"add_rmsnorm_quant full [4096, 5120], group_size {gs}")
     x, gamma = synth.rms_inputs(seed=5)
     r = synth.normal_bf16((4096, 5120), seed=6, std=3.0)
-    _eq_add_rms(x, r, gamma, gs, rows=None if gs == 0 else sample_rows(4096, 256, seed=7))
+    _eq_add_rms(x, r, gamma, gs)
 
 
 def test_add_rmsnorm_quant_cancelling_residual():
@@ -298,10 +298,10 @@ def test_swiglu_quant_extremes():
     _eq_swiglu(gu)
 
 
-def test_swiglu_quant_moe_full_size_sampled():
-    say("swiglu_quant [32768, 2 x 768], sampled rows")
+def test_swiglu_quant_moe_full_size():
+    say("swiglu_quant [32768, 2 x 768], every row")
     gu = synth.normal_bf16((32768, 2 * 768), seed=12, std=2.0)
-    _eq_swiglu(gu, rows=sample_rows(32768, 256, seed=13))
+    _eq_swiglu(gu)
 
 
 # ------------------------------------------------- token gather + 1x128 quant --
@@ -330,11 +330,11 @@ def test_gather_quant_out_of_range_rows_are_zero():
     _eq_gather(x, np.array([0, -1, 9, 10, 2 ** 31 - 1, -2 ** 31, 5, 5]))
 
 
-def test_gather_quant_moe_dispatch_sampled():
-    say("quantize_block_gather: 4096 tokens x 2048 -> 32768 routed rows, sampled")
+def test_gather_quant_moe_dispatch():
+    say("quantize_block_gather: 4096 tokens x 2048 -> 32768 routed rows, every row")
     token_of_row, _ = synth.moe_routing()
     x = synth.normal_bf16((synth.MOE_TOKENS, synth.MOE_HIDDEN), seed=11)
-    _eq_gather(x, token_of_row, rows=sample_rows(token_of_row.size, 256, seed=15))
+    _eq_gather(x, token_of_row)
 
 
 # ---------------------------------------- inverse RoPE + 1x128 E8M0 quant --
@@ -388,12 +388,12 @@ def test_inverse_rope_quant_out_of_range_positions():
     _eq_rope(o, np.array([0, 16, -1, 15, 2 ** 40, 3], np.int64), cos, sin, 2)
 
 
-def test_inverse_rope_quant_full_workload_sampled():
+def test_inverse_rope_quant_full_workload():
     T = 8192
-    say(f"inverse_rope_group_quant [{T}, 64, 128], R = 64, 8 groups, sampled rows")
+    say(f"inverse_rope_group_quant [{T}, 64, 128], R = 64, 8 groups, every row")
     o, pos = synth.rope_inputs(T, seed=42)
     cos, sin = synth.rope_cache()
-    _eq_rope(o, pos, cos, sin, synth.ROPE_GROUPS, rows=sample_rows(T, 128, seed=43))
+    _eq_rope(o, pos, cos, sin, synth.ROPE_GROUPS)
 
 
 def _eq_req(ws, fmt, out=None, block_rows=None):
@@ -437,29 +437,31 @@ def test_requant_more_descriptors_than_one_launch():
     _eq_req(ws, 1)
 
 
+@pytest.mark.parametrize("part", range(4))
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_requant_full_policy_sampled(fmt):
-    say(f"requantize_weights full 36-layer policy fmt {fmt}, sampled block rows")
-    ws, rows = [], []
-    rng = np.random.default_rng(fmt)
+def test_requant_full_policy(fmt, part):
+    """The whole 36-layer policy (144 weights, 6.9e9 elements) in one call;
+    each part compares every code and scale of 9 layers' weights (36
+    tensors) against the oracle, so the four parts cover all 144."""
+    say(f"requantize_weights full 36-layer policy fmt {fmt}, layers {9 * part}..{9 * part + 8}"
+        ", every block")
+    ws = []
     for layer in range(synth.POLICY_LAYERS):
         for j, (name, (N, K)) in enumerate(synth.DENSE_SHAPES.items()):
             ws.append(synth.weight(N, K, seed=1000 + 4 * layer + j, device=dev()))
-            rows.append(int(rng.integers(0, N // 128)))
     res = fp8.requantize_weights(ws, fmt)
     torch.cuda.synchronize()
-    pick = [0, 1, 2, 3, 70, 141, 142, 143]
-    for i in pick:
-        br = rows[i]
-        wh = ws[i][br * 128:(br + 1) * 128].cpu()
-        oq, os_ = oracle.quantize_weight_block(wh, fmt)
+    for i in range(36 * part, 36 * (part + 1)):
+        oq, os_ = oracle.quantize_weight_block(ws[i].cpu(), fmt)
         q, s = res[i]
-        assert np.array_equal(host(q[br * 128:(br + 1) * 128]), oq), f"tensor {i}"
-        gs = host(s[br:br + 1])
+        gq = host(q)
+        assert np.array_equal(gq, oq), f"tensor {i}: codes differ at {np.argwhere(gq != oq)[:5]}"
+        gs = host(s)
         if fmt == 0:
-            assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+            assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), f"tensor {i} scales"
         else:
-            assert np.array_equal(gs, os_)
+            assert np.array_equal(gs, os_), f"tensor {i} E8M0 bytes"
+        del oq, os_, gq
     del ws, res
     torch.cuda.empty_cache()
 
