@@ -96,6 +96,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp], i32),
         "fp8_gemm_workspace_size": ([i64, i64, i64, i32], sz),
+        "fp8_gemm_a8w8_scaled_noalloc": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
         "fp8_grouped_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp], i32),
         "fp8_quantize_tensors": ([ctypes.POINTER(_TensorDesc), i32, vp], i32),
         "fp8_encode_f32_bits": ([ctypes.c_uint64, i64, vp, vp], i32),

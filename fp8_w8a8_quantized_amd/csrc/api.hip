@@ -70,6 +70,36 @@ int workspace_check(const void* ws, size_t bytes, int64_t need) {
     return bytes >= (size_t)need ? FP8_OK : FP8_ERR_ARG;
 }
 
+// Scratch of fp8_gemm_a8w8_scaled_noalloc: the stream-K partial tiles of the
+// largest plan (256 workgroups x 2 slots of 256 x 128 fp32), one array per
+// GPU, held until the process ends.  Host code never uses the array's name as
+// an address: each device's address comes from hipGetSymbolAddress, taken on
+// the first call on that device.
+constexpr int64_t kScratchBytes = fp8k::kGemmWsMaxBytes;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up once per device, with that
+// device current), or null when the lookup failed.
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            p = nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    });
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,6 +301,27 @@ int fp8_gemm_a8w8_scaled(const void* a, const void* w, const float* a_s, const f
         return st;
     if (int st = device_check()) return st;
     const fp8k::GemmWorkspace ws{workspace, (int64_t)workspace_bytes};
+    return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, &ws, as_stream(stream)));
+}
+
+int fp8_gemm_a8w8_scaled_noalloc(const void* a, const void* w, const float* a_s,
+                                 const float* w_s, const void* bias, void* y, int64_t M, int64_t N,
+                                 int64_t K, int gran, void* stream) {
+    if (bias != nullptr) return FP8_ERR_ARG;
+    if (gran != FP8_GRAN_BLOCK && gran != FP8_GRAN_ROW) return FP8_ERR_ARG;
+    if (M < 0) return FP8_ERR_ARG;
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+    if (!gemm_dims_ok(M, N, K)) return FP8_ERR_SHAPE;
+    if (M == 0) return FP8_OK;
+    if (!a || !w || !a_s || !w_s || !y) return FP8_ERR_ARG;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(a_s, 4) ||
+        !aligned(w_s, 4))
+        return FP8_ERR_ALIGN;
+    if (fp8k::gemm_workspace_bytes(M, N, K) > kScratchBytes) return FP8_ERR_SHAPE;
+    if (int st = device_check()) return st;
+    void* ptr = scratch_address();
+    if (ptr == nullptr) return FP8_ERR_DEVICE;
+    const fp8k::GemmWorkspace ws{ptr, kScratchBytes};
     return launched(fp8k::launch_gemm(a, w, a_s, w_s, y, M, N, K, gran, &ws, as_stream(stream)));
 }
 

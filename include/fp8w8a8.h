@@ -311,6 +311,26 @@ int fp8_gemm_a8w8_scaled(const void* a_e4m3, const void* w_e4m3, const float* a_
                          size_t workspace_bytes, void* stream);
 
 /*
+ * fp8_gemm_a8w8_scaled for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace pair, the same
+ * kernels and the same result bytes as fp8_gemm_a8w8_scaled given a workspace
+ * of fp8_gemm_workspace_size bytes.  The partial tiles go to a library array
+ * of 64 MiB in each GPU's memory (the largest workspace any shape needs), set
+ * aside when the library's code is loaded on that GPU and held until the
+ * process ends; no call allocates.  Every call on one GPU shares that array
+ * and it keeps the last call's contents; nothing in it needs clearing, since a
+ * call reads only the partial slots it has written.  Calls that may overlap on
+ * one GPU (other streams, other threads, graph replays) race on it and must be
+ * serialized by the caller.  A shape whose
+ * workspace would exceed the array gets FP8_ERR_SHAPE (none does today);
+ * FP8_ERR_DEVICE if the array's address cannot be found on this device.
+ */
+int fp8_gemm_a8w8_scaled_noalloc(const void* a_e4m3, const void* w_e4m3, const float* a_s,
+                                 const float* w_s, const void* bias, void* y_bf16, int64_t M,
+                                 int64_t N, int64_t K, int gran, void* stream);
+
+/*
  * Grouped (MoE) block-scaled W8A8 GEMM ("FP8-RL" abstract: MoE models; DeepSeek
  * V4 page §2 weight view (groups, out, in) and scale view (groups, out/128,
  * in/128)).  Rows of A are grouped by expert: rows offsets[e] .. offsets[e+1]-1

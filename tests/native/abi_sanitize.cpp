@@ -96,6 +96,8 @@ int main() {
            ARG);
     EXPECT(fp8_gemm_a8w8_scaled(f, f, ff, ff, nullptr, f, 256, 4096, 12288, 0, f, need, nullptr),
            DEVICE);
+    EXPECT(fp8_gemm_a8w8_scaled_noalloc(f, f, ff, ff, nullptr, f, 256, 4096, 12288, 0, nullptr),
+           DEVICE);
     EXPECT(fp8_grouped_gemm_a8w8_scaled(f, f, ff, ff, static_cast<int32_t*>(f), f, 64, 1025, 256,
                                         256, nullptr),
            ARG);
