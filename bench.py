@@ -127,6 +127,83 @@ def one_gemm(M: int, N: int, K: int, reps: int):
                       "tflops": round(2.0 * M * N * K / us / 1e6, 1)}))
 
 
+def environment(torch, dev) -> dict:
+    """What the numbers were measured on: versions, device, clocks, host CPU."""
+    props = torch.cuda.get_device_properties(dev)
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+           "device": torch.cuda.get_device_name(dev),
+           "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
+           "hbm_gib": round(props.total_memory / 2**30, 1), "host_cpu": host_cpu_model()}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    env["sclk"] = gpu_clock()
+    return env
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def gpu_clock():
+    """Current and maximum shader clock as rocm-smi reports them (None if it
+    cannot be read)."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+        lines = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()]
+        return lines[0] if lines else None
+    except Exception:
+        return None
+
+
+def measured_peaks(torch, L, dev, stream) -> dict:
+    """Peaks measured on this GPU: the matrix-core rate of the library's
+    register-operand MFMA probe, and a plain 1 GiB device copy (2 GiB moved)."""
+    import ctypes
+
+    out = torch.empty((4096,), dtype=torch.float32, device=dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    iters = 20000
+    L.fp8_mfma_rate_probe(1000, ctypes.c_void_p(out.data_ptr()), sptr)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    rc = L.fp8_mfma_rate_probe(iters, ctypes.c_void_p(out.data_ptr()), sptr)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    assert rc == 0, rc
+    flops = 4096.0 * iters * 8 * 2 * 16 * 16 * 128
+    mfma = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.full((n,), 3, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    copy = 5 * 2.0 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_fp8_tflops": round(mfma, 1), "copy_gbs": round(copy, 1),
+            "mfma_probe": "4096 waves x 8 independent 16x16x128 E4M3 MFMA chains, register operands",
+            "copy_probe": "torch copy_ of 1 GiB device to device, bytes read + written"}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +254,8 @@ def cpu_baseline(rows: int, layers: int):
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": max(omp, blas),
+        "omp_threads": omp, "blas_threads": blas, "host_cpus": os.cpu_count(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": (f"{layers} layers of the step: requantize each layer's 4 bf16 weights "
                    f"(128x128, fp32 scales), 1x128-quantize {rows} rows of each M=8192 "
@@ -239,6 +318,10 @@ def main():
     # per-token path: RMSNorm + per-token quant -> row-scaled GEMM
     RM, RK, RN = synth.RMS_M, synth.RMS_K, synth.RMS_N
     h, gamma = synth.rms_inputs(seed=1, device=dev)
+    # 8 distinct h buffers (63 MB each), one per step in turn, so the fused
+    # RMSNorm + quant never reads an h the cache still holds
+    NROT = 8
+    hrot = [h] + [synth.rms_inputs(seed=1 + j, device=dev)[0] for j in range(1, NROT)]
     Wr = synth.weight(RN, RK, seed=31, device=dev)
     hx = synth.normal_bf16((RM, RK), seed=2, std=3.0, device=dev)  # residual stream
     hq = torch.empty((RM, RK), dtype=torch.uint8, device=dev)
@@ -329,18 +412,23 @@ def main():
                 key = (li, j, M)
                 calls.append((f"quant_m{M}", L.fp8_quantize_block,
                               (vp(X[key].data_ptr()), M, K, vp(Xq[key].data_ptr()),
-                               vp(Xs[key].data_ptr()), sptr)))
+                               vp(Xs[key].data_ptr()), sptr), name))
                 calls.append((f"gemm_m{M}", L.fp8_gemm_a8w8_scaled,
                               (vp(Xq[key].data_ptr()), vp(Wq[wi].data_ptr()),
                                vp(Xs[key].data_ptr()), vp(Ws[wi].data_ptr()), None,
                                vp(Y[(j, M)].data_ptr()), M, N, K, fp8.GRAN_BLOCK, *gwsa,
-                               sptr)))
+                               sptr), name))
+    rms_at = len(calls)  # these two calls take h from the rotation, per step
     calls.append(("rmsnorm_quant", L.fp8_rmsnorm_quant,
                   (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hs.data_ptr()), vp(gamma.data_ptr()),
                    synth.RMS_EPS, RM, RK, 0, sptr)))
     calls.append(("add_rmsnorm_quant", L.fp8_add_rmsnorm_quant,
                   (vp(hq.data_ptr()), vp(h.data_ptr()), vp(hx.data_ptr()), vp(hs.data_ptr()),
                    vp(gamma.data_ptr()), synth.RMS_EPS, RM, RK, 0, sptr)))
+    rms_args = [[(vp(hq.data_ptr()), vp(hb.data_ptr()), vp(hs.data_ptr()), vp(gamma.data_ptr()),
+                  synth.RMS_EPS, RM, RK, 0, sptr),
+                 (vp(hq.data_ptr()), vp(hb.data_ptr()), vp(hx.data_ptr()), vp(hs.data_ptr()),
+                  vp(gamma.data_ptr()), synth.RMS_EPS, RM, RK, 0, sptr)] for hb in hrot]
     calls.append(("quant_token_w", L.fp8_quantize_token,
                   (vp(Wr.data_ptr()), RN, RK, vp(Wrq.data_ptr()), vp(Wrs.data_ptr()), sptr)))
     calls.append(("gemm_row", L.fp8_gemm_a8w8_scaled,
@@ -451,8 +539,11 @@ def main():
     for M in Ms:
         launches[f"quant_m{M}"] = launches[f"gemm_m{M}"] = layers * len(shapes)
 
-    def run_step(events=None):
-        for cat, fn, a in calls:
+    def run_step(step, events=None):
+        for ci, call in enumerate(calls):
+            cat, fn, a = call[:3]
+            if rms_at <= ci < rms_at + 2:
+                a = rms_args[step % NROT][ci - rms_at]
             if events is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -462,24 +553,28 @@ def main():
                 raise fp8.Fp8Error(cat, rc, fp8.status_string(rc))
             if events is not None:
                 e1.record(stream)
-                events.append((cat, e0, e1))
+                events.append((cat, call[3] if len(call) > 3 else None, e0, e1))
 
-    for _ in range(args.warmup):
-        run_step()
+    peaks = measured_peaks(torch, L, dev, stream)
+    for w in range(args.warmup):
+        run_step(w)
     torch.cuda.synchronize(dev)
 
     # ---- timed region: exactly `steps` steps, wall clock, synchronized ----
     events = []
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step(events)
+    for k in range(args.steps):
+        run_step(args.warmup + k, events)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
 
-    per_cat_ms = {}
-    for cat, e0, e1 in events:
-        per_cat_ms[cat] = per_cat_ms.get(cat, 0.0) + e0.elapsed_time(e1)
+    per_cat_ms, per_shape_ms = {}, {}
+    for cat, shape, e0, e1 in events:
+        ms = e0.elapsed_time(e1)
+        per_cat_ms[cat] = per_cat_ms.get(cat, 0.0) + ms
+        if shape is not None:
+            per_shape_ms[(cat, shape)] = per_shape_ms.get((cat, shape), 0.0) + ms
     ms_per_step = elapsed * 1e3 / args.steps
     total_flops = sum(w.get("flops", 0.0) for w in work.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -492,9 +587,52 @@ def main():
         if "flops" in w:
             d["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 2)
             d["frac_fp8_peak"] = round(d["tflops"] / PEAK_FP8_TFLOPS, 4)
+            d["frac_measured_mfma"] = round(d["tflops"] / peaks["mfma_fp8_tflops"], 4)
         d["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
         d["frac_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        d["frac_measured_copy"] = round(d["gbs"] / peaks["copy_gbs"], 4)
         breakdown[cat] = d
+
+    # the four linears of each M: one launch per layer and step
+    per_shape = {}
+    for (cat, shape), ms_total in per_shape_ms.items():
+        N, K = synth.DENSE_SHAPES[shape]
+        M = int(cat.split("_m")[1])
+        us = ms_total * 1e3 / (args.steps * layers)
+        d = {"M": M, "N": N, "K": K, "avg_launch_us": round(us, 3)}
+        if cat.startswith("gemm"):
+            flops = 2.0 * M * N * K
+            nbytes = M * K + N * K + 4 * (M * (K // 128) + (N // 128) * (K // 128)) + 2 * M * N
+            d["tflops"] = round(flops / us / 1e6, 2)
+            d["frac_fp8_peak"] = round(d["tflops"] / PEAK_FP8_TFLOPS, 4)
+            d["frac_hbm_roofline"] = round(max(flops / (PEAK_FP8_TFLOPS * 1e12),
+                                               nbytes / (PEAK_HBM_GBS * 1e9)) / (us * 1e-6), 4)
+        else:
+            nbytes = 3 * M * K + 4 * M * (K // 128)
+            d["gbs"] = round(nbytes / us / 1e3, 1)
+            d["frac_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        per_shape.setdefault(cat, {})[shape] = d
+
+    # the fused RMSNorm (+ residual) over the 8 rotated h buffers, alone
+    def rms_rotated(which):
+        fn = L.fp8_rmsnorm_quant if which == 0 else L.fp8_add_rmsnorm_quant
+        for j in range(NROT):
+            fn(*rms_args[j][which])
+        torch.cuda.synchronize(dev)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4 * NROT
+        ea.record(stream)
+        for j in range(reps):
+            fn(*rms_args[j % NROT][which])
+        eb.record(stream)
+        torch.cuda.synchronize(dev)
+        us = ea.elapsed_time(eb) * 1e3 / reps
+        nbytes = work["rmsnorm_quant" if which == 0 else "add_rmsnorm_quant"]["bytes"]
+        return {"avg_launch_us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+                "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                "buffers": NROT, "launches": reps}
+
+    rotated = {"rmsnorm_quant": rms_rotated(0), "add_rmsnorm_quant": rms_rotated(1)}
 
     dom = breakdown["gemm_m8192"]
     flops_per_launch = work["gemm_m8192"]["flops"] / launches["gemm_m8192"]
@@ -503,6 +641,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
         "traffic": recorded_traffic(),
+        "frac_of_measured_mfma": round(achieved / peaks["mfma_fp8_tflops"], 4),
         "kernel": "block-scaled FP8 GEMM k_gemm_pp<0, false>, the 144 M=8192 launches of a "
                   "step",
     }
@@ -542,8 +681,11 @@ def main():
             "parallelism": "single-gpu",
         },
         "roofline": roofline,
+        "measured_peaks": peaks,
         "breakdown": breakdown,
-        "device": torch.cuda.get_device_name(dev),
+        "per_shape": per_shape,
+        "rotated_inputs": rotated,
+        "env": environment(torch, dev),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows, args.cpu_sample_layers)

@@ -93,6 +93,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_inverse_rope_group_quant": ([vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
                                           vp], i32),
         "fp8_silu_f32_of_bf16": ([ctypes.c_uint32, i64, vp, vp], i32),
+        "fp8_mfma_rate_probe": ([i64, vp, vp], i32),
         "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp], i32),
         "fp8_gemm_workspace_size": ([i64, i64, i64, i32], sz),

@@ -443,6 +443,14 @@ int fp8_inverse_rope_group_quant(const void* o, const int64_t* positions, const 
                                                 rope_dim, max_pos, q, s, as_stream(stream)));
 }
 
+int fp8_mfma_rate_probe(int64_t iters, float* out, void* stream) {
+    if (iters < 0 || iters > (int64_t(1) << 32)) return FP8_ERR_ARG;
+    if (!out) return FP8_ERR_ARG;
+    if (!aligned(out, 4)) return FP8_ERR_ALIGN;
+    if (int st = device_check()) return st;
+    return launched(fp8k::launch_mfma_probe(iters, out, as_stream(stream)));
+}
+
 int fp8_silu_f32_of_bf16(uint32_t first_bits, int64_t n, float* out, void* stream) {
     if (n < 0 || first_bits > 0xFFFFu || (uint64_t)n > 0x10000u - first_bits) return FP8_ERR_ARG;
     if (n == 0) return FP8_OK;

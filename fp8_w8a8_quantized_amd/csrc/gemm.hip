@@ -2294,6 +2294,38 @@ __global__ __launch_bounds__(kThreadsP) void k_dk_reduce_wide(TileSpace S, int64
     }
 }
 
+// ---------------------------------------------------------------------------
+// Diagnostic: the matrix-core rate with operands in registers.  Every wave
+// runs `iters` rounds of 8 independent 16 x 16 x 128 E4M3 MFMAs (8
+// accumulator chains), so with 4 waves per SIMD the matrix cores never wait
+// on a dependency; the operands are fixed finite E4M3 patterns that vary by
+// lane.  out[wave] receives a sum of the accumulators (keeps the work live).
+// 2 * 16 * 16 * 128 flops per MFMA.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_mfma_probe(int64_t iters, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    v8i a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // bytes below 0x78 in magnitude: finite E4M3 values, never NaN
+        const uint32_t h = (uint32_t)(lane * 2654435761u + i * 40503u);
+        a[i] = (int)(h & 0x37373737u);
+        b[i] = (int)((h >> 3) & 0x37373737u);
+    }
+    v4f acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma_f8(a, b, acc[j]);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (lane == 0) out[wave] = t;
+}
+
 }  // namespace
 
 // The large-M kernel addresses a tile with 32-bit buffer offsets (256 rows x
@@ -2556,6 +2588,12 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
                        static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                        static_cast<const void*>(a_s), static_cast<const void*>(w_s),
                        static_cast<uint16_t*>(y), G, nullptr, 0);
+    return hipGetLastError();
+}
+
+// 1024 workgroups of 4 waves: 4 waves per SIMD on 256 CUs.
+hipError_t launch_mfma_probe(int64_t iters, float* out, hipStream_t st) {
+    hipLaunchKernelGGL(k_mfma_probe, dim3(kMfmaProbeWorkgroups), dim3(256), 0, st, iters, out);
     return hipGetLastError();
 }
 

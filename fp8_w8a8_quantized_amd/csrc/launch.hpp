@@ -70,4 +70,9 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
                                   const uint8_t* w_s, void* y, int64_t B, int64_t M, int64_t N,
                                   int64_t K, const GemmWorkspace* ws, hipStream_t st);
 
+// Diagnostic: matrix-core rate probe (register operands), 1024 workgroups of
+// 4 waves, out [4096] floats.
+constexpr int kMfmaProbeWorkgroups = 1024;
+hipError_t launch_mfma_probe(int64_t iters, float* out, hipStream_t st);
+
 }  // namespace fp8k

@@ -207,6 +207,47 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint4* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
+// One scale per row, one row per workgroup of 4 waves (rows of more than 128
+// vectors): thread t holds vectors t, t + 256, ...; the row's amax is the max
+// of the 4 waves' maxima (order-free).  Shorter chains per wave than one wave
+// per row, so a CU's workgroups drift out of phase and loads overlap stores.
+// ---------------------------------------------------------------------------
+template <int VPL4>
+__global__ __launch_bounds__(256) void k_token_row(const uint4* __restrict__ x,
+                                                   uint2* __restrict__ q,
+                                                   float* __restrict__ s, int64_t V) {
+    __shared__ float red[4];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const uint4* xr = x + row * V;
+    uint2* qr = q + row * V;
+    uint4 v[VPL4];
+#pragma unroll
+    for (int k = 0; k < VPL4; ++k) v[k] = load_or_zero_nt(xr, t + 256 * k, V);
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL4; ++k) {
+        float f[8];
+        unpack8(v[k], f);
+        m = fmaxf(m, amax8(f));
+    }
+    m = max_wave(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    const GroupDiv g = group_div(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+#pragma unroll
+    for (int k = 0; k < VPL4; ++k) {
+        const int64_t idx = t + 256 * k;
+        if (idx < V) {
+            float f[8];
+            unpack8(v[k], f);
+            store_nt8(qr + idx, encode8(f, g));
+        }
+    }
+    if (t == 0) s[row] = g.s;
+}
+
+// ---------------------------------------------------------------------------
 // Fused RMSNorm + quantization, one wave per row.
 //   sum of squares: lane l adds, in order, the squares of its vectors
 //   l, l+64, ... (elements 8v .. 8v+7 in order), then the 64 lane partials are
@@ -383,6 +424,108 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(rms_waves(V
                     store_nt8(qr + idx, encode8(y, g));
                     if ((lane & 15) == 0) s[row * groups + (idx >> 4)] = g.s;
                 }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + quantization, one row per workgroup of 4 waves (rows of
+// more than 128 vectors).  The same fixed order as above, spread over 256
+// lanes: partial l (vectors l, l + 64, l + 128, ... in order) belongs to wave
+// l / 16; lane j of wave w holds partial l = 16 w + (j & 15) and its vectors
+// i = (j >> 4), (j >> 4) + 4, ... (vector v = l + 64 i).  The ordered sum of a
+// partial passes through its 4 lanes in turn: the lane holding vector i adds
+// that vector's 8 squares in order, then a shuffle hands the running sum to
+// the lanes of vector i + 1.  The halving tree ends inside each wave over its
+// 16 partials (xor 1, 2, 4, 8) and through LDS across the waves:
+// S = (T0 + T1) + (T2 + T3).  With the row's work on 4 waves, each wave's
+// chain of loads, sums and stores is a quarter as long, and a CU holds
+// workgroups at different phases, so loads of some rows overlap the stores
+// of others.  A 1x128 group (vectors 16 g .. 16 g + 15) is 16 adjacent lanes
+// of wave g % 4 (vector slot g / 16, lane group (g / 4) % 4).
+// ---------------------------------------------------------------------------
+template <int VPL4, int GROUP, bool RES>
+__global__ __launch_bounds__(256) void k_rms_row(uint2* __restrict__ q,
+                                                 const uint4* __restrict__ x,
+                                                 uint4* __restrict__ res,
+                                                 float* __restrict__ s,
+                                                 const uint4* __restrict__ gamma, float eps,
+                                                 int64_t V) {
+    __shared__ float red[8];
+    const int t = threadIdx.x, j = t & 63, w = t >> 6;
+    const int64_t row = blockIdx.x;
+    const int l = 16 * w + (j & 15), qg = j >> 4;
+    const uint4* xr = x + row * V;
+    uint4* rr = RES ? res + row * V : nullptr;
+    uint2* qr = q + row * V;
+    uint4 v[VPL4];
+#pragma unroll
+    for (int k = 0; k < VPL4; ++k) v[k] = load_or_zero_nt(xr, l + 64 * (qg + 4 * k), V);
+    if constexpr (RES) {
+        uint4 r[VPL4];
+#pragma unroll
+        for (int k = 0; k < VPL4; ++k) r[k] = load_or_zero(rr, l + 64 * (qg + 4 * k), V);
+#pragma unroll
+        for (int k = 0; k < VPL4; ++k) {
+            const int64_t idx = l + 64 * (qg + 4 * k);
+            v[k] = add_bf16x8(v[k], r[k]);
+            if (idx < V) rr[idx] = v[k];
+        }
+    }
+    // ordered partial sums, handed from lane group to lane group
+    float P = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * VPL4; ++i) {
+        const int owner = i & 3;
+        if (qg == owner && l + 64 * i < V) P = sumsq8(P, v[i >> 2]);
+        P = __shfl(P, (j & 15) + 16 * owner);
+    }
+    float T = P;
+    T = T + __shfl_xor(T, 1);
+    T = T + __shfl_xor(T, 2);
+    T = T + __shfl_xor(T, 4);
+    T = T + __shfl_xor(T, 8);
+    if (j == 0) red[w] = T;
+    __syncthreads();
+    const float S = (red[0] + red[1]) + (red[2] + red[3]);
+    const float kf = (float)(V * 8);
+    const float inv = 1.0f / sqrtf(S / kf + eps);
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL4; ++k) {
+        const int64_t idx = l + 64 * (qg + 4 * k);
+        float y[8];
+        rms_y8(v[k], load_or_zero(gamma, idx, V), inv, y);
+        v[k] = pack_bf16x8(y);
+        if constexpr (GROUP == 0) m = fmaxf(m, amax8(y));
+    }
+    if constexpr (GROUP == 0) {
+        m = max_wave(m);
+        if (j == 0) red[4 + w] = m;
+        __syncthreads();
+        const GroupDiv g = group_div(fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+#pragma unroll
+        for (int k = 0; k < VPL4; ++k) {
+            const int64_t idx = l + 64 * (qg + 4 * k);
+            if (idx < V) {
+                float y[8];
+                unpack8(v[k], y);
+                store_nt8(qr + idx, encode8(y, g));
+            }
+        }
+        if (t == 0) s[row] = g.s;
+    } else {
+        const int64_t groups = V / 16;
+#pragma unroll
+        for (int k = 0; k < VPL4; ++k) {
+            const int64_t idx = l + 64 * (qg + 4 * k);
+            float y[8];
+            unpack8(v[k], y);
+            const GroupDiv g = group_div(max_16lanes(amax8(y)));
+            if (idx < V) {
+                store_nt8(qr + idx, encode8(y, g));
+                if ((j & 15) == 0) s[row * groups + (idx >> 4)] = g.s;
             }
         }
     }
@@ -847,6 +990,19 @@ hipError_t launch_quantize_token(const void* x, int64_t M, int64_t K, void* q, f
     const int64_t V = K / 8, blocks = (M + 3) / 4;
     const uint4* xv = static_cast<const uint4*>(x);
     uint2* qv = static_cast<uint2*>(q);
+    // rows of 129 .. 2048 vectors: one row per 4-wave workgroup (W [12288,
+    // 5120]: 33.3 -> 31.1 us on rotated inputs)
+#define FP8_TOKEN_ROW_CASE(VPL4) \
+    if (V <= 256 * VPL4) return launch(k_token_row<VPL4>, M, st, xv, qv, s, V);
+    if (V > 128 && M <= INT32_MAX) {
+        FP8_TOKEN_ROW_CASE(1)
+        FP8_TOKEN_ROW_CASE(2)
+        FP8_TOKEN_ROW_CASE(3)
+        FP8_TOKEN_ROW_CASE(4)
+        FP8_TOKEN_ROW_CASE(6)
+        FP8_TOKEN_ROW_CASE(8)
+    }
+#undef FP8_TOKEN_ROW_CASE
     // vectors per lane: the smallest instantiation that holds the row, so short
     // rows keep few registers and many waves per SIMD
 #define FP8_TOKEN_CASE(VPL) \
@@ -872,6 +1028,27 @@ hipError_t launch_rmsnorm_quant(void* q, const void* x, void* res, float* s, con
     const uint4* xv = static_cast<const uint4*>(x);
     uint4* rv = static_cast<uint4*>(res);
     const uint4* gv = static_cast<const uint4*>(gamma);
+    // with a residual, rows of 129 .. 2048 vectors take one row per 4-wave
+    // workgroup ([4096, 5120]: 32.3 -> 30.4 us on rotated inputs); without one
+    // the one-wave rows are faster (16.3 against 18.2 us)
+#define FP8_RMS_ROW(VPL4, G, R) \
+    launch(k_rms_row<VPL4, G, R>, M, st, qv, xv, rv, s, gv, eps, V)
+#define FP8_RMS_ROW_CASE(VPL4)                                                   \
+    if (V <= 256 * VPL4) {                                                       \
+        if (group_size == 0)                                                     \
+            return rv ? FP8_RMS_ROW(VPL4, 0, true) : FP8_RMS_ROW(VPL4, 0, false);  \
+        return rv ? FP8_RMS_ROW(VPL4, 128, true) : FP8_RMS_ROW(VPL4, 128, false);  \
+    }
+    if (rv != nullptr && V > 128 && M <= INT32_MAX) {
+        FP8_RMS_ROW_CASE(1)
+        FP8_RMS_ROW_CASE(2)
+        FP8_RMS_ROW_CASE(3)
+        FP8_RMS_ROW_CASE(4)
+        FP8_RMS_ROW_CASE(6)
+        FP8_RMS_ROW_CASE(8)
+    }
+#undef FP8_RMS_ROW_CASE
+#undef FP8_RMS_ROW
 #define FP8_RMS_LAUNCH(VPL, G, R) \
     launch(k_rmsnorm_quant<VPL, G, R>, blocks, st, qv, xv, rv, s, gv, eps, M, V)
 #define FP8_RMS_CASE(VPL)                                                            \

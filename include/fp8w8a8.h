@@ -393,6 +393,16 @@ int fp8_batched_gemm_a8w8_mxscale(const void* a_e4m3, const void* w_e4m3, const 
 int fp8_encode_f32_bits(uint64_t first_bits, int64_t n, void* q, void* stream);
 
 /*
+ * Diagnostic (measurement support): the matrix-core rate with operands in
+ * registers.  Launches 1024 workgroups of 4 waves; each wave runs `iters`
+ * rounds of 8 independent 16 x 16 x 128 E4M3 MFMAs (2 * 16 * 16 * 128 flops
+ * each), so the work is 4096 * iters * 8 * 65536 flops.  The caller times it
+ * (events on `stream`).  out : float [4096] device memory (one value per
+ * wave, kept so the work is not optimized away).  iters in [0, 2^32].
+ */
+int fp8_mfma_rate_probe(int64_t iters, float* out, void* stream);
+
+/*
  * Diagnostic: the device bf16 rounding alone.  out[i] = bf16 bit pattern of
  * the float with bit pattern first_bits + i, round to nearest even (the
  * rounding of the RMSNorm output y and of every bf16 GEMM output), for

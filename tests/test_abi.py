@@ -43,7 +43,8 @@ def test_header_declares_the_calls():
                      "fp8_quantize_tensors", "fp8_add_rmsnorm_quant", "fp8_swiglu_quant",
                      "fp8_silu_f32_of_bf16", "fp8_quantize_block_gather",
                      "fp8_inverse_rope_group_quant", "fp8_gemm_workspace_size",
-                     "fp8_batched_gemm_mxscale_workspace_size", "fp8_build_source_hash"):
+                     "fp8_batched_gemm_mxscale_workspace_size", "fp8_build_source_hash",
+                     "fp8_mfma_rate_probe"):
         assert required in names
 
 
@@ -292,6 +293,9 @@ def test_tensor_quant_validation(L):
 
 def test_encode_validation(L):
     vp = ctypes.c_void_p
+    assert L.fp8_mfma_rate_probe(-1, vp(FAKE), None) == ARG
+    assert L.fp8_mfma_rate_probe(4, None, None) == ARG
+    assert L.fp8_mfma_rate_probe(4, vp(FAKE + 2), None) == ALIGN
     assert L.fp8_encode_f32_bits(1 << 32, 1, vp(FAKE), None) == ARG
     assert L.fp8_encode_f32_bits(0xFFFFFFFF, 2, vp(FAKE), None) == ARG
     assert L.fp8_encode_f32_bits(0, 16, vp(FAKE + 3), None) == ALIGN

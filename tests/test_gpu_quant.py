@@ -162,8 +162,10 @@ def _eq_token(x: torch.Tensor, rows=None):
     assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
 
 
+# K = 5120 .. 16384 take one row per 4-wave workgroup (15880: a ragged last
+# vector slot); 200 and 20000 the one-wave rows
 @pytest.mark.parametrize("M,K", [(1, 8), (5, 200), (33, 4096), (64, 5120), (3, 12288),
-                                 (17, 20000), (2, 16384)])
+                                 (17, 20000), (2, 16384), (3, 15880), (1, 1032)])
 def test_token_shapes(M, K):
     say(f"quantize_token [{M}, {K}]")
     _eq_token(synth.act_col_outliers(M, K, seed=M * 7 + K))
@@ -228,9 +230,12 @@ def _eq_add_rms(x, r, gamma, group_size, eps=1e-6, rows=None):
     assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
 
 
+# with a residual, K = 1032 .. 16384 take one row per 4-wave workgroup
+# (15872, 16000: ragged last vector slots)
 @pytest.mark.parametrize("M,K,gs", [(3, 8, 0), (7, 200, 0), (5, 4096, 0), (9, 12288, 0),
                                     (4, 40000, 0), (6, 256, 128), (33, 5120, 128),
-                                    (3, 40064, 128)])
+                                    (3, 40064, 128), (5, 15872, 0), (3, 16000, 128),
+                                    (2, 1032, 0), (4, 1152, 128)])
 def test_add_rmsnorm_quant_shapes(M, K, gs):
     say(f"add_rmsnorm_quant [{M}, {K}] group_size {gs}")
     x, gamma = synth.rms_inputs(M=M, K=K, seed=M * K + 1)
