@@ -39,7 +39,7 @@ def source_hash() -> str:
     header), in name order."""
     h = hashlib.sha256()
     files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                   if f.endswith((".hip", ".hpp", ".h")))
+                   if f.endswith((".hip", ".hpp", ".h", ".c")))
     for path in files + [INCLUDE]:
         h.update(os.path.basename(path).encode() + b"\0")
         with open(path, "rb") as f:
@@ -62,9 +62,32 @@ def is_current(lib: str = LIB) -> bool:
     return built_hash(lib) == source_hash()
 
 
+SILU_GEN = os.path.join(CSRC, "gen_silu_table.c")
+SILU_INC = os.path.join(CSRC, "silu_table.inc")
+
+
+def gen_silu_table(verbose: bool = False) -> str:
+    """Build step: compile and run gen_silu_table.c (gcc, libquadmath), which
+    writes csrc/silu_table.inc, the SwiGLU kernel's table of correctly rounded
+    silu values over the middle band of bf16 inputs (it also checks the
+    kernel's closed forms on every other finite input)."""
+    exe = os.path.join(CSRC, "_gen_silu_table")
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", SILU_GEN, "-o", exe, "-lquadmath", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    try:
+        subprocess.run([exe, SILU_INC + ".tmp"], check=True)
+        os.replace(SILU_INC + ".tmp", SILU_INC)
+    finally:
+        os.remove(exe)
+    return SILU_INC
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into ``fp8_w8a8_quantized_amd/libfp8w8a8.so``,
     recording the sources' hash in it (fp8_build_source_hash)."""
+    gen_silu_table(verbose)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, f'-DFP8W8A8_SOURCE_SHA256="{source_hash()}"', *srcs, "-o", tmp]

@@ -641,28 +641,61 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
 // ---------------------------------------------------------------------------
 // SwiGLU + 1x128 quantization (the MoE chain between the gate_up and down
 // GEMMs).  gu bf16 [T, 2I]: gate = columns [0, I), up = [I, 2I).
-//   silu(g): the fp32 value nearest to g / (1 + e^-g), evaluated in fp64 and
-//   rounded once (the library's fp64 exp and IEEE division are accurate to a
-//   few 2^-53; a test over all 65536 bf16 inputs shows every result equal to
-//   the correctly rounded one);
+//   silu(g): the fp32 value nearest to g / (1 + e^-g), from closed forms and
+//   a small table built in binary128 (silu_f32 above; a test over all 65536
+//   bf16 inputs compares every value with the correctly rounded one);
 //   y = bf16_rne(silu(g) * u), one fp32 multiply;
 //   then y's 1x128 groups are quantized as k_quant_block does.
 // Layout as k_quant_block: a 1x128 group is 16 lanes x 8 elements, a wave
 // covers 4 groups per step; group gid = t * (I/128) + j reads 16 bytes of gate
 // and 16 of up per lane and writes 8 bytes of codes.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_f32(float g) {
-    const double d = (double)g;
-    return (float)(d / (1.0 + exp(-d)));
+// silu(g) of a bf16 gate, correctly rounded to fp32.  The build step
+// gen_silu_table.c computes silu in binary128 for every bf16 pattern, checks
+// that the closed forms below hold outside a middle band, and tabulates the
+// band (3424 values, 13.7 KiB), which each workgroup stages in LDS:
+//   g > 16.625: g;   g < -108.5: -0;   |g| < 2^-8: RN(g/2 + g^2/4), one
+//   fused multiply-add of exact terms (+-0 kept);
+//   else the table: positive 0x3B80..0x4185, then negative 0xBB80..0xC2D9;
+//   +inf gives +inf, -inf the quotient -inf / inf, NaN (0xFFC00000, the
+//   negative quiet NaN an fp64 evaluation of g / (1 + e^-g) returns), and a
+//   NaN gate passes through.
+// Every lane takes one table read (its index clamped into the table) and the
+// result is selected without branches, so a wave issues one LDS read per
+// element whatever the mix of cases (a never-taken fp64 branch for the
+// specials cost 6 of 45 us at the MoE shape).
+constexpr int kSiluBandN = 3424;
+__device__ const uint32_t kSiluBand[kSiluBandN] = {
+#include "silu_table.inc"
+};
+
+__device__ __forceinline__ void silu_band_to_lds(uint32_t* band) {
+    for (int i = threadIdx.x; i < kSiluBandN; i += blockDim.x) band[i] = kSiluBand[i];
+    __syncthreads();
 }
 
-__device__ __forceinline__ void swiglu8(const uint4& gv, const uint4& uv, float (&y)[8]) {
+__device__ __forceinline__ float silu_f32(float g, const uint32_t* band) {  // g a bf16 value
+    const uint32_t b = __float_as_uint(g) >> 16, a = b & 0x7FFFu;
+    const bool neg = b >= 0x8000u;
+    int idx = (int)a - 0x3B80 + (neg ? 1542 : 0);
+    idx = idx < 0 ? 0 : (idx > kSiluBandN - 1 ? kSiluBandN - 1 : idx);
+    const float t = __uint_as_float(band[idx]);
+    const float tiny = g == 0.0f ? g : fmaf(g, g * 0.25f, g * 0.5f);
+    float r = neg ? (a > 0x42D9u ? -0.0f : t) : (a > 0x4185u ? g : t);
+    r = a < 0x3B80u ? tiny : r;
+    r = a >= 0x7F80u ? (b == 0xFF80u ? __uint_as_float(0xFFC00000u) : g) : r;
+    return r;
+}
+
+__device__ __forceinline__ void swiglu8(const uint4& gv, const uint4& uv, const uint32_t* band,
+                                        float (&y)[8]) {
     float g[8], u[8];
     unpack8(gv, g);
     unpack8(uv, u);
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-        const uint32_t p = bf16x2_rne(silu_f32(g[j]) * u[j], silu_f32(g[j + 1]) * u[j + 1]);
+        const uint32_t p =
+            bf16x2_rne(silu_f32(g[j], band) * u[j], silu_f32(g[j + 1], band) * u[j + 1]);
         y[j] = bf16_lo(p);
         y[j + 1] = bf16_hi(p);
     }
@@ -673,28 +706,32 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
                                                       uint2* __restrict__ q,
                                                       float* __restrict__ s, int64_t G,
                                                       int64_t GI) {
+    __shared__ uint32_t band[kSiluBandN];
+    silu_band_to_lds(band);
     const int lane = threadIdx.x & 63, li = lane & 15;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t chunk0 = wave * U;
-    uint4 gv[U], uv[U];
+    const int64_t stride = (int64_t)gridDim.x * 4 * U;  // chunks per grid pass
+    for (int64_t chunk0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * U; chunk0 * 4 < G;
+         chunk0 += stride) {
+        uint4 gv[U], uv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
-        const int64_t gidc = gid < G ? gid : G - 1;  // lanes past the end re-read the last group
-        const int64_t t = gidc / GI, j = gidc - t * GI;
-        const int64_t row = t * GI * 32;             // uint4 index of gu[t][0]
-        gv[u] = load_nt16(gu + row + j * 16 + li);
-        uv[u] = load_nt16(gu + row + GI * 16 + j * 16 + li);
-    }
+        for (int u = 0; u < U; ++u) {
+            const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+            const int64_t gidc = gid < G ? gid : G - 1;  // lanes past the end re-read the last group
+            const int64_t t = gidc / GI, j = gidc - t * GI;
+            const int64_t row = t * GI * 32;             // uint4 index of gu[t][0]
+            gv[u] = load_nt16(gu + row + j * 16 + li);
+            uv[u] = load_nt16(gu + row + GI * 16 + j * 16 + li);
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
-        float y[8];
-        swiglu8(gv[u], uv[u], y);
-        const GroupDiv g = group_div(max_16lanes(amax8(y)));
-        if (gid < G) {
-            store_nt8(q + gid * 16 + li, encode8(y, g));
-            if (li == 0) s[gid] = g.s;
+        for (int u = 0; u < U; ++u) {
+            const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
+            float y[8];
+            swiglu8(gv[u], uv[u], band, y);
+            const GroupDiv g = group_div(max_16lanes(amax8(y)));
+            if (gid < G) {
+                store_nt8(q + gid * 16 + li, encode8(y, g));
+                if (li == 0) s[gid] = g.s;
+            }
         }
     }
 }
@@ -851,8 +888,10 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
 // Diagnostic: silu of the bf16 bit patterns first .. first + n - 1, as fp32.
 __global__ __launch_bounds__(256) void k_silu_bits(uint32_t first, int64_t n,
                                                    float* __restrict__ out) {
+    __shared__ uint32_t band[kSiluBandN];
+    silu_band_to_lds(band);
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) out[i] = silu_f32(__uint_as_float((first + (uint32_t)i) << 16));
+    if (i < n) out[i] = silu_f32(__uint_as_float((first + (uint32_t)i) << 16), band);
 }
 
 // ---------------------------------------------------------------------------
@@ -944,11 +983,14 @@ hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, v
 
 hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s,
                                hipStream_t st) {
+    // persistent: at most 4 workgroups per CU, each staging the silu table
+    // in LDS once and striding over the groups
     constexpr int U = 2;
     const int64_t GI = I / 128, G = T * GI;
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
-    return launch(k_swiglu_quant<U>, (waves + 3) / 4, st, static_cast<const uint4*>(gu),
-                  static_cast<uint2*>(q), s, G, GI);
+    const int64_t blocks = (waves + 3) / 4;
+    return launch(k_swiglu_quant<U>, blocks < 1024 ? blocks : 1024, st,
+                  static_cast<const uint4*>(gu), static_cast<uint2*>(q), s, G, GI);
 }
 
 hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const int32_t* row_token,

@@ -41,6 +41,10 @@ def test_oracle_under_asan_ubsan(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 def test_abi_validation_under_asan_ubsan(tmp_path):
+    from fp8_w8a8_quantized_amd import build
+
+    if not os.path.exists(build.SILU_INC):  # generated at build time
+        build.gen_silu_table()
     exe = str(tmp_path / "abi_sanitize")
     srcs = [os.path.join(CSRC, f) for f in ("api.hip", "quant.hip", "gemm.hip")]
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
