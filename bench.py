@@ -32,7 +32,8 @@ there.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the work.
 ``--calibrate-copy`` instead runs a plain device copy of 1 GiB a few times,
 the reference kernel whose counter reading scales FETCH_SIZE / WRITE_SIZE.
 ``--one-gemm M N K`` instead runs one block-scaled GEMM shape (seeded dense
-inputs, quantized by the library) ``--reps`` times, for counter runs.
+inputs, quantized by the library) ``--reps`` times over ``--copies`` distinct
+operand sets, for counter runs.
 """
 from __future__ import annotations
 
@@ -101,29 +102,38 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
-def one_gemm(M: int, N: int, K: int, reps: int):
-    """One block-scaled GEMM shape, reps launches (for counter runs)."""
+def one_gemm(M: int, N: int, K: int, reps: int, copies: int = 1):
+    """One block-scaled GEMM shape, reps launches (for counter runs).  With
+    copies > 1 the launches rotate over that many distinct operand sets, so
+    weights stream from HBM as in a model's layers."""
     import torch
 
     import fp8_w8a8_quantized_amd as fp8
     import synth
 
     dev = torch.device("cuda:0")
-    X = synth.act_col_outliers(M, K, seed=1, device=dev)
-    W = synth.weight(N, K, seed=2, device=dev)
-    a = fp8.quantize_block(X)
-    (w,) = fp8.requantize_weights([W], fp8.SCALE_F32)
+    ops = []
+    for c in range(copies):
+        X = synth.act_col_outliers(M, K, seed=1 + 2 * c, device=dev)
+        W = synth.weight(N, K, seed=2 + 2 * c, device=dev)
+        a = fp8.quantize_block(X)
+        (w,) = fp8.requantize_weights([W], fp8.SCALE_F32)
+        ops.append((a, w))
+        del X, W
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((max(fp8.gemm_workspace_size(M, N, K), 16),), dtype=torch.uint8, device=dev)
+    for a, w in ops:  # warm-up: one launch per operand set
+        fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK, out=y, workspace=ws)
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
+    for r in range(reps):
+        a, w = ops[r % copies]
         fp8.gemm_a8w8_scaled(a, w, fp8.GRAN_BLOCK, out=y, workspace=ws)
     e1.record()
     torch.cuda.synchronize(dev)
     us = e0.elapsed_time(e1) * 1e3 / reps
-    print(json.dumps({"gemm": [M, N, K], "reps": reps, "avg_us": round(us, 2),
+    print(json.dumps({"gemm": [M, N, K], "reps": reps, "copies": copies, "avg_us": round(us, 2),
                       "tflops": round(2.0 * M * N * K / us / 1e6, 1)}))
 
 
@@ -216,6 +226,7 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--one-gemm", type=int, nargs=3, metavar=("M", "N", "K"))
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=1)
     return ap.parse_args()
 
 
@@ -270,7 +281,7 @@ def main():
         calibrate_copy()
         return
     if args.one_gemm:
-        one_gemm(*args.one_gemm, args.reps)
+        one_gemm(*args.one_gemm, args.reps, args.copies)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
