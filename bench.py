@@ -170,6 +170,10 @@ def gpu_clock():
     cannot be read)."""
     import subprocess
 
+    # under rocprofv3 the child would inherit the profiler's preloaded
+    # library and start on the GPU before rocm-smi's interpreter replaces it
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
                            timeout=20)
