@@ -60,11 +60,23 @@ __device__ __forceinline__ float amax8(const float (&f)[8]) {
 }
 
 // Max over aligned groups of 16 lanes (order-free, so exact).
+// max with the value of another lane of the same 16-lane row, by a DPP
+// move (no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF,
+                                                               0xF, false)));
+}
+
+// Max over each aligned group of 16 lanes, in every lane of the group: lane
+// i ^ 1, then i ^ 2 (quad permutes), then 7 - i within 8 lanes and 15 - i
+// within 16 (half-row and row mirrors); fmax is order-free, so the result is
+// the group's max whatever the pairing.
 __device__ __forceinline__ float max_16lanes(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = max_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = max_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = max_dpp<0x141>(v);  // row_half_mirror
+    v = max_dpp<0x140>(v);  // row_mirror
     return v;
 }
 

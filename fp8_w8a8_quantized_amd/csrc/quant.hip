@@ -642,7 +642,7 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
 // SwiGLU + 1x128 quantization (the MoE chain between the gate_up and down
 // GEMMs).  gu bf16 [T, 2I]: gate = columns [0, I), up = [I, 2I).
 //   silu(g): the fp32 value nearest to g / (1 + e^-g), from closed forms and
-//   a small table built in binary128 (silu_f32 above; a test over all 65536
+//   a small table built in binary128 (silu_f32 below; a test over all 65536
 //   bf16 inputs compares every value with the correctly rounded one);
 //   y = bf16_rne(silu(g) * u), one fp32 multiply;
 //   then y's 1x128 groups are quantized as k_quant_block does.
@@ -653,18 +653,23 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
 // silu(g) of a bf16 gate, correctly rounded to fp32.  The build step
 // gen_silu_table.c computes silu in binary128 for every bf16 pattern, checks
 // that the closed forms below hold outside a middle band, and tabulates the
-// band (3424 values, 13.7 KiB), which each workgroup stages in LDS:
-//   g > 16.625: g;   g < -108.5: -0;   |g| < 2^-8: RN(g/2 + g^2/4), one
-//   fused multiply-add of exact terms (+-0 kept);
-//   else the table: positive 0x3B80..0x4185, then negative 0xBB80..0xC2D9;
-//   +inf gives +inf, -inf the quotient -inf / inf, NaN (0xFFC00000, the
-//   negative quiet NaN an fp64 evaluation of g / (1 + e^-g) returns), and a
-//   NaN gate passes through.
-// Every lane takes one table read (its index clamped into the table) and the
-// result is selected without branches, so a wave issues one LDS read per
-// element whatever the mix of cases (a never-taken fp64 branch for the
-// specials cost 6 of 45 us at the MoE shape).
-constexpr int kSiluBandN = 3424;
+// band, which each workgroup stages in LDS (3426 words, 13.4 KiB):
+//   [0, 1541]     silu of the positive gates 0x3B80..0x4185 (2^-8 .. 16.625)
+//   1542          unused (read by lanes whose value is selected elsewhere)
+//   [1543, 3424]  silu of the negative gates 0xBB80..0xC2D9 (-2^-8 .. -108.5)
+//   3425          -0, silu of every finite gate below -108.5
+// A gate's word is h - 0x3B80 (h >= 0) or h - 0xB579 (h < 0), h its bf16
+// bits, clamped to [0, 3425]; two gates' words come from 16-bit packed
+// integer operations on the pair as loaded.  Then, without branches:
+//   |g| < 2^-8: RN(g/2 + g^2/4), one fused multiply-add of exact terms, with
+//   g's sign (so +-0 stay +-0);   g > 16.625 (and +inf): g;
+//   -inf: the quiet NaN 0xFFC00000 (the quotient -inf / inf an fp64
+//   evaluation of g / (1 + e^-g) returns), which is g's bits with the quiet
+//   bit set; a NaN gate gives a NaN of its sign the same way;
+//   else the table word (-0 for finite g < -108.5).
+// A test over all 65536 bf16 inputs compares every non-NaN value with the
+// correctly rounded one.
+constexpr int kSiluBandN = 3426;
 __device__ const uint32_t kSiluBand[kSiluBandN] = {
 #include "silu_table.inc"
 };
@@ -674,33 +679,72 @@ __device__ __forceinline__ void silu_band_to_lds(uint32_t* band) {
     __syncthreads();
 }
 
-__device__ __forceinline__ float silu_f32(float g, const uint32_t* band) {  // g a bf16 value
-    const uint32_t b = __float_as_uint(g) >> 16, a = b & 0x7FFFu;
-    const bool neg = b >= 0x8000u;
-    int idx = (int)a - 0x3B80 + (neg ? 1542 : 0);
-    idx = idx < 0 ? 0 : (idx > kSiluBandN - 1 ? kSiluBandN - 1 : idx);
-    const float t = __uint_as_float(band[idx]);
-    const float tiny = g == 0.0f ? g : fmaf(g, g * 0.25f, g * 0.5f);
-    float r = neg ? (a > 0x42D9u ? -0.0f : t) : (a > 0x4185u ? g : t);
-    r = a < 0x3B80u ? tiny : r;
-    r = a >= 0x7F80u ? (b == 0xFF80u ? __uint_as_float(0xFFC00000u) : g) : r;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Byte offsets into the table of the two bf16 gates in w (low half, then
+// high half), each computed in its own 16-bit lane.
+__device__ __forceinline__ void silu_offsets(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const u16x2 h = __builtin_bit_cast(u16x2, w);
+    const u16x2 neg = __builtin_bit_cast(u16x2, __builtin_bit_cast(s16x2, h) >> (s16x2)15);
+    const u16x2 d = h - (u16x2)0x3B80u - (neg & (u16x2)(0xB579u - 0x3B80u));
+    s16x2 c = __builtin_elementwise_max(__builtin_bit_cast(s16x2, d), (s16x2)0);
+    c = __builtin_elementwise_min(c, (s16x2)(kSiluBandN - 1));
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, c) << (u16x2)2);
+    lo = b & 0xFFFFu;
+    hi = b >> 16;
+}
+
+__device__ __forceinline__ float silu_select(float g, float t) {
+    // -inf and NaN first, so each select takes cheap operands (the compiler
+    // keeps the sequence branch-free); later selects never fire for them
+    float r = !(g >= -3.40282346638528859812e+38f)
+                  ? __uint_as_float(__float_as_uint(g) | 0x00400000u) : t;
+    const float tiny = __builtin_copysignf(fmaf(g, g * 0.25f, g * 0.5f), g);
+    r = fabsf(g) < 0x1p-8f ? tiny : r;
+    r = g > 16.625f ? g : r;
     return r;
 }
 
+__device__ __forceinline__ float band_word(const uint32_t* band, uint32_t byte_off) {
+    return __uint_as_float(*reinterpret_cast<const uint32_t*>(
+        reinterpret_cast<const uint8_t*>(band) + byte_off));
+}
+
+__device__ __forceinline__ float silu_f32(float g, const uint32_t* band) {  // g a bf16 value
+    uint32_t lo, hi;
+    silu_offsets(__float_as_uint(g) >> 16, lo, hi);
+    return silu_select(g, band_word(band, lo));
+}
+
+// y = bf16_rne(silu(g) * u) for a lane's 8 gate and 8 up values; the 8 table
+// reads are issued before any of them is used.
 __device__ __forceinline__ void swiglu8(const uint4& gv, const uint4& uv, const uint32_t* band,
                                         float (&y)[8]) {
-    float g[8], u[8];
+    float g[8], u[8], t[8];
     unpack8(gv, g);
     unpack8(uv, u);
+    const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t lo, hi;
+        silu_offsets(w[k], lo, hi);
+        t[2 * k] = band_word(band, lo);
+        t[2 * k + 1] = band_word(band, hi);
+    }
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-        const uint32_t p =
-            bf16x2_rne(silu_f32(g[j], band) * u[j], silu_f32(g[j + 1], band) * u[j + 1]);
+        const uint32_t p = bf16x2_rne(silu_select(g[j], t[j]) * u[j],
+                                      silu_select(g[j + 1], t[j + 1]) * u[j + 1]);
         y[j] = bf16_lo(p);
         y[j + 1] = bf16_hi(p);
     }
 }
 
+// Persistent: each workgroup stages the table once and strides over the
+// groups.  A lane keeps, for each of its U groups, the group index and the
+// uint4 offset of its gate chunk in gu, and advances both by the grid
+// stride (the row and the column block as a carry, no division per step).
 template <int U>
 __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ gu,
                                                       uint2* __restrict__ q,
@@ -709,28 +753,44 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
     __shared__ uint32_t band[kSiluBandN];
     silu_band_to_lds(band);
     const int lane = threadIdx.x & 63, li = lane & 15;
-    const int64_t stride = (int64_t)gridDim.x * 4 * U;  // chunks per grid pass
-    for (int64_t chunk0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * U; chunk0 * 4 < G;
-         chunk0 += stride) {
+    const int64_t step = (int64_t)gridDim.x * 16 * U;  // groups per grid pass
+    const int64_t dt = step / GI, dj = step - dt * GI;
+    const int64_t row_u4 = GI * 32;                  // uint4 per row of gu (2I bf16)
+    const int64_t doff = dt * row_u4 + dj * 16;
+    const int64_t first = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * U * 4;
+    int64_t gid[U], j[U], off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        gid[u] = first + u * 4 + (lane >> 4);
+        const int64_t t = gid[u] / GI;
+        j[u] = gid[u] - t * GI;
+        off[u] = t * row_u4 + j[u] * 16;
+    }
+    const int64_t tl = (G - 1) / GI;  // lanes past the end re-read the last group
+    const int64_t off_last = tl * row_u4 + (G - 1 - tl * GI) * 16;
+    for (int64_t g0 = first; g0 < G; g0 += step) {
         uint4 gv[U], uv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
-            const int64_t gidc = gid < G ? gid : G - 1;  // lanes past the end re-read the last group
-            const int64_t t = gidc / GI, j = gidc - t * GI;
-            const int64_t row = t * GI * 32;             // uint4 index of gu[t][0]
-            gv[u] = load_nt16(gu + row + j * 16 + li);
-            uv[u] = load_nt16(gu + row + GI * 16 + j * 16 + li);
+            const int64_t o = (gid[u] < G ? off[u] : off_last) + li;
+            gv[u] = load_nt16(gu + o);
+            uv[u] = load_nt16(gu + o + GI * 16);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
             float y[8];
             swiglu8(gv[u], uv[u], band, y);
             const GroupDiv g = group_div(max_16lanes(amax8(y)));
-            if (gid < G) {
-                store_nt8(q + gid * 16 + li, encode8(y, g));
-                if (li == 0) s[gid] = g.s;
+            if (gid[u] < G) {
+                store_nt8(q + gid[u] * 16 + li, encode8(y, g));
+                if (li == 0) s[gid[u]] = g.s;
+            }
+            gid[u] += step;
+            j[u] += dj;
+            off[u] += doff;
+            if (j[u] >= GI) {  // carry into the next row
+                j[u] -= GI;
+                off[u] += GI * 16;
             }
         }
     }
@@ -983,13 +1043,13 @@ hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, v
 
 hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s,
                                hipStream_t st) {
-    // persistent: at most 4 workgroups per CU, each staging the silu table
-    // in LDS once and striding over the groups
+    // persistent: at most 8 workgroups per CU (8 waves per SIMD), each
+    // staging the silu table in LDS once and striding over the groups
     constexpr int U = 2;
     const int64_t GI = I / 128, G = T * GI;
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
     const int64_t blocks = (waves + 3) / 4;
-    return launch(k_swiglu_quant<U>, blocks < 1024 ? blocks : 1024, st,
+    return launch(k_swiglu_quant<U>, blocks < 2048 ? blocks : 2048, st,
                   static_cast<const uint4*>(gu), static_cast<uint2*>(q), s, G, GI);
 }
 
