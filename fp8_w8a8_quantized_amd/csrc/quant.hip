@@ -622,6 +622,13 @@ hipError_t launch(Kern k, int64_t blocks, hipStream_t st, Args... args) {
     return hipGetLastError();
 }
 
+template <typename Kern, typename... Args>
+hipError_t launch_threads(Kern k, int64_t blocks, int threads, hipStream_t st, Args... args) {
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3((unsigned)threads), 0, st, args...);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Diagnostic: bf16 rounding (the device helper every bf16 output uses) of the
 // fp32 bit patterns first .. first + n - 1.
@@ -653,29 +660,32 @@ __global__ __launch_bounds__(256) void k_bf16_bits(uint64_t first, int64_t n,
 // silu(g) of a bf16 gate, correctly rounded to fp32.  The build step
 // gen_silu_table.c computes silu in binary128 for every bf16 pattern, checks
 // that the closed forms below hold outside a middle band, and tabulates the
-// band, which each workgroup stages in LDS (3426 words, 13.4 KiB):
-//   [0, 1541]     silu of the positive gates 0x3B80..0x4185 (2^-8 .. 16.625)
-//   1542          unused (read by lanes whose value is selected elsewhere)
-//   [1543, 3424]  silu of the negative gates 0xBB80..0xC2D9 (-2^-8 .. -108.5)
-//   3425          -0, silu of every finite gate below -108.5
-// A gate's word is h - 0x3B80 (h >= 0) or h - 0xB579 (h < 0), h its bf16
-// bits, clamped to [0, 3425]; two gates' words come from 16-bit packed
-// integer operations on the pair as loaded.  Then, without branches:
-//   |g| < 2^-8: RN(g/2 + g^2/4), one fused multiply-add of exact terms, with
-//   g's sign (so +-0 stay +-0);   g > 16.625 (and +inf): g;
+// band, which each workgroup stages in LDS (7522 words, 29.4 KiB):
+//   [0, 3589]     silu of the positive gates 0x3380..0x4185 (2^-24 .. 16.625)
+//   3590          unused (read by lanes whose value is selected elsewhere)
+//   [3591, 7520]  silu of the negative gates 0xB380..0xC2D9 (-2^-24 .. -108.5)
+//   7521          -0, silu of every finite gate below -108.5
+// A gate's word is h - 0x3380 (h >= 0) or h - 0xA579 (h < 0), h its bf16
+// bits, clamped to [0, 7521]; two gates' words come from 16-bit packed
+// integer operations on the pair as loaded.  Outside the table:
+//   |g| < 2^-24: g / 2 (exact; the next term, g^2/4, is below half an ulp);
+//   g > 16.625 (and +inf): g;
 //   -inf: the quiet NaN 0xFFC00000 (the quotient -inf / inf an fp64
 //   evaluation of g / (1 + e^-g) returns), which is g's bits with the quiet
 //   bit set; a NaN gate gives a NaN of its sign the same way;
-//   else the table word (-0 for finite g < -108.5).
+//   finite g < -108.5: the table's -0.
 // A test over all 65536 bf16 inputs compares every non-NaN value with the
 // correctly rounded one.
-constexpr int kSiluBandN = 3426;
-__device__ const uint32_t kSiluBand[kSiluBandN] = {
+constexpr int kSiluBandN = 7522;
+constexpr int kSiluBandPad = 7524;  // 16-byte multiple, for the staging copy
+__device__ const uint32_t kSiluBand[kSiluBandPad] = {
 #include "silu_table.inc"
 };
 
 __device__ __forceinline__ void silu_band_to_lds(uint32_t* band) {
-    for (int i = threadIdx.x; i < kSiluBandN; i += blockDim.x) band[i] = kSiluBand[i];
+    const uint4* src = reinterpret_cast<const uint4*>(kSiluBand);
+    uint4* dst = reinterpret_cast<uint4*>(band);
+    for (int i = threadIdx.x; i < kSiluBandPad / 4; i += blockDim.x) dst[i] = src[i];
     __syncthreads();
 }
 
@@ -687,7 +697,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void silu_offsets(uint32_t w, uint32_t& lo, uint32_t& hi) {
     const u16x2 h = __builtin_bit_cast(u16x2, w);
     const u16x2 neg = __builtin_bit_cast(u16x2, __builtin_bit_cast(s16x2, h) >> (s16x2)15);
-    const u16x2 d = h - (u16x2)0x3B80u - (neg & (u16x2)(0xB579u - 0x3B80u));
+    const u16x2 d = h - (u16x2)0x3380u - (neg & (u16x2)(0xA579u - 0x3380u));
     s16x2 c = __builtin_elementwise_max(__builtin_bit_cast(s16x2, d), (s16x2)0);
     c = __builtin_elementwise_min(c, (s16x2)(kSiluBandN - 1));
     const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, c) << (u16x2)2);
@@ -695,13 +705,13 @@ __device__ __forceinline__ void silu_offsets(uint32_t w, uint32_t& lo, uint32_t&
     hi = b >> 16;
 }
 
+// silu of gate g from its table word t, for any g.
 __device__ __forceinline__ float silu_select(float g, float t) {
     // -inf and NaN first, so each select takes cheap operands (the compiler
     // keeps the sequence branch-free); later selects never fire for them
     float r = !(g >= -3.40282346638528859812e+38f)
                   ? __uint_as_float(__float_as_uint(g) | 0x00400000u) : t;
-    const float tiny = __builtin_copysignf(fmaf(g, g * 0.25f, g * 0.5f), g);
-    r = fabsf(g) < 0x1p-8f ? tiny : r;
+    r = fabsf(g) < 0x1p-24f ? g * 0.5f : r;
     r = g > 16.625f ? g : r;
     return r;
 }
@@ -718,47 +728,71 @@ __device__ __forceinline__ float silu_f32(float g, const uint32_t* band) {  // g
 }
 
 // y = bf16_rne(silu(g) * u) for a lane's 8 gate and 8 up values; the 8 table
-// reads are issued before any of them is used.
+// reads are issued before any of them is used.  When every gate of the wave
+// is in the table's domain (2^-24 <= |g| <= 16.625, or g negative and
+// finite: 16-bit min / max of the patterns decide it), the table word is
+// silu(g) and the selects are skipped.
 __device__ __forceinline__ void swiglu8(const uint4& gv, const uint4& uv, const uint32_t* band,
                                         float (&y)[8]) {
     float g[8], u[8], t[8];
     unpack8(gv, g);
     unpack8(uv, u);
     const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+    u16x2 amin = (u16x2)0xFFFFu, amax = (u16x2)0u;
+    s16x2 hmax = (s16x2)-32768;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         uint32_t lo, hi;
         silu_offsets(w[k], lo, hi);
         t[2 * k] = band_word(band, lo);
         t[2 * k + 1] = band_word(band, hi);
+        const u16x2 a = __builtin_bit_cast(u16x2, w[k]) & (u16x2)0x7FFFu;
+        amin = __builtin_elementwise_min(amin, a);
+        amax = __builtin_elementwise_max(amax, a);
+        hmax = __builtin_elementwise_max(hmax, __builtin_bit_cast(s16x2, w[k]));
     }
+    // every |g| >= 2^-24, no gate above 16.625, no infinity or NaN
+    const bool in = amin.x >= 0x3380u && amin.y >= 0x3380u && hmax.x <= 0x4185 &&
+                    hmax.y <= 0x4185 && amax.x < 0x7F80u && amax.y < 0x7F80u;
+    if (__builtin_expect(__all(in), 1)) {
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-        const uint32_t p = bf16x2_rne(silu_select(g[j], t[j]) * u[j],
-                                      silu_select(g[j + 1], t[j + 1]) * u[j + 1]);
-        y[j] = bf16_lo(p);
-        y[j + 1] = bf16_hi(p);
+        for (int j = 0; j < 8; j += 2) {
+            const uint32_t p = bf16x2_rne(t[j] * u[j], t[j + 1] * u[j + 1]);
+            y[j] = bf16_lo(p);
+            y[j + 1] = bf16_hi(p);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const uint32_t p = bf16x2_rne(silu_select(g[j], t[j]) * u[j],
+                                          silu_select(g[j + 1], t[j + 1]) * u[j + 1]);
+            y[j] = bf16_lo(p);
+            y[j + 1] = bf16_hi(p);
+        }
     }
 }
 
-// Persistent: each workgroup stages the table once and strides over the
-// groups.  A lane keeps, for each of its U groups, the group index and the
-// uint4 offset of its gate chunk in gu, and advances both by the grid
-// stride (the row and the column block as a carry, no division per step).
+// Persistent: 512-thread workgroups, each staging the table once and striding
+// over the groups.  A lane keeps, for each of its U groups, the group index
+// and the uint4 offset of its gate chunk in gu, and advances both by the
+// grid stride (the row and the column block as a carry, no division per
+// step).  The loads of a pass are issued before the previous pass is
+// computed (the first pass's before the table is staged), so every wave has
+// a pass of gate and up values in flight while it computes.
+constexpr int kSwigluWaves = 8;
 template <int U>
-__global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ gu,
-                                                      uint2* __restrict__ q,
-                                                      float* __restrict__ s, int64_t G,
-                                                      int64_t GI) {
-    __shared__ uint32_t band[kSiluBandN];
-    silu_band_to_lds(band);
+__global__ __launch_bounds__(64 * kSwigluWaves) void k_swiglu_quant(const uint4* __restrict__ gu,
+                                                                   uint2* __restrict__ q,
+                                                                   float* __restrict__ s,
+                                                                   int64_t G, int64_t GI) {
+    __shared__ __align__(16) uint32_t band[kSiluBandPad];
     const int lane = threadIdx.x & 63, li = lane & 15;
-    const int64_t step = (int64_t)gridDim.x * 16 * U;  // groups per grid pass
+    const int64_t step = (int64_t)gridDim.x * kSwigluWaves * 4 * U;  // groups per grid pass
     const int64_t dt = step / GI, dj = step - dt * GI;
-    const int64_t row_u4 = GI * 32;                  // uint4 per row of gu (2I bf16)
+    const int64_t row_u4 = GI * 32;  // uint4 per row of gu (2I bf16)
     const int64_t doff = dt * row_u4 + dj * 16;
-    const int64_t first = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * U * 4;
-    int64_t gid[U], j[U], off[U];
+    const int64_t first = ((int64_t)blockIdx.x * kSwigluWaves + (threadIdx.x >> 6)) * U * 4;
+    int64_t gid[U], j[U], off[U];  // of the pass being loaded
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         gid[u] = first + u * 4 + (lane >> 4);
@@ -768,23 +802,15 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
     }
     const int64_t tl = (G - 1) / GI;  // lanes past the end re-read the last group
     const int64_t off_last = tl * row_u4 + (G - 1 - tl * GI) * 16;
-    for (int64_t g0 = first; g0 < G; g0 += step) {
-        uint4 gv[U], uv[U];
+    uint4 gv[U], uv[U];
+    int64_t gc[U];  // group index of the pass in gv, uv
+    auto load_pass = [&](uint4 (&a)[U], uint4 (&b)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t o = (gid[u] < G ? off[u] : off_last) + li;
-            gv[u] = load_nt16(gu + o);
-            uv[u] = load_nt16(gu + o + GI * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float y[8];
-            swiglu8(gv[u], uv[u], band, y);
-            const GroupDiv g = group_div(max_16lanes(amax8(y)));
-            if (gid[u] < G) {
-                store_nt8(q + gid[u] * 16 + li, encode8(y, g));
-                if (li == 0) s[gid[u]] = g.s;
-            }
+            a[u] = load_nt16(gu + o);
+            b[u] = load_nt16(gu + o + GI * 16);
+            gc[u] = gid[u];
             gid[u] += step;
             j[u] += dj;
             off[u] += doff;
@@ -792,6 +818,30 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const uint4* __restrict__ 
                 j[u] -= GI;
                 off[u] += GI * 16;
             }
+        }
+    };
+    if (first < G) load_pass(gv, uv);
+    silu_band_to_lds(band);
+    for (int64_t g0 = first; g0 < G; g0 += step) {
+        int64_t gcur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) gcur[u] = gc[u];
+        uint4 gn[U], un[U];
+        if (g0 + step < G) load_pass(gn, un);  // wave-uniform
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float y[8];
+            swiglu8(gv[u], uv[u], band, y);
+            const GroupDiv g = group_div(max_16lanes(amax8(y)));
+            if (gcur[u] < G) {
+                store_nt8(q + gcur[u] * 16 + li, encode8(y, g));
+                if (li == 0) s[gcur[u]] = g.s;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            gv[u] = gn[u];
+            uv[u] = un[u];
         }
     }
 }
@@ -948,7 +998,7 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
 // Diagnostic: silu of the bf16 bit patterns first .. first + n - 1, as fp32.
 __global__ __launch_bounds__(256) void k_silu_bits(uint32_t first, int64_t n,
                                                    float* __restrict__ out) {
-    __shared__ uint32_t band[kSiluBandN];
+    __shared__ __align__(16) uint32_t band[kSiluBandPad];
     silu_band_to_lds(band);
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) out[i] = silu_f32(__uint_as_float((first + (uint32_t)i) << 16), band);
@@ -1043,13 +1093,14 @@ hipError_t launch_quantize_block(const void* x, int64_t M, int64_t K, void* q, v
 
 hipError_t launch_swiglu_quant(const void* gu, int64_t T, int64_t I, void* q, float* s,
                                hipStream_t st) {
-    // persistent: at most 8 workgroups per CU (8 waves per SIMD), each
-    // staging the silu table in LDS once and striding over the groups
-    constexpr int U = 2;
+    // persistent: at most 4 workgroups of 8 waves per CU (the LDS holds four
+    // copies of the table), striding over the groups; one group per lane and
+    // pass keeps the kernel at 55 VGPRs, so all 8 waves per SIMD fit
+    constexpr int U = 1;
     const int64_t GI = I / 128, G = T * GI;
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
-    const int64_t blocks = (waves + 3) / 4;
-    return launch(k_swiglu_quant<U>, blocks < 2048 ? blocks : 2048, st,
+    const int64_t blocks = (waves + kSwigluWaves - 1) / kSwigluWaves;
+    return launch_threads(k_swiglu_quant<U>, blocks < 1024 ? blocks : 1024, 64 * kSwigluWaves, st,
                   static_cast<const uint4*>(gu), static_cast<uint2*>(q), s, G, GI);
 }
 

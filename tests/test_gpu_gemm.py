@@ -409,6 +409,20 @@ def test_grouped_big_tiles_ragged_experts():
     assert_rows_close(y, ref, what="grouped big tiles")
 
 
+def test_grouped_big_tiles_ragged_full_columns():
+    """Experts averaging >= 192 rows with N % 256 == 0 (the ping-pong
+    kernel): counts on both sides of the 128- and 256-row boundaries of an
+    expert's last tile (256 + 1, 256 + 128, 256 + 129, 512 + 1, ...)."""
+    say("grouped GEMM, 256-row tiles, ragged experts, N % 256 == 0")
+    counts = [0, 1, 255, 256, 257, 300, 384, 385, 600, 900, 130, 513, 640, 641]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T, N, K = int(offsets[-1]), 512, 384
+    A = synth.act_col_outliers(T, K, seed=23)
+    W = synth.normal_bf16((len(counts), N, K), seed=24, std=0.02)
+    y, ref, rows = _grouped_pipeline(A, W, offsets)
+    assert_rows_close(y, ref, what="grouped ragged full columns")
+
+
 def test_grouped_big_tiles_rows_outside_offsets_untouched():
     say("grouped GEMM, 256-row tiles, rows outside [offsets[0], offsets[E]) untouched")
     offsets = np.array([10, 300, 300, 1700], np.int32)
