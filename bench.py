@@ -575,14 +575,21 @@ def main():
         run_step(w)
     torch.cuda.synchronize(dev)
 
-    # ---- timed region: exactly `steps` steps, wall clock, synchronized ----
-    events = []
+    # ---- timed region: exactly `steps` steps, wall clock, synchronized; no
+    # per-op events inside it (they would add their own commands to the step)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for k in range(args.steps):
-        run_step(args.warmup + k, events)
+        run_step(args.warmup + k)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+
+    # ---- the same steps again with a HIP event pair around every launch, for
+    # the per-op breakdown (each pair spans its launch on the library's stream)
+    events = []
+    for k in range(args.steps):
+        run_step(args.warmup + args.steps + k, events)
+    torch.cuda.synchronize(dev)
 
     per_cat_ms, per_shape_ms = {}, {}
     for cat, shape, e0, e1 in events:
