@@ -78,8 +78,9 @@ def main():
 
     print("# HBM traffic: block-scaled GEMM `k_gemm_pp<0, false>`, the M=8192 dense linears\n")
     print("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own "
-          "rocprofv3 run, over one step of the four M=8192 linears (qkv, o, gate_up, down; "
-          "one launch each), scaled by the same counters over a plain 1 GiB device copy.\n")
+          "rocprofv3 run, over bench.py's one timed and one instrumented step of the four "
+          "M=8192 linears (qkv, o, gate_up, down; two launches each), scaled by the same "
+          "counters over a plain 1 GiB device copy.\n")
     print("Commands (from the repository root `R` on one MI355X, after "
           "`cd /tmp && export TMPDIR=/tmp`):\n")
     print("```")
@@ -95,7 +96,7 @@ def main():
     print(f"- `algorithmic_bytes_per_launch`: `{alg:.0f}`")
     print(f"- `traffic_over_algorithmic`: `{traffic / alg:.3f}`")
     print(f"- `source_sha256`: `{bench.gemm_source_hash()}`")
-    print("\nPer-launch values are means over the dispatches of the kernel (one per "
+    print("\nPer-launch values are means over the dispatches of the kernel (two per "
           "linear shape, so the mean matches the per-launch mean over a 36-layer step). "
           "The factors are counter bytes per true byte of the copy; traffic divides the "
           "GEMM's counter bytes by them.")
