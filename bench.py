@@ -419,7 +419,7 @@ def main():
     torch.cuda.synchronize(dev)
 
     # ---- pre-marshalled calls of one step, grouped by kernel category ----
-    calls = [("requant", L.fp8_requantize_weights, (descs, len(W), fp8.SCALE_F32, sptr))]
+    calls = [("requant", L.fp8_requantize_weights, (descs, len(W), fp8.SCALE_F32, None, 0, sptr))]
     for li in range(layers):
         for j, (name, (N, K)) in enumerate(shapes):
             wi = 4 * li + j
@@ -450,7 +450,7 @@ def main():
                   (vp(hq.data_ptr()), vp(Wrq.data_ptr()), vp(hs.data_ptr()), vp(Wrs.data_ptr()),
                    None, vp(Yr.data_ptr()), RM, RN, RK, fp8.GRAN_ROW, *gwsa, sptr)))
     calls.append(("requant_e8m0", L.fp8_requantize_weights,
-                  (descs8, len(W), fp8.SCALE_E8M0, sptr)))
+                  (descs8, len(W), fp8.SCALE_E8M0, None, 0, sptr)))
     for j, (name, (N, K)) in enumerate(shapes):
         key = (0, j, MXM)
         calls.append(("quant_e8m0_m8192", L.fp8_quantize_block_e8m0,
@@ -461,7 +461,7 @@ def main():
                        vp(Ws8[j].data_ptr()), vp(Y[(j, MXM)].data_ptr()), 1, MXM, N, K, *gwsa,
                        sptr)))
     calls.append(("quant_kv_tensor", L.fp8_quantize_tensors, (kvdescs, len(kv_x), sptr)))
-    calls.append(("requant_e8m0_wo", L.fp8_requantize_weights, (rdesc, 1, fp8.SCALE_E8M0, sptr)))
+    calls.append(("requant_e8m0_wo", L.fp8_requantize_weights, (rdesc, 1, fp8.SCALE_E8M0, None, 0, sptr)))
     calls.append(("rope_quant_m8192", L.fp8_inverse_rope_group_quant,
                   (vp(ro.data_ptr()), vp(rpos.data_ptr()), vp(rcos.data_ptr()),
                    vp(rsin.data_ptr()), OT, synth.ROPE_HEADS, synth.ROPE_HEAD_DIM,
@@ -470,7 +470,7 @@ def main():
     calls.append(("gemm_mx_wo_m8192", L.fp8_batched_gemm_a8w8_mxscale,
                   (vp(rq.data_ptr()), vp(rWq.data_ptr()), vp(rs.data_ptr()), vp(rWs.data_ptr()),
                    vp(rY.data_ptr()), OG, OT, ON, OKG, *gwsa, sptr)))
-    calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, sptr)))
+    calls.append(("requant_moe", L.fp8_requantize_weights, (mdescs, 2, fp8.SCALE_F32, None, 0, sptr)))
     # the expert chain: 1x128 quant of the routed rows, gate_up GEMM, SwiGLU +
     # 1x128 quant of its output, down GEMM
     mg, md = moe["gate_up"], moe["down"]

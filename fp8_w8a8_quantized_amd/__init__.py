@@ -94,7 +94,8 @@ def load_library() -> ctypes.CDLL:
                                           vp], i32),
         "fp8_silu_f32_of_bf16": ([ctypes.c_uint32, i64, vp, vp], i32),
         "fp8_mfma_rate_probe": ([i64, vp, vp], i32),
-        "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp], i32),
+        "fp8_requantize_workspace_size": ([i32], sz),
+        "fp8_requantize_weights": ([ctypes.POINTER(_WeightDesc), i32, i32, vp, sz, vp], i32),
         "fp8_gemm_a8w8_scaled": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp], i32),
         "fp8_gemm_workspace_size": ([i64, i64, i64, i32], sz),
         "fp8_gemm_a8w8_scaled_noalloc": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp], i32),
@@ -356,8 +357,10 @@ def requantize_weights(weights: Sequence[torch.Tensor], scale_fmt: int = SCALE_F
         results.append((q, s))
     _on_gpu(weights[0], "weights[0]")
     L = load_library()
+    if L.fp8_requantize_workspace_size(len(weights)) != 0:
+        raise RuntimeError("fp8_requantize_weights: the library asks for a workspace")
     _check("fp8_requantize_weights",
-           L.fp8_requantize_weights(descs, len(weights), scale_fmt, _stream(weights[0])))
+           L.fp8_requantize_weights(descs, len(weights), scale_fmt, None, 0, _stream(weights[0])))
     return results
 
 

@@ -189,8 +189,16 @@ int fp8_add_rmsnorm_quant(void* q, const void* x, void* residual, float* s, cons
                                                as_stream(stream)));
 }
 
-int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream) {
+size_t fp8_requantize_workspace_size(int n) {
+    (void)n;
+    return 0;
+}
+
+int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     if (n < 0 || (scale_fmt != FP8_SCALE_F32 && scale_fmt != FP8_SCALE_E8M0)) return FP8_ERR_ARG;
+    if (int st = workspace_check(workspace, workspace_bytes, (int64_t)fp8_requantize_workspace_size(n)))
+        return st;
     if (n == 0) return FP8_OK;
     if (!descs) return FP8_ERR_ARG;
     int work = 0;

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FP8W8A8_ABI_VERSION 2
+#define FP8W8A8_ABI_VERSION 3
 
 typedef enum {
     FP8_OK = 0,
@@ -257,14 +257,28 @@ typedef struct {
 int fp8_quantize_tensors(const fp8_tensor_desc* descs, int n, void* stream);
 
 /*
+ * Workspace of fp8_requantize_weights for n descriptors: 0.  The descriptors
+ * travel in the kernels' arguments (64 per launch), so no device copy of the
+ * table is made; the size query and the workspace arguments keep the call's
+ * shape stable should a layout ever need one.  n < 0 also gives 0.
+ */
+size_t fp8_requantize_workspace_size(int n);
+
+/*
  * Per-RL-step policy weight re-quantization ("FP8-RL" abstract: weights change
  * every step and are re-quantized before each sync into the engine): every
  * descriptor's weight is quantized in 128x128 blocks, with fp32 scales or E8M0
  * bytes (DeepSeek V4 page §1/§2).  `descs` is a host array of n entries, read
  * during the call only.  The library enqueues one kernel per 64 descriptors.
- *   N % 128 or K % 128 != 0 -> FP8_ERR_SHAPE; n < 0 -> FP8_ERR_ARG.
+ * `workspace` (device memory, caller-owned, 16-byte aligned) holds at least
+ * fp8_requantize_workspace_size(n) bytes; with a size of 0 it may be NULL
+ * (workspace_bytes then 0).
+ *   N % 128 or K % 128 != 0 -> FP8_ERR_SHAPE; n < 0 -> FP8_ERR_ARG;
+ *   workspace NULL with workspace_bytes > 0, or too small -> FP8_ERR_ARG;
+ *   workspace misaligned -> FP8_ERR_ALIGN.
  */
-int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* stream);
+int fp8_requantize_weights(const fp8_weight_desc* descs, int n, int scale_fmt, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Workspace of fp8_gemm_a8w8_scaled: the bytes of device memory its split-tile

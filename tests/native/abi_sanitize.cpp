@@ -73,10 +73,12 @@ int main() {
 
     // requantization: a descriptor table of several entries, one bad
     std::vector<fp8_weight_desc> d(70, fp8_weight_desc{f, f, f, 256, 256});
-    EXPECT(fp8_requantize_weights(d.data(), 70, FP8_SCALE_F32, nullptr), DEVICE);
+    EXPECT(fp8_requantize_workspace_size(70), 0u);
+    EXPECT(fp8_requantize_weights(d.data(), 70, FP8_SCALE_F32, nullptr, 0, nullptr), DEVICE);
+    EXPECT(fp8_requantize_weights(d.data(), 70, FP8_SCALE_F32, nullptr, 64, nullptr), ARG);
     d[69].N = 200;
-    EXPECT(fp8_requantize_weights(d.data(), 70, FP8_SCALE_F32, nullptr), SHAPE);
-    EXPECT(fp8_requantize_weights(d.data(), 70, 5, nullptr), ARG);
+    EXPECT(fp8_requantize_weights(d.data(), 70, FP8_SCALE_F32, nullptr, 0, nullptr), SHAPE);
+    EXPECT(fp8_requantize_weights(d.data(), 70, 5, nullptr, 0, nullptr), ARG);
     std::vector<fp8_tensor_desc> t(3, fp8_tensor_desc{f, f, ff, 64});
     t[1].n = 12;
     EXPECT(fp8_quantize_tensors(t.data(), 3, nullptr), SHAPE);

@@ -64,7 +64,7 @@ def test_library_built_from_these_sources(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8_abi_version() == 2
+    assert L.fp8_abi_version() == 3
     for st in (OK, ARG, SHAPE, ALIGN, DEVICE, LAUNCH):
         assert fp8.status_string(st) and fp8.status_string(st) != "unknown status"
     assert fp8.status_string(123) == "unknown status"
@@ -258,15 +258,21 @@ def test_requant_validation(L):
     bad_shape = D(FAKE, FAKE, FAKE, 200, 256)
     bad_align = D(FAKE + 4, FAKE, FAKE, 256, 256)
     arr = (D * 2)(good, bad_shape)
-    assert L.fp8_requantize_weights(arr, 2, 0, None) == SHAPE
+    assert L.fp8_requantize_weights(arr, 2, 0, None, 0, None) == SHAPE
     arr = (D * 2)(good, bad_align)
-    assert L.fp8_requantize_weights(arr, 2, 1, None) == ALIGN
-    assert L.fp8_requantize_weights(arr, 2, 5, None) == ARG
-    assert L.fp8_requantize_weights(None, 0, 0, None) == OK
-    assert L.fp8_requantize_weights(None, -1, 0, None) == ARG
+    assert L.fp8_requantize_weights(arr, 2, 1, None, 0, None) == ALIGN
+    assert L.fp8_requantize_weights(arr, 2, 5, None, 0, None) == ARG
+    assert L.fp8_requantize_weights(None, 0, 0, None, 0, None) == OK
+    assert L.fp8_requantize_weights(None, -1, 0, None, 0, None) == ARG
+    # workspace: none needed; a NULL one with a size, or a misaligned one, is refused
+    for n in (-1, 0, 1, 64, 65, 10000):
+        assert L.fp8_requantize_workspace_size(n) == 0
+    arr = (D * 1)(good)
+    assert L.fp8_requantize_weights(arr, 1, 0, None, 16, None) == ARG
+    assert L.fp8_requantize_weights(arr, 1, 0, FAKE + 4, 16, None) == ALIGN
     if not _gpu():
-        arr = (D * 1)(good)
-        assert L.fp8_requantize_weights(arr, 1, 0, None) == DEVICE
+        assert L.fp8_requantize_weights(arr, 1, 0, None, 0, None) == DEVICE
+        assert L.fp8_requantize_weights(arr, 1, 0, FAKE, 256, None) == DEVICE
 
 
 def test_tensor_quant_validation(L):
