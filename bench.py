@@ -33,7 +33,9 @@ there.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the work.
 the reference kernel whose counter reading scales FETCH_SIZE / WRITE_SIZE.
 ``--one-gemm M N K`` instead runs one block-scaled GEMM shape (seeded dense
 inputs, quantized by the library) ``--reps`` times over ``--copies`` distinct
-operand sets, for counter runs.
+operand sets, for counter runs.  ``--vendor-compare`` times the four M = 8192
+shapes on this library's row- and block-scaled GEMMs and on torch._scaled_mm
+(row-wise and per-tensor FP8 scales) on the same box.
 """
 from __future__ import annotations
 
@@ -137,6 +139,79 @@ def one_gemm(M: int, N: int, K: int, reps: int, copies: int = 1):
                       "tflops": round(2.0 * M * N * K / us / 1e6, 1)}))
 
 
+def vendor_compare(reps: int):
+    """The M=8192 dense shapes on this library's row- and block-scaled GEMMs
+    and on torch._scaled_mm (the vendor library; row-wise and per-tensor FP8
+    scales), same box, same codes for the row-wise pair (one JSON line per
+    shape and GEMM).  Two operand sets alternate, as layers would."""
+    import torch
+
+    import fp8_w8a8_quantized_amd as fp8
+    import synth
+
+    dev = torch.device("cuda:0")
+
+    def timed(fn, n):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for name, (N, K) in synth.DENSE_SHAPES.items():
+        M = 8192
+        row, blk = [], []
+        for c in range(2):
+            X = synth.act_col_outliers(M, K, seed=1 + 2 * c, device=dev)
+            W = synth.weight(N, K, seed=2 + 2 * c, device=dev)
+            row.append((fp8.quantize_token(X), fp8.quantize_token(W)))
+            blk.append((fp8.quantize_block(X), fp8.requantize_weights([W], fp8.SCALE_F32)[0]))
+            del X, W
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((16,), dtype=torch.uint8, device=dev)
+        one = torch.ones((), dtype=torch.float32, device=dev)
+
+        def vend(i, per_tensor=False):
+            (qa, sa), (qw, sw) = row[i % 2]
+            a8 = qa.view(torch.float8_e4m3fn)
+            w8 = qw.view(torch.float8_e4m3fn)
+            if per_tensor:
+                return torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one,
+                                        out_dtype=torch.bfloat16)
+            return torch._scaled_mm(a8, w8.t(), scale_a=sa.view(M, 1), scale_b=sw.view(1, N),
+                                    out_dtype=torch.bfloat16)
+
+        calls = {
+            "library_row": lambda i: fp8.gemm_a8w8_scaled(*row[i % 2], fp8.GRAN_ROW, out=y,
+                                                          workspace=ws),
+            "library_block": lambda i: fp8.gemm_a8w8_scaled(*blk[i % 2], fp8.GRAN_BLOCK, out=y,
+                                                            workspace=ws),
+            "vendor_row": lambda i: vend(i),
+            "vendor_tensor": lambda i: vend(i, True),
+        }
+        # two rounds over the four, keeping each one's faster round
+        res = {}
+        for _ in range(2):
+            for kind, fn in calls.items():
+                us = timed(fn, reps)
+                res[kind] = min(us, res.get(kind, us))
+        # the row-wise pair computes the same products: their outputs agree to bf16 rounding
+        fp8.gemm_a8w8_scaled(*row[0], fp8.GRAN_ROW, out=y, workspace=ws)
+        ref = vend(0).float()
+        rel = float(((y.float() - ref).abs().amax(dim=1) /
+                     ref.abs().amax(dim=1).clamp_min(1e-30)).max())
+        for kind, us in res.items():
+            print(json.dumps({"shape": name, "M": M, "N": N, "K": K, "gemm": kind,
+                              "avg_us": round(us, 2),
+                              "tflops": round(2.0 * M * N * K / us / 1e6, 1),
+                              "row_pair_max_rel_diff": round(rel, 6)}), flush=True)
+
+
 def environment(torch, dev) -> dict:
     """What the numbers were measured on: versions, device, clocks, host CPU."""
     props = torch.cuda.get_device_properties(dev)
@@ -231,6 +306,7 @@ def parse():
     ap.add_argument("--one-gemm", type=int, nargs=3, metavar=("M", "N", "K"))
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--copies", type=int, default=1)
+    ap.add_argument("--vendor-compare", action="store_true")
     return ap.parse_args()
 
 
@@ -286,6 +362,9 @@ def main():
         return
     if args.one_gemm:
         one_gemm(*args.one_gemm, args.reps, args.copies)
+        return
+    if args.vendor_compare:
+        vendor_compare(args.reps if args.reps > 3 else 10)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
