@@ -290,6 +290,21 @@ def test_swiglu_quant_shapes(T, I):
     _eq_swiglu(gu)
 
 
+def test_swiglu_quant_every_gate_pattern():
+    """Every finite bf16 gate (65280 patterns, in pattern order: some waves'
+    gates all lie in the silu table's domain and take the select-free path,
+    others hold tiny, large or negative-tail gates), with up values small
+    enough that no product overflows; codes and scales bit-exact."""
+    say("swiglu_quant over every finite bf16 gate")
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    g = bits[(bits & 0x7F80) != 0x7F80].astype(np.uint16)
+    T, I = 85, 768
+    assert g.size == T * I
+    gate = torch.from_numpy(g.view(np.int16).reshape(T, I).copy()).view(torch.bfloat16)
+    up = (synth.normal_bf16((T, I), seed=5).float() * 1e-3).to(torch.bfloat16)
+    _eq_swiglu(torch.cat([gate, up], dim=1))
+
+
 def test_swiglu_quant_extremes():
     """Gates far in both tails (silu = g, silu = -0), zero groups and
     outlier up values in one tensor."""
