@@ -853,12 +853,14 @@ __global__ __launch_bounds__(64 * kSwigluWaves) void k_swiglu_quant(const uint4*
 // wave step); each group looks up its source row first.  An index outside
 // [0, n_src) yields a zero row (codes 0, scale 0) and reads nothing.
 // ---------------------------------------------------------------------------
-template <int U>
+// IDX: the index type of groups (32-bit when every group index fits, which
+// lets the row of a group come from a multiply and shift).
+template <int U, typename IDX>
 __global__ __launch_bounds__(256) void k_quant_gather(const uint4* __restrict__ x,
                                                       const int32_t* __restrict__ row_token,
                                                       uint2* __restrict__ q,
                                                       float* __restrict__ s, int64_t G,
-                                                      int64_t GK, int64_t n_src) {
+                                                      int64_t GK, int64_t n_src, FastDiv fgk) {
     const int lane = threadIdx.x & 63, li = lane & 15;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t chunk0 = wave * U;
@@ -868,7 +870,10 @@ __global__ __launch_bounds__(256) void k_quant_gather(const uint4* __restrict__ 
         const int64_t gid = (chunk0 + u) * 4 + (lane >> 4);
         v[u] = uint4{0u, 0u, 0u, 0u};
         if (gid < G) {
-            const int64_t t = gid / GK, j = gid - t * GK;
+            int64_t t;
+            if constexpr (sizeof(IDX) == 4) t = fdiv((uint32_t)gid, fgk);
+            else t = gid / GK;
+            const int64_t j = gid - t * GK;
             const int64_t src = row_token[t];
             if (src >= 0 && src < n_src) v[u] = x[src * GK * 16 + j * 16 + li];
         }
@@ -905,12 +910,21 @@ template <int U, typename IDX, bool VEC>
 __global__ __launch_bounds__(256) void k_inv_rope_quant(
     const uint4* __restrict__ o, const int64_t* __restrict__ pos, const float* __restrict__ cosc,
     const float* __restrict__ sinc, uint2* __restrict__ q, uint8_t* __restrict__ s, int64_t G64,
-    int64_t GK64, int D, int R, int64_t P) {
+    int64_t GK64, int D, int R, int64_t P, FastDiv fgk, FastDiv fd) {
     const int lane = threadIdx.x & 63, li = lane & 15;
     const IDX G = (IDX)G64, GK = (IDX)GK64;
     const IDX wave = (IDX)blockIdx.x * 4 + (IDX)(threadIdx.x >> 6);
     const IDX chunk0 = wave * U;
     const int half = R >> 1, rope0 = D - R;
+    // 32-bit indices divide by multiply and shift (every dividend < 2^31)
+    auto div_gk = [&](IDX n) -> IDX {
+        if constexpr (sizeof(IDX) == 4) return (IDX)fdiv((uint32_t)n, fgk);
+        else return n / GK;
+    };
+    auto mod_d = [&](int e) -> int {
+        if constexpr (sizeof(IDX) == 4) return e - (int)fdiv((uint32_t)e, fd) * D;
+        else return e - (e / D) * D;
+    };
     uint4 v[U];
     int64_t p[U];
 #pragma unroll
@@ -919,7 +933,7 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
         v[u] = uint4{0u, 0u, 0u, 0u};
         p[u] = -1;
         if (gid < G) {  // both loads in bounds; an invalid position zeroes the row after
-            p[u] = pos[gid / GK];
+            p[u] = pos[div_gk(gid)];
             v[u] = load_nt16(o + (int64_t)gid * 16 + li);
         }
     }
@@ -933,9 +947,9 @@ __global__ __launch_bounds__(256) void k_inv_rope_quant(
         float f[8];
         unpack8(v[u], f);
         if (p[u] >= 0) {
-            const IDX j = gid - (gid / GK) * GK;
+            const IDX j = gid - div_gk(gid) * GK;
             const int e0 = (int)(j * 128) + li * 8;    // element offset in the row
-            const int d0 = e0 - (e0 / D) * D;          // its dim within the head
+            const int d0 = mod_d(e0);                  // its dim within the head
             const float* cr = cosc + p[u] * half;
             const float* sr = sinc + p[u] * half;
             float x[8];
@@ -1109,8 +1123,12 @@ hipError_t launch_quant_gather(const void* x, int64_t n_src, int64_t K, const in
     constexpr int U = 4;
     const int64_t GK = K / 128, G = T * GK;
     const int64_t waves = (G + 4 * U - 1) / (4 * U);
-    return launch(k_quant_gather<U>, (waves + 3) / 4, st, static_cast<const uint4*>(x), row_token,
-                  static_cast<uint2*>(q), s, G, GK, n_src);
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks * 16 * U < (int64_t(1) << 31))  // every group index fits in 31 bits
+        return launch(k_quant_gather<U, int32_t>, blocks, st, static_cast<const uint4*>(x),
+                      row_token, static_cast<uint2*>(q), s, G, GK, n_src, fast_div(GK));
+    return launch(k_quant_gather<U, int64_t>, blocks, st, static_cast<const uint4*>(x), row_token,
+                  static_cast<uint2*>(q), s, G, GK, n_src, FastDiv{1u, 0});
 }
 
 hipError_t launch_inv_rope_quant(const void* o, const int64_t* pos, const float* cosc,
@@ -1126,9 +1144,10 @@ hipError_t launch_inv_rope_quant(const void* o, const int64_t* pos, const float*
                      reinterpret_cast<uintptr_t>(sinc) % 16 == 0;
     const auto* ov = static_cast<const uint4*>(o);
     auto* qv = static_cast<uint2*>(q);
+    const FastDiv fgk = fast_div(GK), fd = fast_div(D);
 #define FP8_ROPE(IDX, VEC) \
     launch(k_inv_rope_quant<U, IDX, VEC>, blocks, st, ov, pos, cosc, sinc, qv, s, G, GK, (int)D, \
-           (int)R, P)
+           (int)R, P, fgk, fd)
     if (small) return vec ? FP8_ROPE(int32_t, true) : FP8_ROPE(int32_t, false);
     return vec ? FP8_ROPE(int64_t, true) : FP8_ROPE(int64_t, false);
 #undef FP8_ROPE

@@ -323,6 +323,17 @@ def test_quotient_path_equals_ieee_division_exhaustively(tmp_path):
     assert "mismatches 0" in r.stdout
 
 
+def test_fast_division_equals_integer_division(tmp_path):
+    """The kernels' multiply-and-shift division of 31-bit group indices
+    (fastdiv.hpp, host build of the same header) equals integer division."""
+    src = os.path.join(ROOT, "tests", "native", "fastdiv_check.cpp")
+    exe = str(tmp_path / "fastdiv_check")
+    subprocess.run(["g++", "-O2", "-std=c++17", src, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert " 0 wrong" in r.stdout
+
+
 # ---------------------------------------------- Python binding validation --
 # Buffers passed by raw pointer are checked (dtype, exact shape, contiguity,
 # device) before any call: a wrong buffer raises TypeError / ValueError on the
