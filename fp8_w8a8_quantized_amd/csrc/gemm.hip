@@ -770,10 +770,13 @@ __device__ __forceinline__ void pp_store(v4f (&acc)[4][8], __amdgpu_buffer_rsrc_
 }
 
 // Store tile k's block of this wave.
+// Y is [M, B, N]: batch b's rows are B N apart.
 __device__ __forceinline__ void pp_store_tile(v4f (&acc)[4][8], const BigTile& t, uint16_t* Y,
-                                              int N, int wn, int wm, int lr, int lk) {
-    const __amdgpu_buffer_rsrc_t Yr = buffer_rsrc(Y + t.row0 * N, t.rows * N * 2);
-    pp_store(acc, Yr, N, t.tn * BN2 + wn * 128, wm, lr, lk);
+                                              int N, int B, int wn, int wm, int lr, int lk) {
+    const int ldy = B * N;
+    const __amdgpu_buffer_rsrc_t Yr =
+        buffer_rsrc(Y + (t.row0 * B + t.b) * N, ((t.rows - 1) * ldy + N) * 2);
+    pp_store(acc, Yr, ldy, t.tn * BN2 + wn * 128, wm, lr, lk);
 }
 
 // Everything a ping-pong wave needs besides its registers.
@@ -785,10 +788,12 @@ struct PPCtx {
     uint16_t* Y;
     BigGeom G;
     int tm_count, tn_count, first, nwg, NS, KB, K;
+    int lda;          // bytes between consecutive rows of one batch of A (B K)
     bool grouped;     // MoE: tiles over the expert tables in grp
     BigGroups grp;
     int wave, wm, wn, lr, lk;
-    int off0;  // lane's byte offset of its first A / W chunk of a block
+    int off0;  // group 0: lane's byte offset of its first W chunk of a block
+    int offA;  // group 1: the same for its first A chunk (rows lda apart)
     int offa;  // group 1: lane's byte offset of its sA scale at kb = 0
     int offw;  // group 1: lane's byte offset of its sW scale at kb = 0
 };
@@ -802,7 +807,8 @@ __device__ __forceinline__ BigTile pp_tile(const PPCtx& c, int k) {
     if (!c.grouped) t.row0 = (int64_t)t.tm * BM2;
     t.tn = __builtin_amdgcn_readfirstlane(t.tn);
     t.rows = __builtin_amdgcn_readfirstlane(t.rows);
-    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.e = __builtin_amdgcn_readfirstlane(c.grouped ? t.e : t.b);  // the weight batch
+    t.b = __builtin_amdgcn_readfirstlane(t.b);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)t.row0);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)t.row0 >> 32));
     t.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
@@ -827,8 +833,11 @@ __device__ __forceinline__ PPSrc pp_src(const PPCtx& c, int tile) {
         S.r0 = buffer_rsrc(c.W + n0 * K, BN2 * K);
         S.r1 = S.r2 = S.r0;
     } else {
-        S.r0 = buffer_rsrc(c.A + row0 * K, t.rows * K);
-        S.r1 = buffer_rsrc(c.sA + row0 * KB * SB, t.rows * KB * SB);
+        // batch b of A is every B-th K-row ([M, B, K]); its scales [M, B, KB]
+        const int B = c.G.B;
+        const int64_t arow = row0 * B + t.b;
+        S.r0 = buffer_rsrc(c.A + arow * K, (t.rows - 1) * c.lda + K);
+        S.r1 = buffer_rsrc(c.sA + arow * KB * SB, ((t.rows - 1) * B * KB + KB) * SB);
         S.r2 = buffer_rsrc(c.sW + (n0 / BK) * KB * SB, 2 * KB * SB);
     }
     return S;
@@ -872,7 +881,7 @@ __device__ __forceinline__ void pp_load1(uint8_t* lds, const PPCtx& c, const PPC
     const int q = c.wave & 3, st = L.b & 1;
     uint8_t* la = lds + st * kStage2;
     if (n < 8)
-        b2l(L.S.r0, la + (n * 4 + q) * 64 * 16, 16, o + n * 32 * c.K, L.kb * BK);
+        b2l(L.S.r0, la + (n * 4 + q) * 64 * 16, 16, o + n * 32 * c.lda, L.kb * BK);
     else if (n == 8)
         b2l(L.S.r1, lds + 2 * kStage2 + st * BM2 * 4 + q * 256, SB, c.offa, L.kb * SB);
     else
@@ -981,7 +990,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
         if (stored) {  // the previous tile is complete: store it
             const BigTile t = pp_tile(c, ct - 1);
             if constexpr (GRAN == GRAN_ROW) pp_row_scale(acc, c, t, wn, wm, lr, lk);
-            pp_store_tile(acc, t, c.Y, (int)c.G.N, wn, wm, lr, lk);
+            pp_store_tile(acc, t, c.Y, (int)c.G.N, c.G.B, wn, wm, lr, lk);
         }
         pp_read<GRAN>(lds, c, s, x, w, ps);
         __builtin_amdgcn_s_waitcnt(kLgkm0);  // fragments and scales in registers
@@ -1001,7 +1010,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
         } else {
             cur.next(c);  // block s + 2
         }
-        int o = c.off0;
+        int o = GRP == 0 ? c.off0 : c.offA;
         asm volatile("" : "+v"(o));  // recomputed per phase, not held across the loop
         __builtin_amdgcn_sched_barrier(0);
         v4f pr[3];
@@ -1061,7 +1070,7 @@ __device__ __forceinline__ void pp_loop(uint8_t* lds, const PPCtx& c,
     promote(acc[3][7], carry, carry_sc);
     const BigTile t = pp_tile(c, ct - 1);
     if constexpr (GRAN == GRAN_ROW) pp_row_scale(acc, c, t, wn, wm, lr, lk);
-    pp_store_tile(acc, t, c.Y, (int)c.G.N, wn, wm, lr, lk);
+    pp_store_tile(acc, t, c.Y, (int)c.G.N, c.G.B, wn, wm, lr, lk);
 }
 
 // GRAN_BLOCK (fp32 scales, promotion FMAs), GRAN_MX (E8M0 scales applied by
@@ -1090,7 +1099,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
     c.tn_count = (int)(G.N / BN2);
     c.grouped = GROUPED;
     c.grp = BigGroups{};
-    int T = c.tm_count * c.tn_count;
+    int T = c.tm_count * c.tn_count * G.B;  // batch-major (B = 1 but for the batched MX GEMM)
     if constexpr (GROUPED) {
         big_groups(lds + kLds2, offsets, E, G.M, c.tn_count);
         __syncthreads();
@@ -1116,8 +1125,10 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
     c.wn = grp;
     c.lr = lane & 15;
     c.lk = lane >> 4;
+    c.lda = G.B * c.K;
     c.off0 = (wq * 8 + (lane >> 3)) * c.K + swz_pos(lane >> 3, lane & 7) * 16;
-    c.offa = (wq * 64 + lane) * c.KB * SB;
+    c.offA = (wq * 8 + (lane >> 3)) * c.lda + swz_pos(lane >> 3, lane & 7) * 16;
+    c.offa = (wq * 64 + lane) * G.B * c.KB * SB;
     c.offw = (lane & 1) * c.KB * SB;
     asm volatile("" ::"s"(Y));
     // prologue: all of block 0 and, of block 1, everything but W half 1
@@ -1138,7 +1149,7 @@ __global__ __launch_bounds__(kThreads2) void k_gemm_pp(const uint8_t* __restrict
     } else {
         PPCur<1, SB> cur;
         cur.start(c, 0);
-        const int o = c.off0;
+        const int o = c.offA;
 #pragma unroll
         for (int n = 0; n < NL1; ++n) pp_load1(lds, c, cur, o, n);  // block 0
         cur.next(c);
@@ -2575,9 +2586,9 @@ hipError_t launch_batched_gemm_mx(const void* a, const void* w, const uint8_t* a
     const int64_t tiles = B * ((M + BM2 - 1) / BM2) * ((N + BN2 - 1) / BN2);
     const unsigned grid = (unsigned)(tiles < 256 ? tiles : 256);  // one per CU
     const BigGeom G{M, N, K, (int)B};
-    // dense, full 256-column tiles: the ping-pong kernel (32-bit offsets into
-    // 256 output rows x N bf16)
-    if (B == 1 && N % BN2 == 0 && N < (int64_t(1) << 22)) {
+    // full 256-column tiles: the ping-pong kernel (32-bit offsets into 256
+    // output rows of B N bf16, batch-major tiles)
+    if (N % BN2 == 0 && B * N < (int64_t(1) << 22)) {
         hipLaunchKernelGGL(k_gemm_pp<GRAN_MX>, dim3(grid), dim3(kThreads2), 0, st,
                            static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(w),
                            static_cast<const void*>(a_s), static_cast<const void*>(w_s),
