@@ -640,6 +640,52 @@ def test_inverse_rope_quant_into_batched_mx_gemm():
     assert_rows_close(got, ref.reshape(rows.size * G, N), what="rope -> mx gemm")
 
 
+def test_mx_batched_ragged_rows_full_tiles():
+    """Batched MX GEMM on the ping-pong kernel (N a multiple of 256): 300
+    tokens leave a 44-row last tile in every group, K = 640 is 5 K steps.
+    Every output row of every group against the oracle."""
+    M, B, N, K = 300, 3, 512, 640
+    say(f"batched MX GEMM M={M} B={B} N={N} K={K}, ragged row tiles")
+    X = synth.act_col_outliers(M * B, K, seed=93)
+    W = synth.normal_bf16((B * N, K), seed=94, std=0.02)
+    qa, sa = fp8.quantize_block_e8m0(X.to(dev()))
+    (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_E8M0)
+    y = fp8.batched_gemm_a8w8_mxscale((qa.view(M, B, K), sa.view(M, B, K // 128)),
+                                      (qw.view(B, N, K), sw.view(B, N // 128, K // 128)))
+    oqa, osa = oracle.quantize_block_e8m0(X)
+    oqw, osw = oracle.quantize_weight_block(W, 1)
+    ref = oracle.batched_mx_gemm(oqa.reshape(M, B, K), oqw.reshape(B, N, K),
+                                 osa.reshape(M, B, K // 128), osw.reshape(B, N // 128, K // 128))
+    assert_rows_close(y.view(M * B, N), ref.reshape(M * B, N), what="batched mx ragged")
+
+
+def test_output_projection_full_size():
+    """The output projection at the workload size: inverse RoPE + E8M0 group
+    quant of o [8192, 64, 128] as 8 groups of 1024, per-group weights
+    [8, 1024, 1024] re-quantized with E8M0 scales, the batched MX GEMM.
+    Every output row of every group against the oracle's fp64 product of its
+    own codes (the quantizer is bit-exact in its own full-size test)."""
+    T, G, N = synth.ROPE_TOKENS, synth.ROPE_GROUPS, synth.ROPE_OUT
+    K = synth.ROPE_HEADS * synth.ROPE_HEAD_DIM // G
+    say(f"output projection T={T} groups={G} N={N} K={K}, every row")
+    o, pos = synth.rope_inputs(T, seed=46)
+    cos, sin = synth.rope_cache()
+    W = synth.normal_bf16((G * N, K), seed=47, std=0.02)
+    qa, sa = fp8.inverse_rope_group_quant(o.to(dev()), torch.as_tensor(pos, device=dev()),
+                                          torch.as_tensor(cos, device=dev()),
+                                          torch.as_tensor(sin, device=dev()), G)
+    (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_E8M0)
+    y = fp8.batched_gemm_a8w8_mxscale((qa, sa), (qw.view(G, N, K), sw.view(G, N // 128, -1)))
+    oq, os_, _ = oracle.inverse_rope_group_quant(o, pos, cos, sin, synth.ROPE_DIM)
+    oq, os_ = oq.reshape(T, G, K), os_.reshape(T, G, K // 128)
+    oqw, osw = oracle.quantize_weight_block(W, 1)
+    oqw, osw = oqw.reshape(G, N, K), osw.reshape(G, N // 128, K // 128)
+    for g in range(G):
+        assert_gemm_all_rows(y[:, g, :], oq[:, g, :], oracle.e8m0_value(os_[:, g, :]), oqw[g],
+                             oracle.e8m0_value(osw[g]), oracle.GRAN_BLOCK,
+                             what=f"output projection group {g}")
+
+
 @pytest.mark.parametrize("M,N,K", [(200, 8960, 640), (3, 1024, 12288), (256, 4096, 4096)])
 def test_mx_small_m_stream_k(M, N, K):
     # dense small M takes the stream-K kernels with E8M0 scales: tiles split
