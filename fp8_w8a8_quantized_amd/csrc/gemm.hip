@@ -1315,6 +1315,16 @@ struct TileSpace {
     int64_t tm_count;        // dense only
 };
 
+// Every kernel argument the small-M kernels read, wanted in SGPRs at once:
+// the compiler then issues all the argument loads together and waits for
+// them once, instead of one round trip per group of first uses spread over
+// the index arithmetic (three to four at these kernels' starts).
+template <class T0, class T1, class T2>
+__device__ __forceinline__ void args_ready(const TileSpace& S, T0 a, T1 b, T2 c) {
+    asm volatile("" ::"s"(S.A), "s"(S.W), "s"(S.sA), "s"(S.sW), "s"(S.Y), "s"(S.M), "s"(S.N),
+                 "s"(S.K), "s"(S.tm_count), "s"(a), "s"(b), "s"(c));
+}
+
 template <int GRAN, bool GROUPED>
 __device__ __forceinline__ Tile tile_at(const TileSpace& S, int64_t logical) {
     const int64_t KB = S.K / BK, NT = S.N / BNP;
@@ -1633,6 +1643,7 @@ __device__ __forceinline__ int64_t sk_owner(int64_t u, int64_t Wt, int64_t G) {
 
 template <int GRAN, bool BUF>
 __global__ __launch_bounds__(kThreadsP) void k_gemm_sk(TileSpace S, int64_t tiles, SkWork ws) {
+    args_ready(S, tiles, ws.part, gridDim.x);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1732,6 +1743,7 @@ constexpr int kSkRedSplit = 4;
 template <int GRAN>
 __global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t tiles, int64_t G,
                                                         const v4f* __restrict__ part) {
+    args_ready(S, tiles, G, part);
     const int64_t t = blockIdx.x / kSkRedSplit, KB = S.K / BK, Wt = tiles * KB;
     const int i = (int)(blockIdx.x % kSkRedSplit);
     const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
@@ -1783,6 +1795,7 @@ __global__ __launch_bounds__(kThreadsP) void k_sk_reduce(TileSpace S, int64_t ti
 template <int GRAN, int SPLIT>
 __global__ __launch_bounds__(kThreadsP) void k_sk_reduce_wide(TileSpace S, int64_t tiles, int64_t G,
                                                         const v4f* __restrict__ part) {
+    args_ready(S, tiles, G, part);
     constexpr int NF = 8 / SPLIT;
     const int64_t t = blockIdx.x / SPLIT, KB = S.K / BK, Wt = tiles * KB;
     const int f0 = (int)(blockIdx.x % SPLIT) * NF;
@@ -2104,6 +2117,7 @@ __device__ __forceinline__ void dk_store_frag(const Tile& ct, const v4f (&v4)[4]
 
 template <int GRAN, bool SG>
 __global__ __launch_bounds__(kThreadsP) void k_gemm_dk(TileSpace S, int64_t tiles, SkWork ws) {
+    args_ready(S, tiles, ws.part, gridDim.x);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsD];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2210,6 +2224,7 @@ __global__ __launch_bounds__(kThreadsP) void k_gemm_dk(TileSpace S, int64_t tile
 template <int GRAN>
 __global__ __launch_bounds__(kThreadsP) void k_dk_reduce(TileSpace S, int64_t tiles, int64_t G,
                                                         const v4f* __restrict__ part) {
+    args_ready(S, tiles, G, part);
     const int64_t t = blockIdx.x >> 2, KB = S.K / BK, Wt = tiles * KB;
     const int i = (int)(blockIdx.x & 3);
     const int64_t c_lo = sk_owner(t * KB, Wt, G), c_hi = sk_owner(t * KB + KB - 1, Wt, G);
@@ -2242,6 +2257,7 @@ __global__ __launch_bounds__(kThreadsP) void k_dk_reduce(TileSpace S, int64_t ti
 template <int GRAN, int SPLIT>
 __global__ __launch_bounds__(kThreadsP) void k_dk_reduce_wide(TileSpace S, int64_t tiles, int64_t G,
                                                         const v4f* __restrict__ part) {
+    args_ready(S, tiles, G, part);
     constexpr int NF = 16 / SPLIT;
     const int64_t t = blockIdx.x / SPLIT, KB = S.K / BK, Wt = tiles * KB;
     const int f0 = (int)(blockIdx.x % SPLIT) * NF;
