@@ -6,8 +6,9 @@ the same bf16 inputs itself and multiplies in fp64.  Shapes: small ones that
 span several 128 x 128 tiles with ragged M, the tiny linear, every dense
 linear at M = 256 and M = 8192, the per-row workload (RMSNorm + per-token
 activations x per-row weights), the MX-scaled linears at M = 8192, and the MoE
-grouped GEMMs at full size plus small ragged cases with empty experts.  Every
-test compares every output row (full-size outputs in chunks of rows).
+grouped GEMMs at full size plus small ragged cases with empty experts, seeded
+sweeps of shapes and routings, and a chain of launches captured in a HIP graph.
+Every test compares every output row (full-size outputs in chunks of rows).
 """
 import numpy as np
 import pytest
@@ -717,3 +718,131 @@ def test_mx_dense_full_size(name):
     say(f"MX GEMM {name} M={M} ({M}x{N}x{K}), every row")
     X, W = synth.dense_linear(name, M, seed=13)
     _mx_check(X, W, f"mx {name}")
+
+
+def _sweep_shapes(seed: int, n: int):
+    """Seeded (M, N, K) triples: M over 1..1400 with the tile edges 127, 128,
+    129, 255, 256, 257, 1023, 1024, 1025 mixed in; N and K multiples of 128
+    up to 3072 (N with an odd count of 128-column halves as often as not)."""
+    rng = np.random.default_rng(seed)
+    edges = [1, 127, 128, 129, 255, 256, 257, 1023, 1024, 1025]
+    out = []
+    for i in range(n):
+        M = int(edges[i]) if i < len(edges) else int(rng.integers(1, 1401))
+        N = 128 * int(rng.integers(1, 25))
+        K = 128 * int(rng.integers(1, 25))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("gran", ["block", "row", "mx"])
+def test_random_shape_sweep(gran):
+    """24 seeded shapes per scale form, the kernel choice left to the
+    launcher (stream-K, 256-row tiles, whole tiles, the ping-pong kernel,
+    128-column tails): every output row of each against the oracle."""
+    for i, (M, N, K) in enumerate(_sweep_shapes({"block": 11, "row": 12, "mx": 13}[gran], 24)):
+        say(f"{gran} GEMM sweep {i}: {M}x{N}x{K}")
+        X = synth.act_col_outliers(M, K, seed=1000 + i)
+        W = synth.weight(N, K, seed=2000 + i)
+        if gran == "block":
+            _block_check(X, W, f"sweep block {M}x{N}x{K}")
+        elif gran == "row":
+            _row_check(X, W, f"sweep row {M}x{N}x{K}")
+        else:
+            _mx_check(X, W, f"sweep mx {M}x{N}x{K}")
+
+
+def test_grouped_random_routing_sweep():
+    """Grouped GEMM over seeded routings: 1 to 40 experts, counts from 0 to
+    600 rows (empty experts, single rows, 256-row edges), N and K multiples
+    of 128; every routed row against the per-expert oracle product."""
+    rng = np.random.default_rng(21)
+    for i in range(8):
+        E = int(rng.integers(1, 41))
+        counts = rng.integers(0, 601, size=E)
+        if i % 2 == 0:
+            counts[rng.integers(0, E)] = 0
+            counts[rng.integers(0, E)] = 256
+        T = int(counts.sum())
+        if T == 0:
+            counts[0] = 1
+            T = 1
+        N = 128 * int(rng.integers(1, 17))
+        K = 128 * int(rng.integers(1, 17))
+        offsets = np.zeros(E + 1, np.int32)
+        offsets[1:] = np.cumsum(counts)
+        say(f"grouped GEMM sweep {i}: E={E} T={T} N={N} K={K}")
+        A = synth.act_col_outliers(T, K, seed=3000 + i)
+        W = synth.normal_bf16((E * N, K), seed=4000 + i, std=0.02)
+        qa, sa = fp8.quantize_block(A.to(dev()))
+        (qw, sw), = fp8.requantize_weights([W.to(dev())], fp8.SCALE_F32)
+        y = fp8.grouped_gemm_a8w8_scaled((qa, sa), (qw.view(E, N, K), sw.view(E, N // 128, K // 128)),
+                                         torch.as_tensor(offsets, device=dev()))
+        oqa, osa = oracle.quantize_block(A)
+        oqw, osw = oracle.quantize_weight_block(W, 0)
+        oqw, osw = oqw.reshape(E, N, K), osw.reshape(E, N // 128, K // 128)
+        for e in range(E):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 > r0:
+                assert_gemm_all_rows(y[r0:r1], oqa[r0:r1], osa[r0:r1], oqw[e], osw[e],
+                                     oracle.GRAN_BLOCK, what=f"sweep {i} expert {e}")
+
+
+def test_layer_chain_in_graph_capture():
+    """One captured graph runs a chain of the library's launches: 1x128 quant
+    -> block GEMM on the large-M kernel, 1x128 quant -> decode-size block GEMM
+    (stream-K with its reduce, workspace from the graph pool), RMSNorm +
+    per-token quant -> row-scaled GEMM.  Every replay, with eager work and
+    synchronizations between, is bitwise equal to the same chain run eagerly."""
+    say("layer chain captured in a HIP graph, 3 replays")
+    M, Md, K, N1, N2 = 1024, 256, 2048, 2048, 1536
+    x = synth.act_col_outliers(M, K, seed=81).to(dev())
+    xd = synth.act_col_outliers(Md, K, seed=82).to(dev())
+    h = synth.normal_bf16((M, K), seed=83).to(dev())
+    gamma = synth.normal_bf16((K,), seed=84, std=0.5).to(dev())
+    (qw1, sw1), = fp8.requantize_weights([synth.weight(N1, K, seed=85).to(dev())], fp8.SCALE_F32)
+    qw2, sw2 = fp8.quantize_token(synth.weight(N2, K, seed=86).to(dev()))
+    bufs = {
+        "qa": torch.empty((M, K), dtype=torch.uint8, device=dev()),
+        "sa": torch.empty((M, K // 128), dtype=torch.float32, device=dev()),
+        "qd": torch.empty((Md, K), dtype=torch.uint8, device=dev()),
+        "sd": torch.empty((Md, K // 128), dtype=torch.float32, device=dev()),
+        "q2": torch.empty((M, K), dtype=torch.uint8, device=dev()),
+        "s2": torch.empty((M,), dtype=torch.float32, device=dev()),
+        "y1": torch.empty((M, N1), dtype=torch.bfloat16, device=dev()),
+        "yd": torch.empty((Md, N1), dtype=torch.bfloat16, device=dev()),
+        "y2": torch.empty((M, N2), dtype=torch.bfloat16, device=dev()),
+    }
+
+    def chain(b):
+        fp8.quantize_block(x, out=(b["qa"], b["sa"]))
+        fp8.gemm_a8w8_scaled((b["qa"], b["sa"]), (qw1, sw1), fp8.GRAN_BLOCK, out=b["y1"])
+        fp8.quantize_block(xd, out=(b["qd"], b["sd"]))
+        fp8.gemm_a8w8_scaled((b["qd"], b["sd"]), (qw1, sw1), fp8.GRAN_BLOCK, out=b["yd"])
+        fp8.rmsnorm_quant(h, gamma, 1e-6, 0, out=(b["q2"], b["s2"]))
+        fp8.gemm_a8w8_scaled((b["q2"], b["s2"]), (qw2, sw2), fp8.GRAN_ROW, out=b["y2"])
+
+    chain(bufs)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in bufs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(bufs)
+    for rep in range(3):
+        for v in bufs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in bufs:
+            a, b = bufs[k], eager[k]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), f"replay {rep}: {k} differs from the eager chain"
+        _ = fp8.gemm_a8w8_scaled((eager["qd"], eager["sd"]), (qw1, sw1), fp8.GRAN_BLOCK)
+        torch.cuda.synchronize()
+    oqa, osa = oracle.quantize_block(x.cpu())
+    oqw, osw = oracle.quantize_weight_block(synth.weight(N1, K, seed=85), 0)
+    rows = [0, 511, 1023]
+    ref = oracle.gemm(oqa[rows], oqw, osa[rows], osw, oracle.GRAN_BLOCK)
+    assert_rows_close(eager["y1"], ref, rows=rows, what="chain y1")
