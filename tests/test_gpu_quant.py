@@ -507,3 +507,34 @@ def test_forced_foreign_arch_is_refused(monkeypatch):
     with pytest.raises(fp8.Fp8Error) as ei:
         fp8.quantize_block(x)
     assert ei.value.status == -4
+
+
+# ------------------------------------------------------------ seeded sweeps --
+def test_quantizer_shape_sweep():
+    """Seeded shapes through every quantizer, each bit-exact against the
+    oracle: rows 1..3000 with the 64- and 256-row edges mixed in, K a multiple
+    of 128 up to 6144 (RMSNorm forms: any K up to 6144, multiples of 8 for
+    the per-token form), SwiGLU widths up to 3072, gathers with repeated and
+    unsorted source rows."""
+    rng = np.random.default_rng(31)
+    edges = [1, 63, 64, 65, 255, 256, 257]
+    for i in range(10):
+        M = edges[i] if i < len(edges) else int(rng.integers(1, 3001))
+        K = 128 * int(rng.integers(1, 49))
+        say(f"quantizer sweep {i}: M={M} K={K}")
+        x = synth.act_col_outliers(M, K, seed=5000 + i)
+        _eq_block(x)
+        _eq_block_e8m0(x)
+        _eq_token(x)
+        h, gamma = synth.rms_inputs(M=M, K=K, seed=6000 + i)
+        _eq_rms(h, gamma, 128)
+        Kr = 8 * int(rng.integers(1, 769))
+        h2, gamma2 = synth.rms_inputs(M=M, K=Kr, seed=7000 + i)
+        say(f"quantizer sweep {i}: rmsnorm per token K={Kr}")
+        _eq_rms(h2, gamma2, 0)
+        _eq_add_rms(h2, synth.normal_bf16((M, Kr), seed=8000 + i, std=3.0), gamma2, 0)
+        I = 128 * int(rng.integers(1, 25))
+        say(f"quantizer sweep {i}: swiglu I={I}, gather")
+        _eq_swiglu(synth.normal_bf16((M, 2 * I), seed=9000 + i, std=3.0))
+        n_src = int(rng.integers(1, 400))
+        _eq_gather(synth.normal_bf16((n_src, K), seed=9500 + i), rng.integers(0, n_src, size=M))
