@@ -367,7 +367,7 @@ def main():
         vendor_compare(args.reps if args.reps > 3 else 10)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
                           "(the sharded path is not built)"}))
         sys.exit(2)
 

@@ -1,6 +1,6 @@
 """bench.py on the CPU: it imports, refuses more than one GPU with a message,
-and the helpers its GPU path calls exist (a missing one would surface only on
-the GPU machine)."""
+and the helpers its GPU path calls exist (a missing one would otherwise surface
+only on a GPU)."""
 import json
 import os
 import subprocess
